@@ -1,0 +1,227 @@
+"""Benchmark of the DoRA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+
+A step is one pass of the whole hot path over one synthetic layer: the
+factored norm (Gram, W0 streaming pass, assembly -> wnorm, g), the fused
+compose forward and the fused compose backward (d_base, d_lora, d_m).  The
+default workload is the headline shape d_out = d_in = 8192, r = 384, bf16,
+T = 2048 tokens.
+
+Inputs are resident in HBM before timing starts.  Several copies of every
+input are rotated so that one step's working set is not served from the 256 MB
+Infinity Cache (MALL) by the previous step.  HIP events recorded on the stream
+the library launches on time each call; the step loop is bracketed by
+device synchronisations.  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import dora_inputs as DI  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "factored-norm TFLOP/s & compose HBM GB/s (% roofline), d_in=8192 r=384 bf16"
+MALL_BYTES = 256 << 20
+
+
+def norm_flops(d_out, d_in, r):
+    """Algorithmic FLOPs of the factored norm: U = W0 A^T (2 d_out d_in r),
+    base squares (2 d_out d_in), Gram symmetric half (r (r+1) d_in),
+    B G (2 d_out r^2), the two row dots (4 d_out r)."""
+    return 2 * d_out * d_in * r + 2 * d_out * d_in + r * (r + 1) * d_in + 2 * d_out * r * r + 4 * d_out * r
+
+
+def norm_bytes(d_out, d_in, r, esz):
+    """Algorithmic bytes: W0, A, B read once; m read; wnorm and g written."""
+    return (d_out * d_in + r * d_in + d_out * r) * esz + 3 * d_out * 4
+
+
+def compose_fwd_bytes(T, d_out, esz):
+    return 3 * T * d_out * esz + d_out * 4
+
+
+def compose_bwd_bytes(T, d_out, esz):
+    # dy, base, lora read; d_base, d_lora written; g, wnorm read; d_m written
+    return 5 * T * d_out * esz + 3 * d_out * 4
+
+
+def cpu_baseline(layer, budget_s=12.0):
+    """The oracle as it stands, on a bounded row sample of the same layer."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    spec = layer.spec
+    W0, A, B = layer.W0.cpu(), layer.A.cpu(), layer.B.cpu()
+    m = oracle.as_f64(layer.m.cpu())
+    chunk = 256
+    rows_done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and rows_done < spec.d_out:
+        rows = np.arange(rows_done, min(spec.d_out, rows_done + chunk))
+        wn = oracle.dense_row_norm(W0, A, B, spec.s, rows=rows)
+        oracle.magnitude_scale(m[rows], wn, 1e-7)
+        rows_done += rows.size
+    t_norm = time.perf_counter() - t0
+    flops = norm_flops(spec.d_out, spec.d_in, spec.r) * rows_done / spec.d_out
+    # compose forward + backward on a token sample
+    tok = min(spec.T, 256)
+    base, lora, dy = (oracle.as_f64(t[:tok].cpu()) for t in (layer.base_out, layer.lora_out, layer.dy))
+    g = np.ones(spec.d_out)
+    t1 = time.perf_counter()
+    oracle.compose_forward(base, lora, g, spec.s)
+    t_fwd = time.perf_counter() - t1
+    t1 = time.perf_counter()
+    oracle.compose_backward(dy, base, lora, g, g, spec.s, 1e-7)
+    t_bwd = time.perf_counter() - t1
+    esz = layer.W0.element_size()
+    return {
+        "value": flops / t_norm / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"dense fp64 norm of rows 0..{rows_done - 1} of {spec.d_out} ({t_norm:.1f} s); "
+                  f"compose fwd+bwd on {tok} of {spec.T} tokens",
+        "compose_fwd_GBps": compose_fwd_bytes(tok, spec.d_out, esz) / t_fwd / 1e9,
+        "compose_bwd_GBps": compose_bwd_bytes(tok, spec.d_out, esz) / t_bwd / 1e9,
+        "cpu": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the DoRA norm and compose are "
+              "per-layer kernels; multi-GPU sharding is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import dora_adapter_factored_amd as D
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = DI.CONFIGS[args.config]
+    print(f"[bench] generating {spec.name}", file=sys.stderr, flush=True)
+    layer = DI.make_layer(spec, DI.config_seed(args.config), device=dev)
+    dt = layer.W0.dtype
+    esz = layer.W0.element_size()
+    d_out, d_in, r, T, s = spec.d_out, spec.d_in, spec.r, spec.T, spec.s
+    eps = D.default_eps(dt)
+
+    # rotating copies: one step touches its own set of inputs and outputs
+    step_bytes = (d_out * d_in + 2 * r * (d_in + d_out)) * esz + 6 * T * d_out * esz
+    nsets = max(2, int(np.ceil(2 * MALL_BYTES / step_bytes)) + 1)
+    sets = []
+    for i in range(nsets):
+        c = (lambda t: t) if i == 0 else (lambda t: t.clone())
+        sets.append(dict(W0=c(layer.W0), A=c(layer.A), B=c(layer.B), m=c(layer.m), base=c(layer.base_out),
+                         lora=c(layer.lora_out), dy=c(layer.dy),
+                         wn=torch.empty(d_out, device=dev), g=torch.empty(d_out, device=dev),
+                         y=torch.empty_like(layer.base_out), db=torch.empty_like(layer.base_out),
+                         dl=torch.empty_like(layer.base_out), dm=torch.empty(d_out, device=dev)))
+    ws_norm = torch.empty(D.norm_workspace_size(d_out, d_in, r, dt), dtype=torch.uint8, device=dev)
+    ws_bwd = torch.empty(max(1, D.compose_backward_workspace_size(T, d_out)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(st, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        D.factored_norm(st["W0"], st["A"], st["B"], s, st["m"], eps, wnorm=st["wn"], g=st["g"], ws=ws_norm)
+        if ev is not None:
+            ev[1].record(stream)
+        D.compose(st["base"], st["lora"], st["g"], s, out=st["y"])
+        if ev is not None:
+            ev[2].record(stream)
+        D.compose_backward(st["dy"], st["base"], st["lora"], st["g"], st["wn"], s, eps,
+                           d_base=st["db"], d_lora=st["dl"], d_m=st["dm"], ws=ws_bwd)
+        if ev is not None:
+            ev[3].record(stream)
+
+    print(f"[bench] warmup {args.warmup} steps ({nsets} rotating input sets)", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % nsets], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    t_norm = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    t_fwd = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    t_bwd = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
+    F = norm_flops(d_out, d_in, r)
+    nb = norm_bytes(d_out, d_in, r, esz)
+    fb, bb = compose_fwd_bytes(T, d_out, esz), compose_bwd_bytes(T, d_out, esz)
+    norm_tflops = F / t_norm.mean() / 1e12
+    fwd_gbs, bwd_gbs = fb / t_fwd.mean() / 1e9, bb / t_bwd.mean() / 1e9
+    peak_mm = PEAK_BF16_TFLOPS if dt != torch.float32 else PEAK_F32_MFMA_TFLOPS
+
+    out = {
+        "metric": METRIC,
+        "value": round(norm_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {torch.bfloat16: "bf16", torch.float32: "f32"}[dt],
+        "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
+        "config": {"workload": spec.name, "d_out": d_out, "d_in": d_in, "r": r, "tokens": T, "s": s,
+                   "rotating_input_sets": nsets},
+        "norm": {"ms": round(t_norm.mean() * 1e3, 4), "ms_p10": round(np.percentile(t_norm, 10) * 1e3, 4),
+                 "ms_p90": round(np.percentile(t_norm, 90) * 1e3, 4), "TFLOPs": round(norm_tflops, 2),
+                 "frac_mfma_peak": round(norm_tflops / peak_mm, 4), "algorithmic_flop": F,
+                 "algorithmic_bytes": nb, "GBps": round(nb / t_norm.mean() / 1e9, 1),
+                 "workspace_bytes": int(ws_norm.numel())},
+        "compose_fwd": {"ms": round(t_fwd.mean() * 1e3, 4), "GBps": round(fwd_gbs, 1),
+                        "frac_hbm_peak": round(fwd_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": fb},
+        "compose_bwd": {"ms": round(t_bwd.mean() * 1e3, 4), "GBps": round(bwd_gbs, 1),
+                        "frac_hbm_peak": round(bwd_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": bb},
+        "roofline": {"kernel": "dora_factored_norm (gram_partial + gram_finalize + w0_pass + norm_finalize)",
+                     "bound": "mfma", "achieved": round(norm_tflops, 2), "peak": peak_mm, "unit": "TFLOP/s",
+                     "frac": round(norm_tflops / peak_mm, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(layer, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

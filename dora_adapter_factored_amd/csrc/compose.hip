@@ -1,0 +1,347 @@
+// Fused DoRA compose, forward and backward, for gfx950.
+//
+// Forward ("Scaling DoRA", §3 compose kernel and Data Availability contract):
+//   y = base + ((g - 1) * base + (g * s) * lora)      (delta_only drops base)
+// in fp32 with one rounding to the activation dtype; 2 reads + 1 write per
+// element.  Backward (§3 backward kernel, norm detached):
+//   d_base = g * dy (delta_only: (g - 1) * dy),  d_lora = (g * s) * dy,
+//   d_m_j  = sum_t dy_tj * (base_tj + s * lora_tj) / max(wnorm_j, eps)
+// with d_m reduced in a fixed order: per-token-block partial sums written to
+// the workspace, then one finalize pass.  No atomics, so d_m is bitwise
+// reproducible.
+//
+// Both kernels are HBM-bound streams over [T, d_out].  A workgroup owns a
+// strip of 64 sixteen-byte packets along d_out (one wave reads 1 KiB of a
+// row) and 4 row lanes; each thread keeps g for its packet in registers for
+// the whole strip and walks rows, with several rows' loads in flight before
+// the first store.
+#include "dora_device.h"
+#include "dora_launch.h"
+
+namespace dora {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTC = 64;          // packets along d_out per workgroup
+constexpr int kTR = 4;           // row lanes per workgroup
+constexpr int kRPT = 4;          // rows per thread per step (loads in flight)
+constexpr int kFwdRowsPerBlock = kTR * kRPT;
+constexpr int kBwdTokenBlock = 32;   // rows summed into one d_m partial row
+constexpr int kMaxParts = 1024;      // cap on d_m partial rows (grid-strides beyond)
+constexpr int kMaxGridY = 65535;
+
+template <typename T, bool DELTA>
+__global__ __launch_bounds__(kThreads) void compose_fwd_vec(const T* base, const T* __restrict__ lora,
+                                                            const float* __restrict__ g, float s,
+                                                            int64_t nrows, int64_t d_out, T* y) {
+    constexpr int N = Pack<T>::N;
+    const int tc = threadIdx.x % kTC, tr = threadIdx.x / kTC;
+    const int64_t col = ((int64_t)blockIdx.x * kTC + tc) * N;
+    if (col >= d_out) return;
+    float gm1[N], gs[N];
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        const float gv = g[col + e];
+        gm1[e] = gv - 1.0f;
+        gs[e] = gv * s;
+    }
+    for (int64_t rb = blockIdx.y; rb * kFwdRowsPerBlock < nrows; rb += gridDim.y) {
+        const int64_t r0 = rb * kFwdRowsPerBlock + tr;
+        Pack<T> b[kRPT], l[kRPT];
+#pragma unroll
+        for (int i = 0; i < kRPT; ++i) {
+            const int64_t row = r0 + (int64_t)i * kTR;
+            if (row < nrows) {
+                b[i] = load_pack_stream(base + row * d_out + col);
+                l[i] = load_pack_stream(lora + row * d_out + col);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kRPT; ++i) {
+            const int64_t row = r0 + (int64_t)i * kTR;
+            if (row < nrows) {
+                Pack<T> o;
+#pragma unroll
+                for (int e = 0; e < N; ++e) {
+                    const float bf = Cvt<T>::to_f(b[i].e[e]);
+                    const float lf = Cvt<T>::to_f(l[i].e[e]);
+                    const float d = fmaf(gm1[e], bf, gs[e] * lf);
+                    o.e[e] = Cvt<T>::from_f(DELTA ? d : bf + d);
+                }
+                store_pack_stream(y + row * d_out + col, o);
+            }
+        }
+    }
+}
+
+template <typename T, bool DELTA>
+__global__ __launch_bounds__(kThreads) void compose_fwd_scalar(const T* base, const T* __restrict__ lora,
+                                                               const float* __restrict__ g, float s,
+                                                               int64_t n, int64_t d_out, T* y) {
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * kThreads) {
+        const float gv = g[i % d_out];
+        const float bf = Cvt<T>::to_f(base[i]);
+        const float lf = Cvt<T>::to_f(lora[i]);
+        const float d = fmaf(gv - 1.0f, bf, (gv * s) * lf);
+        y[i] = Cvt<T>::from_f(DELTA ? d : bf + d);
+    }
+}
+
+template <typename T, bool DELTA, bool DM, bool DB, bool DL>
+__global__ __launch_bounds__(kThreads) void compose_bwd_vec(const T* dy, const T* __restrict__ base,
+                                                            const T* __restrict__ lora,
+                                                            const float* __restrict__ g, float s,
+                                                            int64_t nrows, int64_t d_out, T* d_base,
+                                                            T* d_lora, float* __restrict__ dm_part) {
+    constexpr int N = Pack<T>::N;
+    constexpr int kSteps = kBwdTokenBlock / (kTR * kRPT);
+    __shared__ float red[kTR - 1][kTC * N];
+    const int tc = threadIdx.x % kTC, tr = threadIdx.x / kTC;
+    const int64_t col = ((int64_t)blockIdx.x * kTC + tc) * N;
+    const bool active = col < d_out;
+    float gb[N], gl[N], acc[N];
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        const float gv = active ? g[col + e] : 0.0f;
+        gb[e] = DELTA ? gv - 1.0f : gv;
+        gl[e] = gv * s;
+        acc[e] = 0.0f;
+    }
+    if (active) {
+        for (int64_t rb = blockIdx.y; rb * kBwdTokenBlock < nrows; rb += gridDim.y) {
+#pragma unroll
+            for (int st = 0; st < kSteps; ++st) {
+                const int64_t r0 = rb * kBwdTokenBlock + st * (kTR * kRPT) + tr;
+                Pack<T> dv[kRPT], bv[kRPT], lv[kRPT];
+#pragma unroll
+                for (int i = 0; i < kRPT; ++i) {
+                    const int64_t row = r0 + (int64_t)i * kTR;
+                    if (row < nrows) {
+                        const int64_t off = row * d_out + col;
+                        dv[i] = load_pack_stream(dy + off);
+                        if (DM) {
+                            bv[i] = load_pack_stream(base + off);
+                            lv[i] = load_pack_stream(lora + off);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < kRPT; ++i) {
+                    const int64_t row = r0 + (int64_t)i * kTR;
+                    if (row < nrows) {
+                        const int64_t off = row * d_out + col;
+                        Pack<T> ob, ol;
+#pragma unroll
+                        for (int e = 0; e < N; ++e) {
+                            const float df = Cvt<T>::to_f(dv[i].e[e]);
+                            if (DB) ob.e[e] = Cvt<T>::from_f(gb[e] * df);
+                            if (DL) ol.e[e] = Cvt<T>::from_f(gl[e] * df);
+                            if (DM) {
+                                const float inner = fmaf(s, Cvt<T>::to_f(lv[i].e[e]),
+                                                         Cvt<T>::to_f(bv[i].e[e]));
+                                acc[e] = fmaf(df, inner, acc[e]);
+                            }
+                        }
+                        if (DB) store_pack_stream(d_base + off, ob);
+                        if (DL) store_pack_stream(d_lora + off, ol);
+                    }
+                }
+            }
+        }
+    }
+    if (DM) {
+        if (tr > 0) {
+#pragma unroll
+            for (int e = 0; e < N; ++e) red[tr - 1][tc * N + e] = acc[e];
+        }
+        __syncthreads();
+        if (tr == 0 && active) {
+#pragma unroll
+            for (int e = 0; e < N; ++e) {
+                float v = acc[e];
+#pragma unroll
+                for (int q = 0; q < kTR - 1; ++q) v += red[q][tc * N + e];
+                dm_part[(int64_t)blockIdx.y * d_out + col + e] = v;
+            }
+        }
+    }
+}
+
+template <typename T, bool DELTA, bool DM, bool DB, bool DL>
+__global__ __launch_bounds__(kThreads) void compose_bwd_scalar(const T* dy, const T* __restrict__ base,
+                                                               const T* __restrict__ lora,
+                                                               const float* __restrict__ g, float s,
+                                                               int64_t nrows, int64_t d_out, T* d_base,
+                                                               T* d_lora, float* __restrict__ dm_part) {
+    const int64_t col = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (col >= d_out) return;
+    const float gv = g[col];
+    const float gb = DELTA ? gv - 1.0f : gv, gl = gv * s;
+    float acc = 0.0f;
+    for (int64_t rb = blockIdx.y; rb * kBwdTokenBlock < nrows; rb += gridDim.y) {
+        const int64_t rend = (rb + 1) * kBwdTokenBlock < nrows ? (rb + 1) * kBwdTokenBlock : nrows;
+        for (int64_t row = rb * kBwdTokenBlock; row < rend; ++row) {
+            const int64_t off = row * d_out + col;
+            const float df = Cvt<T>::to_f(dy[off]);
+            if (DM) acc = fmaf(df, fmaf(s, Cvt<T>::to_f(lora[off]), Cvt<T>::to_f(base[off])), acc);
+            if (DB) d_base[off] = Cvt<T>::from_f(gb * df);
+            if (DL) d_lora[off] = Cvt<T>::from_f(gl * df);
+        }
+    }
+    if (DM) dm_part[(int64_t)blockIdx.y * d_out + col] = acc;
+}
+
+__global__ __launch_bounds__(kThreads) void dm_finalize(const float* __restrict__ part, int nparts,
+                                                        const float* __restrict__ wnorm, float eps,
+                                                        int64_t d_out, float* __restrict__ d_m) {
+    const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (j >= d_out) return;
+    float acc = 0.0f;
+    for (int p = 0; p < nparts; ++p) acc += part[(int64_t)p * d_out + j];
+    d_m[j] = nparts > 0 ? acc / fmaxf(wnorm[j], eps) : 0.0f;
+}
+
+inline bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int bwd_parts(int64_t T) {
+    int64_t p = (T + kBwdTokenBlock - 1) / kBwdTokenBlock;
+    return (int)(p < kMaxParts ? p : kMaxParts);
+}
+
+template <typename T>
+hipError_t fwd_typed(const void* base, const void* lora, const float* g, float s, int64_t nrows,
+                     int64_t d_out, bool delta, void* y, hipStream_t st) {
+    constexpr int N = Pack<T>::N;
+    const T* b = static_cast<const T*>(base);
+    const T* l = static_cast<const T*>(lora);
+    T* o = static_cast<T*>(y);
+    if (d_out % N == 0 && aligned16(base) && aligned16(lora) && aligned16(y)) {
+        const int64_t nvec = d_out / N;
+        const int64_t gx = (nvec + kTC - 1) / kTC;
+        int64_t gy = (nrows + kFwdRowsPerBlock - 1) / kFwdRowsPerBlock;
+        if (gy > kMaxGridY) gy = kMaxGridY;
+        dim3 grid((unsigned)gx, (unsigned)gy);
+        if (delta)
+            compose_fwd_vec<T, true><<<grid, kThreads, 0, st>>>(b, l, g, s, nrows, d_out, o);
+        else
+            compose_fwd_vec<T, false><<<grid, kThreads, 0, st>>>(b, l, g, s, nrows, d_out, o);
+    } else {
+        const int64_t n = nrows * d_out;
+        int64_t gx = (n + kThreads - 1) / kThreads;
+        if (gx > 65536) gx = 65536;
+        if (delta)
+            compose_fwd_scalar<T, true><<<(unsigned)gx, kThreads, 0, st>>>(b, l, g, s, n, d_out, o);
+        else
+            compose_fwd_scalar<T, false><<<(unsigned)gx, kThreads, 0, st>>>(b, l, g, s, n, d_out, o);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, bool DELTA, bool DM, bool DB, bool DL>
+void bwd_launch(bool vec, const T* dy, const T* b, const T* l, const float* g, float s, int64_t nrows,
+                int64_t d_out, T* db, T* dl, float* part, int nparts, hipStream_t st) {
+    if (vec) {
+        constexpr int N = Pack<T>::N;
+        const int64_t gx = (d_out / N + kTC - 1) / kTC;
+        dim3 grid((unsigned)gx, (unsigned)nparts);
+        compose_bwd_vec<T, DELTA, DM, DB, DL><<<grid, kThreads, 0, st>>>(dy, b, l, g, s, nrows, d_out, db,
+                                                                        dl, part);
+    } else {
+        dim3 grid((unsigned)((d_out + kThreads - 1) / kThreads), (unsigned)nparts);
+        compose_bwd_scalar<T, DELTA, DM, DB, DL><<<grid, kThreads, 0, st>>>(dy, b, l, g, s, nrows, d_out,
+                                                                           db, dl, part);
+    }
+}
+
+template <typename T, bool DELTA, bool DM>
+void bwd_dispatch_outputs(bool vec, const T* dy, const T* b, const T* l, const float* g, float s,
+                          int64_t nrows, int64_t d_out, T* db, T* dl, float* part, int nparts,
+                          hipStream_t st) {
+    if (db && dl)
+        bwd_launch<T, DELTA, DM, true, true>(vec, dy, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
+    else if (db)
+        bwd_launch<T, DELTA, DM, true, false>(vec, dy, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
+    else if (dl)
+        bwd_launch<T, DELTA, DM, false, true>(vec, dy, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
+    else
+        bwd_launch<T, DELTA, DM, false, false>(vec, dy, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
+}
+
+template <typename T>
+hipError_t bwd_typed(const void* dy, const void* base, const void* lora, const float* g,
+                     const float* wnorm, float s, float eps, int64_t nrows, int64_t d_out, bool delta,
+                     void* d_base, void* d_lora, float* d_m, void* ws, hipStream_t st) {
+    constexpr int N = Pack<T>::N;
+    const T* dyp = static_cast<const T*>(dy);
+    const T* b = static_cast<const T*>(base);
+    const T* l = static_cast<const T*>(lora);
+    T* db = static_cast<T*>(d_base);
+    T* dl = static_cast<T*>(d_lora);
+    const bool want_dm = d_m != nullptr;
+    if (nrows > 0 && (db || dl || want_dm)) {
+        const bool vec = d_out % N == 0 && aligned16(dy) && aligned16(db) && aligned16(dl) &&
+                         (!want_dm || (aligned16(base) && aligned16(lora)));
+        float* part = static_cast<float*>(ws);
+        if (want_dm) {
+            const int nparts = bwd_parts(nrows);
+            if (delta)
+                bwd_dispatch_outputs<T, true, true>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
+            else
+                bwd_dispatch_outputs<T, false, true>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
+        } else {
+            // frozen magnitude: only dy is read; the token grid needs no partials
+            int64_t gy = (nrows + kBwdTokenBlock - 1) / kBwdTokenBlock;
+            const int nblk = (int)(gy < kMaxGridY ? gy : kMaxGridY);
+            if (delta)
+                bwd_dispatch_outputs<T, true, false>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, nullptr, nblk, st);
+            else
+                bwd_dispatch_outputs<T, false, false>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, nullptr, nblk, st);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (want_dm) {
+        const int nparts = nrows > 0 ? bwd_parts(nrows) : 0;
+        dm_finalize<<<(unsigned)((d_out + kThreads - 1) / kThreads), kThreads, 0, st>>>(
+            static_cast<const float*>(ws), nparts, wnorm, eps, d_out, d_m);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+size_t compose_bwd_workspace_bytes(int64_t T, int64_t d_out) {
+    if (T <= 0) return 0;
+    return align_up((size_t)bwd_parts(T) * (size_t)d_out * sizeof(float), 256);
+}
+
+hipError_t launch_compose_fwd(const void* base, const void* lora, const float* g, float s, int64_t T,
+                              int64_t d_out, int dtype, bool delta_only, void* y, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    switch (dtype) {
+        case kF32: return fwd_typed<float>(base, lora, g, s, T, d_out, delta_only, y, stream);
+        case kBF16: return fwd_typed<bf16_t>(base, lora, g, s, T, d_out, delta_only, y, stream);
+        default: return fwd_typed<f16_t>(base, lora, g, s, T, d_out, delta_only, y, stream);
+    }
+}
+
+hipError_t launch_compose_bwd(const void* dy, const void* base, const void* lora, const float* g,
+                              const float* wnorm, float s, float eps, int64_t T, int64_t d_out,
+                              int dtype, bool delta_only, void* d_base, void* d_lora, float* d_m,
+                              void* workspace, hipStream_t stream) {
+    switch (dtype) {
+        case kF32:
+            return bwd_typed<float>(dy, base, lora, g, wnorm, s, eps, T, d_out, delta_only, d_base, d_lora,
+                                    d_m, workspace, stream);
+        case kBF16:
+            return bwd_typed<bf16_t>(dy, base, lora, g, wnorm, s, eps, T, d_out, delta_only, d_base, d_lora,
+                                     d_m, workspace, stream);
+        default:
+            return bwd_typed<f16_t>(dy, base, lora, g, wnorm, s, eps, T, d_out, delta_only, d_base, d_lora,
+                                    d_m, workspace, stream);
+    }
+}
+
+}  // namespace dora

@@ -1,0 +1,155 @@
+// C ABI of the DoRA hot path: host-side validation, workspace queries and
+// dispatch to the kernel launchers.  Nothing is enqueued unless every argument
+// checks out; errors carry a thread-local detail string.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "../../include/dora.h"
+#include "dora_launch.h"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_detail[0] = '\0';
+    return DORA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(DORA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+bool dim_ok(int64_t v, int64_t lo) { return v >= lo && v < kMaxDim; }
+bool dtype_ok(int dt) { return dt == DORA_F32 || dt == DORA_BF16 || dt == DORA_F16; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dora_status_string(int status) {
+    switch (status) {
+        case DORA_OK: return "ok";
+        case DORA_ERR_INVALID_ARG: return "invalid argument";
+        case DORA_ERR_UNSUPPORTED: return "unsupported";
+        case DORA_ERR_WORKSPACE: return "workspace missing or too small";
+        case DORA_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char* dora_last_error_detail(void) { return g_detail; }
+
+int dora_version(void) { return 100; }
+
+int dora_factored_norm_workspace_size(int64_t d_out, int64_t d_in, int64_t r, int dtype, size_t* bytes) {
+    if (!bytes) return fail(DORA_ERR_INVALID_ARG, "bytes is NULL");
+    if (!dim_ok(d_out, 1) || !dim_ok(d_in, 1) || !dim_ok(r, 1))
+        return fail(DORA_ERR_INVALID_ARG, "sizes must satisfy 1 <= d_out, d_in, r < 2^31 (got %lld, %lld, %lld)",
+                    (long long)d_out, (long long)d_in, (long long)r);
+    if (!dtype_ok(dtype)) return fail(DORA_ERR_INVALID_ARG, "unknown dtype code %d", dtype);
+    if (dtype == DORA_F16) return fail(DORA_ERR_UNSUPPORTED, "factored norm supports bf16 and fp32 inputs");
+    // The s == 0 path needs less; the query reports the general size.
+    *bytes = dora::plan_norm(d_out, d_in, r, dtype, false).bytes;
+    return ok();
+}
+
+int dora_factored_norm(const void* W0, const void* A, const void* B, const float* m, int64_t d_out, int64_t d_in,
+                       int64_t r, int dtype, float s, float eps, float* wnorm, float* g, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (!W0 || !A || !B) return fail(DORA_ERR_INVALID_ARG, "W0, A and B must be non-NULL");
+    if (!wnorm) return fail(DORA_ERR_INVALID_ARG, "wnorm must be non-NULL");
+    if (m && !g) return fail(DORA_ERR_INVALID_ARG, "g must be non-NULL when m is given");
+    if (!dim_ok(d_out, 1) || !dim_ok(d_in, 1) || !dim_ok(r, 1))
+        return fail(DORA_ERR_INVALID_ARG, "sizes must satisfy 1 <= d_out, d_in, r < 2^31 (got %lld, %lld, %lld)",
+                    (long long)d_out, (long long)d_in, (long long)r);
+    if (!dtype_ok(dtype)) return fail(DORA_ERR_INVALID_ARG, "unknown dtype code %d", dtype);
+    if (dtype == DORA_F16) return fail(DORA_ERR_UNSUPPORTED, "factored norm supports bf16 and fp32 inputs");
+    if (!std::isfinite(s)) return fail(DORA_ERR_INVALID_ARG, "s must be finite");
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(DORA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    const dora::NormPlan plan = dora::plan_norm(d_out, d_in, r, dtype, s == 0.0f);
+    if (plan.bytes > 0) {
+        if (!workspace) return fail(DORA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", plan.bytes);
+        if (workspace_bytes < plan.bytes)
+            return fail(DORA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, plan.bytes);
+        if (!aligned256(workspace)) return fail(DORA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    }
+    hipError_t e = dora::launch_norm(plan, W0, A, B, m, s, eps, wnorm, g, workspace,
+                                     static_cast<hipStream_t>(stream));
+    return hip_status(e, "dora_factored_norm launch");
+}
+
+int dora_compose(const void* base_out, const void* lora_out, const float* g, float s, int64_t T, int64_t d_out,
+                 int dtype, int delta_only, void* y, void* stream) {
+    if (!g) return fail(DORA_ERR_INVALID_ARG, "g must be non-NULL");
+    if (T != 0 && (!base_out || !lora_out || !y))
+        return fail(DORA_ERR_INVALID_ARG, "base_out, lora_out and y must be non-NULL when T > 0");
+    if (!dim_ok(d_out, 1) || T < 0 || T >= ((int64_t)1 << 40))
+        return fail(DORA_ERR_INVALID_ARG, "sizes must satisfy 1 <= d_out < 2^31, 0 <= T < 2^40 (got T=%lld, d_out=%lld)",
+                    (long long)T, (long long)d_out);
+    if (!dtype_ok(dtype)) return fail(DORA_ERR_INVALID_ARG, "unknown dtype code %d", dtype);
+    if (delta_only != 0 && delta_only != 1) return fail(DORA_ERR_INVALID_ARG, "delta_only must be 0 or 1");
+    if (!std::isfinite(s)) return fail(DORA_ERR_INVALID_ARG, "s must be finite");
+    if (T != 0 && y == lora_out) return fail(DORA_ERR_INVALID_ARG, "y may alias base_out only");
+    hipError_t e = dora::launch_compose_fwd(base_out, lora_out, g, s, T, d_out, dtype, delta_only != 0, y,
+                                            static_cast<hipStream_t>(stream));
+    return hip_status(e, "dora_compose launch");
+}
+
+int dora_compose_backward_workspace_size(int64_t T, int64_t d_out, size_t* bytes) {
+    if (!bytes) return fail(DORA_ERR_INVALID_ARG, "bytes is NULL");
+    if (!dim_ok(d_out, 1) || T < 0 || T >= ((int64_t)1 << 40))
+        return fail(DORA_ERR_INVALID_ARG, "sizes must satisfy 1 <= d_out < 2^31, 0 <= T < 2^40");
+    *bytes = dora::compose_bwd_workspace_bytes(T, d_out);
+    return ok();
+}
+
+int dora_compose_backward(const void* dy, const void* base_out, const void* lora_out, const float* g,
+                          const float* wnorm, float s, float eps, int64_t T, int64_t d_out, int dtype,
+                          int delta_only, void* d_base, void* d_lora, float* d_m, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    if (!g) return fail(DORA_ERR_INVALID_ARG, "g must be non-NULL");
+    if (T != 0 && !dy) return fail(DORA_ERR_INVALID_ARG, "dy must be non-NULL when T > 0");
+    if (d_m && !wnorm) return fail(DORA_ERR_INVALID_ARG, "wnorm must be non-NULL when d_m is requested");
+    if (d_m && T != 0 && (!base_out || !lora_out))
+        return fail(DORA_ERR_INVALID_ARG, "base_out and lora_out must be non-NULL when d_m is requested and T > 0");
+    if (!dim_ok(d_out, 1) || T < 0 || T >= ((int64_t)1 << 40))
+        return fail(DORA_ERR_INVALID_ARG, "sizes must satisfy 1 <= d_out < 2^31, 0 <= T < 2^40 (got T=%lld, d_out=%lld)",
+                    (long long)T, (long long)d_out);
+    if (!dtype_ok(dtype)) return fail(DORA_ERR_INVALID_ARG, "unknown dtype code %d", dtype);
+    if (delta_only != 0 && delta_only != 1) return fail(DORA_ERR_INVALID_ARG, "delta_only must be 0 or 1");
+    if (!std::isfinite(s)) return fail(DORA_ERR_INVALID_ARG, "s must be finite");
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(DORA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (T != 0 && d_base && d_lora && d_base == d_lora)
+        return fail(DORA_ERR_INVALID_ARG, "d_base and d_lora must differ");
+    if (d_m) {
+        const size_t need = dora::compose_bwd_workspace_bytes(T, d_out);
+        if (need > 0) {
+            if (!workspace) return fail(DORA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+            if (workspace_bytes < need)
+                return fail(DORA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+            if (!aligned256(workspace)) return fail(DORA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        }
+    }
+    hipError_t e = dora::launch_compose_bwd(dy, base_out, lora_out, g, wnorm, s, eps, T, d_out, dtype,
+                                            delta_only != 0, d_base, d_lora, d_m, workspace,
+                                            static_cast<hipStream_t>(stream));
+    return hip_status(e, "dora_compose_backward launch");
+}
+
+}  // extern "C"

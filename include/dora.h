@@ -1,0 +1,156 @@
+/*
+ * dora.h -- C ABI of the MI355X (gfx950) DoRA hot path: factored row norm and
+ * fused compose, forward and backward.
+ *
+ * Sources, cited by short title and section:
+ *   [ScalingDoRA]  "Scaling DoRA: High-Rank Adaptation via Factored Norms and
+ *                  Fused Kernels" (arXiv:2603.22276, paperlayer.ai summary).
+ *   [DoRA-wiki]    "DoRA" (aiwiki entry), DoRALinear.
+ *   [LoRA&DoRA]    "LoRA & DoRA: The Math, Memory, and Trade-offs".
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers to dense, row-major, contiguous
+ *     arrays (no strides).  W0, A, B and the activations share one element
+ *     type `dtype`; m, g, wnorm and d_m are always fp32.
+ *   - Layouts: W0 [d_out, d_in] (nn.Linear layout), A [r, d_in],
+ *     B [d_out, r]; activations [T, d_out] with the per-feature vectors
+ *     (g, wnorm, m, d_m) broadcast along the last axis.
+ *   - Ownership: the caller owns every buffer, workspace included.  The
+ *     library allocates nothing and keeps no mutable global state, so calls
+ *     are re-entrant; calls that share a workspace must not overlap.
+ *   - Execution: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     null stream) and the call returns without synchronising.  Arguments are
+ *     validated on the host before anything is enqueued; on any error nothing
+ *     is launched and no output is written.
+ *   - Errors: every entry point returns a dora_status_t.  DORA_ERR_HIP means a
+ *     HIP runtime call or a launch failed (dora_last_error_detail() names it);
+ *     faults inside kernels surface at the caller's next synchronisation.
+ *   - Sizes: any d_out, d_in, r >= 1 and T >= 0 are accepted (no multiple-of
+ *     tile requirement); each dimension must be below 2^31.
+ */
+#ifndef DORA_H_
+#define DORA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DORA_F32 = 0,   /* IEEE binary32 */
+    DORA_BF16 = 1,  /* bfloat16 */
+    DORA_F16 = 2    /* IEEE binary16 (compose only) */
+} dora_dtype_t;
+
+typedef enum {
+    DORA_OK = 0,
+    DORA_ERR_INVALID_ARG = 1,  /* NULL pointer, bad size, bad dtype code, bad flag */
+    DORA_ERR_UNSUPPORTED = 2,  /* valid request this library does not implement */
+    DORA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than the size query */
+    DORA_ERR_HIP = 4           /* HIP runtime or launch failure */
+} dora_status_t;
+
+/* Static string naming a status code (unknown codes give "unknown status"). */
+const char* dora_status_string(int status);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* dora_last_error_detail(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int dora_version(void);
+
+/*
+ * Workspace bytes needed by dora_factored_norm for these sizes (host call,
+ * launches nothing).  *bytes receives the size; 0 is possible.
+ */
+int dora_factored_norm_workspace_size(int64_t d_out, int64_t d_in, int64_t r, int dtype,
+                                      size_t* bytes);
+
+/*
+ * Factored row norm and magnitude scale, never forming B @ A.
+ *
+ * [ScalingDoRA] §2 (squared row norm = base + cross + Gram terms through
+ * O(d_out r + r^2) intermediates), App. B (assembly max(base + 2s cross +
+ * s^2 ba, 0), square root) and §4 (g = m / max(wnorm, eps)):
+ *   wnorm_i = sqrt(max(||W0_i||^2 + 2s B_i.(W0 A^T)_i + s^2 B_i (A A^T) B_i^T, 0))
+ *   g_i     = m_i / max(wnorm_i, eps)
+ * which equals ||W0_i + s (BA)_i|| ([DoRA-wiki] forward).  Accumulation is
+ * fp32 whatever the input dtype ([ScalingDoRA] §2, Data Availability).
+ *
+ *   W0, A, B  device, dtype DORA_BF16 or DORA_F32 (DORA_F16 returns
+ *             DORA_ERR_UNSUPPORTED), layouts above.
+ *   m         device fp32 [d_out], or NULL to compute wnorm only.
+ *   s         LoRA scale (alpha / r); s == 0 takes a base-norm-only path.
+ *   eps       clamp of the magnitude division, >= 0.
+ *   wnorm     device fp32 [d_out], output.
+ *   g         device fp32 [d_out], output; required when m != NULL, ignored
+ *             (may be NULL) when m == NULL.
+ *   workspace device scratch of at least dora_factored_norm_workspace_size()
+ *             bytes, 256-byte aligned; contents need no initialisation.
+ */
+int dora_factored_norm(const void* W0, const void* A, const void* B, const float* m,
+                       int64_t d_out, int64_t d_in, int64_t r, int dtype, float s, float eps,
+                       float* wnorm, float* g, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * Fused compose forward, one pass: 2 reads + 1 write per element.
+ *
+ * [ScalingDoRA] §3 (compose kernel, numerically stable form with fp32
+ * intermediates and an explicit (g - 1) correction), Data Availability
+ * (module contract dY = g*(s lora) + (g - 1)*base) and App. B (g broadcast
+ * along the last axis; activations stay in their dtype):
+ *   delta_only == 0:  y = base + ((g - 1)*base + (g*s)*lora)
+ *   delta_only == 1:  y =         (g - 1)*base + (g*s)*lora
+ * evaluated in fp32 and rounded once (round-to-nearest-even) to dtype.
+ *
+ *   base_out, lora_out  device [T, d_out], dtype; lora_out excludes s.
+ *   g                   device fp32 [d_out].
+ *   y                   device [T, d_out], dtype, output; may alias base_out
+ *                       exactly (in-place), must not partially overlap.
+ * T == 0 is a no-op; the activation pointers may then be NULL.
+ */
+int dora_compose(const void* base_out, const void* lora_out, const float* g, float s,
+                 int64_t T, int64_t d_out, int dtype, int delta_only, void* y, void* stream);
+
+/* Workspace bytes needed by dora_compose_backward when d_m != NULL. */
+int dora_compose_backward_workspace_size(int64_t T, int64_t d_out, size_t* bytes);
+
+/*
+ * Fused compose backward with the norm detached.
+ *
+ * [ScalingDoRA] §3 (backward kernel: d_lora and d_base in one pass; the
+ * magnitude gradient as a separate deterministic reduction, no atomics),
+ * Data Availability (norm detached); [DoRA-wiki] .detach() note:
+ *   d_base = g*dy          (delta_only: (g - 1)*dy)
+ *   d_lora = (g*s)*dy
+ *   d_m_j  = sum_t dy_tj*(base_tj + s*lora_tj) / max(wnorm_j, eps)
+ * d_m is summed in a fixed order, so results are bitwise reproducible.
+ *
+ *   dy                  device [T, d_out], dtype.
+ *   base_out, lora_out  device [T, d_out], dtype; read only when d_m != NULL
+ *                       (may be NULL otherwise).
+ *   g                   device fp32 [d_out]; wnorm device fp32 [d_out] (read
+ *                       only when d_m != NULL).
+ *   d_base, d_lora      device [T, d_out], dtype, outputs, each may be NULL
+ *                       to skip it; either may alias dy exactly.
+ *   d_m                 device fp32 [d_out], output (overwritten, not
+ *                       accumulated), or NULL when the magnitude is frozen.
+ *   workspace           needed only when d_m != NULL: at least
+ *                       dora_compose_backward_workspace_size() bytes,
+ *                       256-byte aligned, no initialisation needed.
+ * T == 0 writes zeros to d_m and nothing else; the activation pointers may
+ * then be NULL.
+ */
+int dora_compose_backward(const void* dy, const void* base_out, const void* lora_out,
+                          const float* g, const float* wnorm, float s, float eps, int64_t T,
+                          int64_t d_out, int dtype, int delta_only, void* d_base, void* d_lora,
+                          float* d_m, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DORA_H_ */

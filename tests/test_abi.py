@@ -1,0 +1,158 @@
+"""The C-ABI library: it loads, exports every symbol include/dora.h declares, and
+rejects bad arguments on the host before any launch (no GPU needed: every
+call here returns from validation, so no device memory is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import dora_adapter_factored_amd as D
+from dora_adapter_factored_amd import binding as Bn
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dora.h")
+FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: validation fails first
+FAKE_WS = ctypes.c_void_p(0x100000)   # 256-byte aligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(dora_\w+)\s*\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return D.load()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(D.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.dora_status_string(0) == b"ok"
+    assert lib.dora_status_string(3).startswith(b"workspace")
+    assert lib.dora_status_string(99) == b"unknown status"
+    assert lib.dora_version() >= 100
+
+
+def test_workspace_queries(lib):
+    n = ctypes.c_size_t()
+    assert lib.dora_factored_norm_workspace_size(8192, 8192, 384, 1, ctypes.byref(n)) == 0
+    # O(d_out r + r^2)-sized: far below the dense [d_out, d_in] product (128 MiB in bf16)
+    assert 0 < n.value < 16 << 20
+    assert lib.dora_factored_norm_workspace_size(64, 48, 8, 0, ctypes.byref(n)) == 0 and n.value > 0
+    assert lib.dora_factored_norm_workspace_size(0, 48, 8, 0, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
+    assert lib.dora_factored_norm_workspace_size(64, 48, 8, 7, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
+    assert lib.dora_factored_norm_workspace_size(64, 48, 8, 2, ctypes.byref(n)) == Bn.DORA_ERR_UNSUPPORTED
+    assert lib.dora_factored_norm_workspace_size(64, 48, 8, 1, None) == Bn.DORA_ERR_INVALID_ARG
+    assert lib.dora_compose_backward_workspace_size(2048, 8192, ctypes.byref(n)) == 0
+    assert n.value == 64 * 8192 * 4
+    assert lib.dora_compose_backward_workspace_size(0, 8192, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.dora_compose_backward_workspace_size(-1, 8192, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
+
+
+def _norm(lib, **kw):
+    a = dict(W0=FAKE, A=FAKE, B=FAKE, m=FAKE, d_out=64, d_in=48, r=8, dtype=1, s=1.0, eps=1e-6,
+             wnorm=FAKE, g=FAKE, ws=FAKE_WS, nbytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.dora_factored_norm(a["W0"], a["A"], a["B"], a["m"], a["d_out"], a["d_in"], a["r"], a["dtype"],
+                                  a["s"], a["eps"], a["wnorm"], a["g"], a["ws"], a["nbytes"], a["stream"])
+
+
+def test_norm_validation(lib):
+    E = Bn
+    assert _norm(lib, W0=None) == E.DORA_ERR_INVALID_ARG
+    assert _norm(lib, A=None) == E.DORA_ERR_INVALID_ARG
+    assert _norm(lib, B=None) == E.DORA_ERR_INVALID_ARG
+    assert _norm(lib, wnorm=None) == E.DORA_ERR_INVALID_ARG
+    assert _norm(lib, g=None) == E.DORA_ERR_INVALID_ARG          # m given without g
+    assert _norm(lib, d_out=0) == E.DORA_ERR_INVALID_ARG
+    assert _norm(lib, d_in=-3) == E.DORA_ERR_INVALID_ARG
+    assert _norm(lib, r=1 << 31) == E.DORA_ERR_INVALID_ARG
+    assert _norm(lib, dtype=5) == E.DORA_ERR_INVALID_ARG
+    assert _norm(lib, dtype=2) == E.DORA_ERR_UNSUPPORTED
+    assert _norm(lib, s=float("nan")) == E.DORA_ERR_INVALID_ARG
+    assert _norm(lib, eps=-1.0) == E.DORA_ERR_INVALID_ARG
+    assert _norm(lib, eps=float("inf")) == E.DORA_ERR_INVALID_ARG
+    assert _norm(lib, ws=None) == E.DORA_ERR_WORKSPACE
+    assert _norm(lib, nbytes=16) == E.DORA_ERR_WORKSPACE
+    assert _norm(lib, ws=ctypes.c_void_p(0x100010)) == E.DORA_ERR_WORKSPACE   # misaligned
+    assert b"256-byte" in lib.dora_last_error_detail()
+
+
+def _compose(lib, **kw):
+    a = dict(base=FAKE, lora=ctypes.c_void_p(0x20000), g=FAKE, s=1.0, T=4, d_out=8, dtype=1, delta=0,
+             y=ctypes.c_void_p(0x30000), stream=None)
+    a.update(kw)
+    return lib.dora_compose(a["base"], a["lora"], a["g"], a["s"], a["T"], a["d_out"], a["dtype"], a["delta"],
+                            a["y"], a["stream"])
+
+
+def test_compose_validation(lib):
+    E = Bn
+    assert _compose(lib, base=None) == E.DORA_ERR_INVALID_ARG
+    assert _compose(lib, lora=None) == E.DORA_ERR_INVALID_ARG
+    assert _compose(lib, g=None) == E.DORA_ERR_INVALID_ARG
+    assert _compose(lib, y=None) == E.DORA_ERR_INVALID_ARG
+    assert _compose(lib, T=-1) == E.DORA_ERR_INVALID_ARG
+    assert _compose(lib, d_out=0) == E.DORA_ERR_INVALID_ARG
+    assert _compose(lib, dtype=3) == E.DORA_ERR_INVALID_ARG
+    assert _compose(lib, delta=2) == E.DORA_ERR_INVALID_ARG
+    assert _compose(lib, s=float("inf")) == E.DORA_ERR_INVALID_ARG
+    assert _compose(lib, y=ctypes.c_void_p(0x20000)) == E.DORA_ERR_INVALID_ARG   # y aliases lora_out
+    # T == 0 is a no-op with NULL activations and launches nothing
+    assert _compose(lib, T=0, base=None, lora=None, y=None) == E.DORA_OK
+
+
+def _bwd(lib, **kw):
+    a = dict(dy=FAKE, base=FAKE, lora=FAKE, g=FAKE, wnorm=FAKE, s=1.0, eps=1e-6, T=64, d_out=8, dtype=1,
+             delta=0, db=ctypes.c_void_p(0x40000), dl=ctypes.c_void_p(0x50000), dm=FAKE, ws=FAKE_WS,
+             nbytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.dora_compose_backward(a["dy"], a["base"], a["lora"], a["g"], a["wnorm"], a["s"], a["eps"], a["T"],
+                                     a["d_out"], a["dtype"], a["delta"], a["db"], a["dl"], a["dm"], a["ws"],
+                                     a["nbytes"], a["stream"])
+
+
+def test_compose_backward_validation(lib):
+    E = Bn
+    assert _bwd(lib, dy=None) == E.DORA_ERR_INVALID_ARG
+    assert _bwd(lib, g=None) == E.DORA_ERR_INVALID_ARG
+    assert _bwd(lib, base=None) == E.DORA_ERR_INVALID_ARG        # d_m requested
+    assert _bwd(lib, lora=None) == E.DORA_ERR_INVALID_ARG
+    assert _bwd(lib, wnorm=None) == E.DORA_ERR_INVALID_ARG
+    assert _bwd(lib, T=-5) == E.DORA_ERR_INVALID_ARG
+    assert _bwd(lib, d_out=1 << 31) == E.DORA_ERR_INVALID_ARG
+    assert _bwd(lib, dtype=-1) == E.DORA_ERR_INVALID_ARG
+    assert _bwd(lib, delta=7) == E.DORA_ERR_INVALID_ARG
+    assert _bwd(lib, eps=-0.5) == E.DORA_ERR_INVALID_ARG
+    assert _bwd(lib, dl=ctypes.c_void_p(0x40000)) == E.DORA_ERR_INVALID_ARG   # d_base == d_lora
+    assert _bwd(lib, ws=None) == E.DORA_ERR_WORKSPACE
+    assert _bwd(lib, nbytes=4) == E.DORA_ERR_WORKSPACE
+    assert _bwd(lib, ws=ctypes.c_void_p(0x100004)) == E.DORA_ERR_WORKSPACE
+
+
+def test_binding_rejects_bad_tensors_before_the_library():
+    # host tensors are refused by the shape/device checks of the binding
+    cpu = torch.zeros(4, 8, dtype=torch.bfloat16)
+    g = torch.ones(8)
+    with pytest.raises(ValueError):
+        D.compose(cpu, torch.zeros(4, 9, dtype=torch.bfloat16), g, 1.0)
+    with pytest.raises(ValueError):
+        D.compose(cpu, cpu.t(), g, 1.0)
+    with pytest.raises(ValueError):
+        D.factored_norm(cpu, torch.zeros(2, 8, dtype=torch.float32), torch.zeros(4, 2, dtype=torch.bfloat16), 1.0)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(Bn, "_lib", None)
+    monkeypatch.setattr(Bn, "_LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        Bn.load()

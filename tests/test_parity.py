@@ -1,0 +1,367 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Inputs come from dora_inputs (seeded, synthetic); the oracle sees exact host
+copies of the tensors the GPU consumed.  Small cases are compared element by
+element; the full-size workloads (the bench's launch configuration) on
+sampled rows / columns the oracle computes one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import dora_adapter_factored_amd as D
+import dora_inputs as DI
+import oracle
+from parity_utils import NORM_RTOL, check_act, check_rel, host64, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+_layers = {}
+
+
+def config_layer(cfg):
+    if cfg not in _layers:
+        say(f"[parity] generating config {cfg} ({DI.CONFIGS[cfg].name})")
+        _layers[cfg] = DI.make_config(cfg, device=DEV)
+        torch.cuda.synchronize()
+    return _layers[cfg]
+
+
+def gpu_norm(L, s=None, m=True, eps=None):
+    s = L.spec.s if s is None else s
+    wn, g = D.factored_norm(L.W0, L.A, L.B, s, L.m if m else None, eps)
+    torch.cuda.synchronize()
+    return wn, g
+
+
+def oracle_norm(L, rows=None, s=None, eps=None):
+    s = L.spec.s if s is None else s
+    eps = D.default_eps(L.W0.dtype) if eps is None else eps
+    W0, A, B = L.W0.cpu(), L.A.cpu(), L.B.cpu()
+    wn = oracle.dense_row_norm(W0, A, B, s, rows=rows)
+    m = host64(L.m)
+    g = oracle.magnitude_scale(m if rows is None else m[rows], wn, eps)
+    return wn, g
+
+
+# ------------------------------------------------------------------ norm
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_norm_config(cfg):
+    L = config_layer(cfg)
+    say(f"[parity] norm config {cfg}")
+    wn, g = gpu_norm(L)
+    rows = None if L.spec.d_out <= 4096 else sample_rows(L.spec.d_out, 384, seed=cfg)
+    ref_wn, ref_g = oracle_norm(L, rows)
+    got_wn, got_g = host64(wn), host64(g)
+    if rows is not None:
+        got_wn, got_g = got_wn[rows], got_g[rows]
+        assert np.all(np.isfinite(host64(wn))) and np.all(host64(wn) > 0)
+    rtol = NORM_RTOL[L.W0.dtype]
+    check_rel(got_wn, ref_wn, rtol, f"cfg{cfg} wnorm")
+    check_rel(got_g, ref_g, rtol, f"cfg{cfg} g")
+
+
+EDGE_SHAPES = [
+    # d_out, d_in, r, dtype
+    (1000, 777, 13, "bf16"),     # nothing aligned: element-wise loads, ragged tiles
+    (1000, 777, 13, "f32"),
+    (1, 64, 1, "bf16"),          # single row, rank 1
+    (130, 40, 100, "bf16"),      # r > d_in, d_in below one K tile
+    (257, 512, 512, "bf16"),     # two slices of r
+    (200, 264, 777, "bf16"),     # three slices, ragged last slice
+    (96, 1032, 16, "bf16"),      # narrow-r tile
+    (300, 136, 384, "f32"),      # fp32 with two slices of r
+    (129, 256, 32, "bf16"), (129, 256, 64, "bf16"), (129, 256, 192, "bf16"), (129, 256, 384, "bf16"),
+    (64, 48, 8, "f32"), (64, 48, 8, "bf16"),
+]
+
+
+@pytest.mark.parametrize("d_out,d_in,r,dt", EDGE_SHAPES)
+def test_norm_edge_shapes(d_out, d_in, r, dt):
+    say(f"[parity] norm edge {d_out}x{d_in} r={r} {dt}")
+    spec = DI.custom_spec(d_out, d_in, r, 1, dtype=dt, s=1.5, b_std=0.05)
+    L = DI.make_layer(spec, 17 + d_out + r, device=DEV, activations=False)
+    wn, g = gpu_norm(L)
+    ref_wn, ref_g = oracle_norm(L)
+    check_rel(host64(wn), ref_wn, NORM_RTOL[L.W0.dtype], "wnorm")
+    check_rel(host64(g), ref_g, NORM_RTOL[L.W0.dtype], "g")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_norm_dominated_by_low_rank_term(dt):
+    # W0 = 0: the whole norm comes from the cross-free s^2 B G B^T term
+    say(f"[parity] norm W0=0 {dt}")
+    spec = DI.custom_spec(300, 520, 48, 1, dtype=dt, s=2.0, b_std=0.3)
+    L = DI.make_layer(spec, 5, device=DEV, activations=False, w_scale=0.0)
+    wn, _ = gpu_norm(L, m=False)
+    ref, _ = oracle_norm(L)
+    check_rel(host64(wn), ref, NORM_RTOL[L.W0.dtype], "wnorm W0=0")
+
+
+def test_norm_zero_row_eps_clamp():
+    say("[parity] zero row / eps clamp")
+    spec = DI.custom_spec(64, 128, 8, 1, dtype="bf16")
+    L = DI.make_layer(spec, 3, device=DEV, activations=False)
+    L.W0[5].zero_()
+    L.B[5].zero_()
+    eps = 0.25
+    wn, g = gpu_norm(L, eps=eps)
+    assert wn[5].item() == 0.0
+    assert g[5].item() == np.float32(L.m[5].item() / eps)
+    ref_wn, ref_g = oracle_norm(L, eps=eps)
+    check_rel(host64(wn)[np.arange(64) != 5], ref_wn[np.arange(64) != 5], 2e-3, "wnorm")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_norm_scale_zero(dt):
+    say(f"[parity] s = 0 {dt}")
+    spec = DI.custom_spec(333, 4104, 16, 1, dtype=dt)
+    L = DI.make_layer(spec, 9, device=DEV, activations=False)
+    wn, g = gpu_norm(L, s=0.0)
+    ref = np.linalg.norm(host64(L.W0), axis=1)
+    check_rel(host64(wn), ref, NORM_RTOL[L.W0.dtype], "wnorm s=0")
+
+
+def test_norm_deterministic():
+    L = config_layer(3)
+    say("[parity] norm determinism")
+    a = gpu_norm(L)
+    b = gpu_norm(L)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# --------------------------------------------------------------- compose
+def oracle_g_f32(L):
+    """g from the oracle, rounded to fp32: compose tests feed both sides this g."""
+    _, g = oracle_norm(L)
+    return torch.tensor(g, dtype=torch.float32)
+
+
+def _compose_check(L, g32, rows=None, delta=False, tag=""):
+    dt = L.base_out.dtype
+    s = L.spec.s
+    y = D.compose(L.base_out, L.lora_out, g32.to(DEV), s, delta_only=delta)
+    torch.cuda.synchronize()
+    base, lora, got = host64(L.base_out), host64(L.lora_out), host64(y)
+    if rows is not None:
+        base, lora, got = base[rows], lora[rows], got[rows]
+    ref = oracle.compose_forward(base, lora, oracle.as_f64(g32), s, delta_only=delta)
+    check_act(got, ref, dt, f"{tag} y(delta={delta})")
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_compose_forward_config(cfg):
+    L = config_layer(cfg)
+    say(f"[parity] compose fwd config {cfg}")
+    g32 = oracle_g_f32(L) if cfg != 4 else gpu_norm(L)[1].cpu()
+    rows = None if cfg in (1, 2) else sample_rows(L.spec.T, 256, seed=cfg)
+    _compose_check(L, g32, rows=rows, tag=f"cfg{cfg}")
+    _compose_check(L, g32, rows=rows, delta=True, tag=f"cfg{cfg}")
+
+
+def _bwd_check(L, g32, wn32, delta=False, rows=None, cols=None, tag=""):
+    dt = L.dy.dtype
+    s = L.spec.s
+    eps = D.default_eps(dt)
+    g, wn = g32.to(DEV), wn32.to(DEV)
+    db, dl, dm = D.compose_backward(L.dy, L.base_out, L.lora_out, g, wn, s, eps, delta_only=delta)
+    torch.cuda.synchronize()
+    csel = slice(None) if cols is None else cols
+    dy, base, lora = (host64(t)[:, csel] for t in (L.dy, L.base_out, L.lora_out))
+    r_db, r_dl, r_dm = oracle.compose_backward(dy, base, lora, oracle.as_f64(g32)[csel],
+                                               oracle.as_f64(wn32)[csel], s, eps, delta_only=delta)
+    got_db, got_dl = host64(db)[:, csel], host64(dl)[:, csel]
+    if rows is not None:
+        got_db, got_dl, r_db, r_dl = got_db[rows], got_dl[rows], r_db[rows], r_dl[rows]
+    check_act(got_db, r_db, dt, f"{tag} d_base")
+    check_act(got_dl, r_dl, dt, f"{tag} d_lora")
+    check_act(host64(dm)[csel], r_dm, dt, f"{tag} d_m")
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_compose_backward_config(cfg):
+    L = config_layer(cfg)
+    say(f"[parity] compose bwd config {cfg}")
+    if cfg == 4:
+        wn, g = gpu_norm(L)
+        g32, wn32 = g.cpu(), wn.cpu()
+        cols = sample_rows(L.spec.d_out, 256, seed=44)
+    else:
+        wn64, g64 = oracle_norm(L)
+        g32, wn32 = torch.tensor(g64, dtype=torch.float32), torch.tensor(wn64, dtype=torch.float32)
+        cols = None
+    rows = None if cfg in (1, 2) else sample_rows(L.spec.T, 256, seed=cfg + 1)
+    _bwd_check(L, g32, wn32, rows=rows, cols=cols, tag=f"cfg{cfg}")
+    if cfg in (1, 3):
+        _bwd_check(L, g32, wn32, delta=True, rows=rows, cols=cols, tag=f"cfg{cfg}")
+
+
+COMPOSE_EDGE = [
+    # T, d_out, dtype
+    (1, 1000, "bf16"), (37, 1000, "bf16"), (37, 1003, "bf16"), (5, 7, "f32"), (70, 517, "f32"),
+    (33, 520, "f16"), (65, 8, "bf16"), (2, 1, "bf16"), (300, 4104, "bf16"),
+]
+
+
+@pytest.mark.parametrize("T,d_out,dt", COMPOSE_EDGE)
+def test_compose_edge_shapes(T, d_out, dt):
+    say(f"[parity] compose edge T={T} d_out={d_out} {dt}")
+    torch.manual_seed(T * 1000 + d_out)
+    dtype = DI.DTYPES[dt]
+    base = torch.randn(T, d_out).to(dtype).to(DEV)
+    lora = torch.randn(T, d_out).to(dtype).to(DEV)
+    dy = torch.randn(T, d_out).to(dtype).to(DEV)
+    g32 = (1.0 + 1e-3 * torch.randn(d_out)).float()
+    wn32 = (1.0 + 0.1 * torch.rand(d_out)).float()
+    s = 0.75
+    y = D.compose(base, lora, g32.to(DEV), s)
+    db, dl, dm = D.compose_backward(dy, base, lora, g32.to(DEV), wn32.to(DEV), s, 1e-6)
+    torch.cuda.synchronize()
+    b64, l64, d64 = host64(base), host64(lora), host64(dy)
+    g64, w64 = oracle.as_f64(g32), oracle.as_f64(wn32)
+    check_act(host64(y), oracle.compose_forward(b64, l64, g64, s), dtype, "y")
+    r_db, r_dl, r_dm = oracle.compose_backward(d64, b64, l64, g64, w64, s, 1e-6)
+    tol_dtype = torch.bfloat16 if dtype == torch.float16 else dtype
+    check_act(host64(db), r_db, tol_dtype, "d_base")
+    check_act(host64(dl), r_dl, tol_dtype, "d_lora")
+    check_act(host64(dm), r_dm, tol_dtype, "d_m")
+
+
+def _misaligned(t):
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    v = buf[1:].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 16 != 0
+    return v
+
+
+def test_unaligned_pointers_take_the_scalar_path():
+    say("[parity] unaligned pointers")
+    L = DI.make_layer(DI.custom_spec(256, 512, 16, 64, dtype="bf16"), 21, device=DEV)
+    wn_a, g_a = gpu_norm(L)
+    W0u, Au, Bu = _misaligned(L.W0), _misaligned(L.A), _misaligned(L.B)
+    wn_u, g_u = D.factored_norm(W0u, Au, Bu, L.spec.s, L.m)
+    ref, _ = oracle_norm(L)
+    check_rel(host64(wn_u), ref, 2e-3, "wnorm unaligned")
+    bu, lu = _misaligned(L.base_out), _misaligned(L.lora_out)
+    y_a = D.compose(L.base_out, L.lora_out, g_a, L.spec.s)
+    y_u = D.compose(bu, lu, g_a, L.spec.s)
+    torch.cuda.synchronize()
+    assert torch.equal(y_a, y_u)   # same arithmetic on either path
+
+
+def test_t_zero():
+    say("[parity] T = 0")
+    g = torch.ones(64, device=DEV)
+    empty = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
+    y = D.compose(empty, empty, g, 1.0)
+    _, _, dm = D.compose_backward(empty, empty, empty, g, g, 1.0, 1e-6)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 64)
+    assert torch.equal(dm, torch.zeros(64, device=DEV))
+
+
+def test_init_exact_reproduces_base_output():
+    # m0 = ||W0||_row from the same GPU routine and B = 0: g == 1 exactly and
+    # y == base_out bitwise, delta == 0.
+    say("[parity] init exactness")
+    L = DI.make_layer(DI.custom_spec(1024, 2048, 64, 128, dtype="bf16", s=2.0), 31, device=DEV)
+    L.B.zero_()
+    DI.branch_outputs(L)
+    m0, _ = D.factored_norm(L.W0, L.A, L.B, 2.0)
+    _, g = D.factored_norm(L.W0, L.A, L.B, 2.0, m0.clone())
+    y = D.compose(L.base_out, L.lora_out, g, 2.0)
+    dlt = D.compose(L.base_out, L.lora_out, g, 2.0, delta_only=True)
+    torch.cuda.synchronize()
+    assert torch.equal(g, torch.ones_like(g))
+    assert torch.equal(y, L.base_out)
+    assert torch.count_nonzero(dlt).item() == 0
+
+
+def test_inplace_alias_and_frozen_magnitude():
+    say("[parity] aliasing and frozen m")
+    L = DI.make_layer(DI.custom_spec(512, 256, 16, 96, dtype="bf16"), 41, device=DEV)
+    _, g = gpu_norm(L)
+    y_ref = D.compose(L.base_out, L.lora_out, g, L.spec.s)
+    b = L.base_out.clone()
+    y_in = D.compose(b, L.lora_out, g, L.spec.s, out=b)
+    d_base, d_lora, _ = D.compose_backward(L.dy, None, None, g, None, L.spec.s, need_d_m=False)
+    dyc = L.dy.clone()
+    d_base2, _, _ = D.compose_backward(dyc, None, None, g, None, L.spec.s, need_d_m=False, need_d_lora=False,
+                                       d_base=dyc)
+    torch.cuda.synchronize()
+    assert torch.equal(y_in, y_ref)
+    assert torch.equal(d_base2, d_base)
+    ref_db, ref_dl, _ = oracle.compose_backward(host64(L.dy), host64(L.base_out), host64(L.lora_out),
+                                                host64(g), np.ones(512), L.spec.s, 1e-6)
+    check_act(host64(d_base), ref_db, torch.bfloat16, "d_base frozen")
+    check_act(host64(d_lora), ref_dl, torch.bfloat16, "d_lora frozen")
+
+
+def test_backward_deterministic():
+    L = config_layer(3)
+    say("[parity] bwd determinism")
+    wn, g = gpu_norm(L)
+    a = D.compose_backward(L.dy, L.base_out, L.lora_out, g, wn, L.spec.s)
+    a = tuple(t.clone() for t in a)
+    b = D.compose_backward(L.dy, L.base_out, L.lora_out, g, wn, L.spec.s)
+    torch.cuda.synchronize()
+    for x, z in zip(a, b):
+        assert torch.equal(x, z)
+
+
+def test_end_to_end_chain_against_oracle():
+    # GPU norm -> GPU g -> GPU compose, against the oracle's fp64 chain.
+    for cfg in (1, 3):
+        L = config_layer(cfg)
+        say(f"[parity] end-to-end chain config {cfg}")
+        wn, g = gpu_norm(L)
+        y = D.compose(L.base_out, L.lora_out, g, L.spec.s)
+        torch.cuda.synchronize()
+        rows = None if cfg == 1 else sample_rows(L.spec.T, 128, seed=5)
+        _, g_ref = oracle_norm(L)
+        base, lora = host64(L.base_out), host64(L.lora_out)
+        if rows is not None:
+            base, lora = base[rows], lora[rows]
+        ref = oracle.compose_forward(base, lora, g_ref, L.spec.s)
+        got = host64(y) if rows is None else host64(y)[rows]
+        check_act(got, ref, L.base_out.dtype, f"cfg{cfg} chain")
+
+
+def test_autograd_function_matches_direct_calls():
+    say("[parity] autograd wiring")
+    L = DI.make_layer(DI.custom_spec(256, 128, 8, 40, dtype="bf16"), 51, device=DEV)
+    wn, g = gpu_norm(L)
+    base = L.base_out.clone().requires_grad_(True)
+    lora = L.lora_out.clone().requires_grad_(True)
+    m = L.m.clone().requires_grad_(True)
+    eps = D.default_eps(torch.bfloat16)
+    y = D.DoRACompose.apply(base, lora, m, g, wn, L.spec.s, eps, False)
+    y.backward(L.dy)
+    db, dl, dm = D.compose_backward(L.dy, L.base_out, L.lora_out, g, wn, L.spec.s, eps)
+    torch.cuda.synchronize()
+    assert torch.equal(base.grad, db) and torch.equal(lora.grad, dl) and torch.equal(m.grad, dm)
+
+
+def test_sweep_layer_modules():
+    # one layer of the many-module sweep (7 projections), sampled rows
+    for proj in range(len(DI.SWEEP_PROJECTIONS)):
+        spec = DI.sweep_spec(proj)
+        say(f"[parity] sweep module {spec.name}")
+        L = DI.make_layer(spec, DI.sweep_seed(0, proj), device=DEV, activations=False)
+        wn, g = gpu_norm(L)
+        rows = sample_rows(spec.d_out, 128, seed=proj)
+        ref_wn, ref_g = oracle_norm(L, rows)
+        check_rel(host64(wn)[rows], ref_wn, 2e-3, f"{spec.name} wnorm")
+        check_rel(host64(g)[rows], ref_g, 2e-3, f"{spec.name} g")
+        del L
+        torch.cuda.empty_cache()
