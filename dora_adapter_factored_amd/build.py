@@ -23,10 +23,15 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ("dora_capi.hip", "compose.hip", "norm.hip")
 ARCH = "gfx950"
 
-# Packed-fp32 VALU ops are kept out of the device code.
+# Packed-fp32 VALU ops are kept out of the device code.  MFMA results are
+# kept in VGPR form: with the large accumulator tiles of the W0 pass the
+# default heuristics otherwise shuttle accumulators between AGPRs and VGPRs
+# every k-tile and spill to scratch; in VGPR form AGPRs only serve as spill
+# space and nothing reaches scratch memory.
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 

@@ -192,14 +192,30 @@ __global__ __launch_bounds__(kThreads) void compose_bwd_scalar(const T* dy, cons
     if (DM) dm_part[(int64_t)blockIdx.y * d_out + col] = acc;
 }
 
+// d_m_j = (sum over partial rows p of part[p][j]) / max(wnorm_j, eps).
+// A workgroup owns 64 columns; its 4 waves sum interleaved partial rows
+// (p = w, w + 4, ...) with independent loads in flight, then wave 0 adds the
+// four sums in wave order.  The order is fixed, so d_m is reproducible.
+constexpr int kFinCols = 64;
 __global__ __launch_bounds__(kThreads) void dm_finalize(const float* __restrict__ part, int nparts,
                                                         const float* __restrict__ wnorm, float eps,
                                                         int64_t d_out, float* __restrict__ d_m) {
-    const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (j >= d_out) return;
+    __shared__ float red[kThreads / kFinCols][kFinCols];
+    const int c = threadIdx.x % kFinCols, w = threadIdx.x / kFinCols;
+    const int64_t j = (int64_t)blockIdx.x * kFinCols + c;
     float acc = 0.0f;
-    for (int p = 0; p < nparts; ++p) acc += part[(int64_t)p * d_out + j];
-    d_m[j] = nparts > 0 ? acc / fmaxf(wnorm[j], eps) : 0.0f;
+    if (j < d_out) {
+#pragma unroll 8
+        for (int p = w; p < nparts; p += kThreads / kFinCols) acc += part[(int64_t)p * d_out + j];
+    }
+    red[w][c] = acc;
+    __syncthreads();
+    if (w == 0 && j < d_out) {
+        float v = red[0][c];
+#pragma unroll
+        for (int q = 1; q < kThreads / kFinCols; ++q) v += red[q][c];
+        d_m[j] = nparts > 0 ? v / fmaxf(wnorm[j], eps) : 0.0f;
+    }
 }
 
 inline bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -303,7 +319,7 @@ hipError_t bwd_typed(const void* dy, const void* base, const void* lora, const f
     }
     if (want_dm) {
         const int nparts = nrows > 0 ? bwd_parts(nrows) : 0;
-        dm_finalize<<<(unsigned)((d_out + kThreads - 1) / kThreads), kThreads, 0, st>>>(
+        dm_finalize<<<(unsigned)((d_out + kFinCols - 1) / kFinCols), kThreads, 0, st>>>(
             static_cast<const float*>(ws), nparts, wnorm, eps, d_out, d_m);
         return hipGetLastError();
     }

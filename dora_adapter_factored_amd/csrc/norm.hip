@@ -46,6 +46,25 @@ template <> struct Mma<bf16_t> {
     __device__ __forceinline__ static void mma(f32x4_t& c, const frag_t& a, const frag_t& b) {
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
+    // DMA layout: k-step ks, lane group q reads logical chunk 4 ks + q of a
+    // 128-byte row whose swizzle is sw.
+    __device__ __forceinline__ static frag_t load_frag_swz(const char* row, int ks, int q, int sw) {
+        return *reinterpret_cast<const bf16x8_t*>(row + (((ks * 4 + q) ^ sw) << 4));
+    }
+    __device__ __forceinline__ static float frag_sumsq(const frag_t& a) {
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = static_cast<float>(a[e]);
+            s = fmaf(x, x, s);
+        }
+        return s;
+    }
+    // A fragment held as FL = 1 sixteen-byte register packet.
+    static constexpr int FL = 1;
+    __device__ __forceinline__ static frag_t frag_from_regs(const u32x4_t* r) {
+        return __builtin_bit_cast(bf16x8_t, r[0]);
+    }
 };
 
 template <> struct Mma<float> {
@@ -65,6 +84,30 @@ template <> struct Mma<float> {
         for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[i], b.lo[i], c, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[i], b.hi[i], c, 0, 0, 0);
+    }
+    // DMA layout: one k-step per tile; lane group q reads logical chunks 2q
+    // and 2q + 1 (8 floats) of a 128-byte row whose swizzle is sw.
+    __device__ __forceinline__ static frag_t load_frag_swz(const char* row, int ks, int q, int sw) {
+        frag_t f;
+        f.lo = *reinterpret_cast<const f32x4_t*>(row + (((ks * 8 + 2 * q) ^ sw) << 4));
+        f.hi = *reinterpret_cast<const f32x4_t*>(row + (((ks * 8 + 2 * q + 1) ^ sw) << 4));
+        return f;
+    }
+    __device__ __forceinline__ static float frag_sumsq(const frag_t& a) {
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = fmaf(a.lo[e], a.lo[e], s);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = fmaf(a.hi[e], a.hi[e], s);
+        return s;
+    }
+    // A fragment held as FL = 2 sixteen-byte register packets.
+    static constexpr int FL = 2;
+    __device__ __forceinline__ static frag_t frag_from_regs(const u32x4_t* r) {
+        frag_t f;
+        f.lo = __builtin_bit_cast(f32x4_t, r[0]);
+        f.hi = __builtin_bit_cast(f32x4_t, r[1]);
+        return f;
     }
 };
 
@@ -112,39 +155,58 @@ __device__ __forceinline__ float chunk_sumsq(u32x4_t u) {
 }
 
 // Tile geometry of a workgroup: WM x WN waves, each wave MT x NT blocks of
-// 16 x 16 outputs.
+// 16 x 16 outputs.  A tile row holds BK elements = 128 bytes = 8 chunks.
 template <typename E, int WM, int WN, int MT, int NT>
 struct Tile {
-    static constexpr int NTH = WM * WN * 64;
+    static constexpr int NW = WM * WN;
+    static constexpr int NTH = NW * 64;
     static constexpr int BM = WM * MT * 16;
     static constexpr int BN = WN * NT * 16;
     static constexpr int BK = Mma<E>::BK;
     static constexpr int VEC = Mma<E>::VEC;
     static constexpr int CPR = BK / VEC;   // 16-byte chunks per tile row (8)
-    static constexpr int LD = BK + VEC;    // LDS row pitch: +16 bytes keeps 16 rows on distinct banks
-    static constexpr int LCH = (BM * CPR + NTH - 1) / NTH;
-    static constexpr int RCH = (BN * CPR + NTH - 1) / NTH;
-    static constexpr int BUF = (BM + BN) * LD;   // elements per LDS stage
-    static constexpr int LDS_BYTES = 2 * BUF * (int)sizeof(E);
     static_assert(CPR == 8, "tile rows are 8 chunks");
     static_assert(NTH % CPR == 0, "a thread keeps the same chunk column across tiles");
+
+    // Register-staged path (unaligned operands): rows padded by 16 bytes so
+    // that the 16 rows one MFMA fragment read touches fall on distinct banks.
+    static constexpr int LD = BK + VEC;
+    static constexpr int LCH = (BM * CPR + NTH - 1) / NTH;
+    static constexpr int RCH = (BN * CPR + NTH - 1) / NTH;
+    static constexpr int BUF = (BM + BN) * LD;
+    static constexpr int STAGED_BYTES = 2 * BUF * (int)sizeof(E);
+
+    // LDS-DMA path (aligned operands): unpadded 128-byte rows, chunk-swizzled;
+    // a ring of LS stages for the left operand (the HBM stream) and RS stages
+    // for the right operand (L2-resident).
+    static constexpr int LS = 3, RS = 2;
+    static constexpr int LBYTES = BM * 128, RBYTES = BN * 128;
+    static constexpr int DMA_BYTES = LS * LBYTES + RS * RBYTES;
+    static constexpr int LPW = BM / 8 / NW;   // left DMA instructions per wave per tile
+    static_assert(BM / 8 % NW == 0, "left tile splits evenly across waves");
+
 };
 
+// Register-staged main loop, used when operands are not 16-byte aligned.
 // Streams k-tiles [kt_begin, kt_end) of `c` through double-buffered LDS into
-// the MFMA accumulators.  When `base_rows` is set, the squares of every phase-0
-// left element are summed per thread (bsum[j] covers chunk j of the thread).
-template <typename E, int WM, int WN, int MT, int NT, bool ALIGNED>
-__device__ __forceinline__ void mainloop(const Contraction& c, int64_t m0, int64_t n0, int kt_begin,
-                                         int kt_end, bool base_rows, f32x4_t (&acc)[MT][NT],
-                                         float (&bsum)[Tile<E, WM, WN, MT, NT>::LCH], E* lds) {
+// the MFMA accumulators.  When base_dst is set, the squares of every phase-0
+// left element are summed and row partials written to base_dst[m].
+template <typename E, int WM, int WN, int MT, int NT>
+__device__ __forceinline__ void mainloop_staged(const Contraction& c, int64_t m0, int64_t n0, int kt_begin,
+                                                int kt_end, float* base_dst, int64_t d_out,
+                                                f32x4_t (&acc)[MT][NT], char* smem) {
     typedef Tile<E, WM, WN, MT, NT> TL;
     typedef Mma<E> M;
+    E* lds = reinterpret_cast<E*>(smem);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int cc = tid % TL::CPR;   // chunk column, fixed for this thread
 
     u32x4_t lreg[TL::LCH], rreg[TL::RCH];
+    float bsum[TL::LCH];
+#pragma unroll
+    for (int j = 0; j < TL::LCH; ++j) bsum[j] = 0.0f;
 
     auto load_tile = [&](int kt) {
         const bool ph0 = kt < c.nkt0;
@@ -155,13 +217,13 @@ __device__ __forceinline__ void mainloop(const Contraction& c, int64_t m0, int64
         for (int j = 0; j < TL::LCH; ++j) {
             const int ch = tid + j * TL::NTH;
             if (TL::BM * TL::CPR % TL::NTH == 0 || ch < TL::BM * TL::CPR)
-                lreg[j] = load_chunk<E, ALIGNED>(L, m0 + ch / TL::CPR, k);
+                lreg[j] = load_chunk<E, false>(L, m0 + ch / TL::CPR, k);
         }
 #pragma unroll
         for (int j = 0; j < TL::RCH; ++j) {
             const int ch = tid + j * TL::NTH;
             if (TL::BN * TL::CPR % TL::NTH == 0 || ch < TL::BN * TL::CPR)
-                rreg[j] = load_chunk<E, ALIGNED>(R, n0 + ch / TL::CPR, k);
+                rreg[j] = load_chunk<E, false>(R, n0 + ch / TL::CPR, k);
         }
     };
     auto store_tile = [&](int buf, bool ph0) {
@@ -172,7 +234,7 @@ __device__ __forceinline__ void mainloop(const Contraction& c, int64_t m0, int64
             const int ch = tid + j * TL::NTH;
             if (TL::BM * TL::CPR % TL::NTH == 0 || ch < TL::BM * TL::CPR) {
                 *reinterpret_cast<u32x4_t*>(Ls + (ch / TL::CPR) * TL::LD + cc * TL::VEC) = lreg[j];
-                if (base_rows && ph0) bsum[j] += chunk_sumsq<E>(lreg[j]);
+                if (base_dst && ph0) bsum[j] += chunk_sumsq<E>(lreg[j]);
             }
         }
 #pragma unroll
@@ -199,18 +261,414 @@ __device__ __forceinline__ void mainloop(const Contraction& c, int64_t m0, int64
         }
     };
 
-    if (kt_begin >= kt_end) return;
-    load_tile(kt_begin);
-    store_tile(0, kt_begin < c.nkt0);
-    __syncthreads();
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-        const int buf = (kt - kt_begin) & 1;
-        const bool more = kt + 1 < kt_end;
-        if (more) load_tile(kt + 1);
-        compute(buf);
-        if (more) store_tile(buf ^ 1, kt + 1 < c.nkt0);
+    if (kt_begin < kt_end) {
+        load_tile(kt_begin);
+        store_tile(0, kt_begin < c.nkt0);
         __syncthreads();
+        for (int kt = kt_begin; kt < kt_end; ++kt) {
+            const int buf = (kt - kt_begin) & 1;
+            const bool more = kt + 1 < kt_end;
+            if (more) load_tile(kt + 1);
+            compute(buf);
+            if (more) store_tile(buf ^ 1, kt + 1 < c.nkt0);
+            __syncthreads();
+        }
     }
+    if (base_dst) {
+        // the 8 threads of a row hold its 8 chunk columns
+#pragma unroll
+        for (int j = 0; j < TL::LCH; ++j) {
+            float v = bsum[j];
+            v += __shfl_xor(v, 1);
+            v += __shfl_xor(v, 2);
+            v += __shfl_xor(v, 4);
+            const int ch = tid + j * TL::NTH;
+            const int64_t m = m0 + ch / TL::CPR;
+            if (cc == 0 && ch < TL::BM * TL::CPR && m < d_out) base_dst[m] = v;
+        }
+    }
+}
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Buffer load of 4 dwords per lane straight into LDS (M0-based destination,
+// lane l writes 16 bytes at dst + 16 l).  An offset at or beyond the buffer's
+// size reads zeros.
+__device__ void raw_buffer_load_lds(i32x4_t rsrc, lds_void_t* lds, int size, int voffset, int soffset,
+                                    int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+constexpr int kOutOfRange = (int)0x80000000;
+
+// Chunk swizzle of the DMA layout: logical chunk c of tile row i sits in
+// physical slot c ^ swz(i).  Any 8 consecutive rows, and the even (odd) rows
+// of any aligned 16 rows, map one logical chunk to 8 distinct slots, so a
+// 16-row fragment read is free of bank conflicts with 32 or 64 banks.  Within
+// a DMA group of 8 rows the swizzle depends only on the group's parity.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// s_waitcnt on vector-memory operations only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One operand of one phase as the DMA sees it: a buffer starting at the
+// workgroup's first tile row, sized to the rows that exist, so rows past the
+// operand read zeros.  A lane's chunk depends on the parity of its 8-row
+// group (the swizzle flips with row bit 3), so offsets come in two flavours.
+struct DmaSrc {
+    i32x4_t rsrc;
+    int ld_bytes, kmax_bytes;
+    int off_even, off_odd;       // lane byte offset inside an even / odd group
+    int chunk_even, chunk_odd;   // byte offset of the lane's chunk within its row
+};
+
+template <typename E>
+__device__ __forceinline__ DmaSrc make_dma_src(const Operand& o, int64_t row0, int lane) {
+    DmaSrc d;
+    const int64_t ldb = o.ld * (int64_t)sizeof(E);
+    const uint64_t addr = reinterpret_cast<uint64_t>(static_cast<const char*>(o.p) + row0 * ldb);
+    int64_t bytes = (o.rows - row0) * ldb;
+    if (bytes < 0) bytes = 0;
+    if (bytes > 0x7ffffff0) bytes = 0x7ffffff0;
+    d.rsrc[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+    d.rsrc[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32));
+    d.rsrc[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    d.rsrc[3] = 0x00020000;
+    d.ld_bytes = (int)ldb;
+    d.kmax_bytes = (int)(o.kmax * (int64_t)sizeof(E));
+    const int r_in = lane >> 3;
+    d.chunk_even = ((lane & 7) ^ r_in) * 16;
+    d.chunk_odd = ((lane & 7) ^ r_in ^ 1) * 16;
+    d.off_even = r_in * (int)ldb + d.chunk_even;
+    d.off_odd = r_in * (int)ldb + d.chunk_odd;
+    return d;
+}
+
+// Enqueue the DMA of tile rows [0, ROWS) at K byte offset k0b into LDS at
+// dst.  One instruction moves a group of 8 rows (1 KiB): lane l fills slot
+// l % 8 of row l / 8 with the logical chunk the swizzle puts there.  The
+// groups are dealt to waves [W_FIRST, W_FIRST + W_COUNT); other waves issue
+// nothing.  Chunks past the K extent of the operand read zeros.
+template <int ROWS, int W_FIRST, int W_COUNT>
+__device__ __forceinline__ void dma_tile(const DmaSrc& d, int k0b, char* dst, int wave, int tile_kbytes) {
+    constexpr int GROUPS = ROWS / 8;
+    if (wave < W_FIRST || wave >= W_FIRST + W_COUNT) return;
+    const int w = wave - W_FIRST;
+    const bool full = k0b + tile_kbytes <= d.kmax_bytes;
+    const int kleft = d.kmax_bytes - k0b;
+#pragma unroll
+    for (int q = 0; q < (GROUPS + W_COUNT - 1) / W_COUNT; ++q) {
+        const int grp = w + q * W_COUNT;
+        if (GROUPS % W_COUNT == 0 || grp < GROUPS) {
+            const bool odd = grp & 1;
+            int voff = (odd ? d.off_odd : d.off_even) + grp * 8 * d.ld_bytes + k0b;
+            if (!full) voff = (odd ? d.chunk_odd : d.chunk_even) < kleft ? voff : kOutOfRange;
+            raw_buffer_load_lds(d.rsrc, (lds_void_t*)(dst + grp * 1024), 16, voff, 0, 0, 0);
+        }
+    }
+}
+
+// LDS-DMA main loop for 16-byte aligned operands.  Tiles go global -> LDS
+// without passing through registers (global -> VGPR loads interleaved with
+// MFMA measure ~40% slower): the left operand (W0, streamed from HBM) runs
+// LS = 3 stages deep, i.e. is requested two k-tiles ahead, the right operand
+// (A or Gs, L2-resident) RS = 2 stages, one tile ahead.  Per k-tile j:
+//   wait for this thread's DMA of tiles <= j (only left(j+1) may be pending),
+//   barrier (all threads' DMA landed; stage of tile j-1 free),
+//   enqueue right(j+1) and left(j+2), then MFMA over tile j.
+// The walk over the k-tiles starts at tile `rot`: with a power-of-two row
+// pitch, workgroups that walk K in lockstep read the same column offset of
+// every row and pile onto a few memory channels; rotating the start spreads
+// them.  The base term is summed from the left fragments the MFMAs consume;
+// the WN waves sharing a row block split its 16-row blocks between them.
+template <typename E, int WM, int WN, int MT, int NT, bool ROLES>
+__device__ __forceinline__ void mainloop_dma(const Contraction& c, int64_t m0, int64_t n0, int kt_begin,
+                                             int kt_end, int rot, float* base_dst, int64_t d_out,
+                                             f32x4_t (&acc)[MT][NT], char* smem) {
+    typedef Tile<E, WM, WN, MT, NT> TL;
+    typedef Mma<E> M;
+    static_assert(TL::NW % 2 == 0, "DMA lane offsets assume an even wave count");
+    constexpr int TKB = TL::BK * (int)sizeof(E);   // bytes of K per tile row (128)
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int q = lane >> 4;
+    char* lring = smem;
+    char* rring = smem + TL::LS * TL::LBYTES;
+
+    const DmaSrc L0 = make_dma_src<E>(c.left0, m0, lane);
+    const DmaSrc R0 = make_dma_src<E>(c.right0, n0, lane);
+    const DmaSrc L1 = make_dma_src<E>(c.left1, m0, lane);
+    const DmaSrc R1 = make_dma_src<E>(c.right1, n0, lane);
+    // Load roles.  Vector-memory loads complete in issue order per wave, so a
+    // wave that issues both streams makes every L2-resident right tile wait
+    // behind the HBM-latency left tile issued before it.  With ROLES, wave 0
+    // issues all left (W0) DMA and waves 1.. all right (A / Gs) DMA, and each
+    // waits only on its own queue.
+    constexpr int LW0 = 0, LWN = ROLES ? 1 : TL::NW;
+    constexpr int RW0 = ROLES ? 1 : 0, RWN = ROLES ? TL::NW - 1 : TL::NW;
+    constexpr int LPI = (TL::BM / 8 + LWN - 1) / LWN;   // left DMA instructions per issuing wave per tile
+
+    int lrow[MT], lsw[MT], rrow[NT], rsw[NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        lrow[mt] = wm * MT * 16 + mt * 16 + (lane & 15);
+        lsw[mt] = swz(lrow[mt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        rrow[nt] = wn * NT * 16 + nt * 16 + (lane & 15);
+        rsw[nt] = swz(rrow[nt]);
+    }
+    float bs[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) bs[mt] = 0.0f;
+
+    const int n = kt_end - kt_begin;
+    // k-tile visited at step i (the walk starts at a rotated tile)
+    auto tile = [&](int i) __attribute__((always_inline)) {
+        int t = i + rot;
+        if (t >= n) t -= n;
+        return kt_begin + t;
+    };
+    auto issue_left = [&](int i, int stage) __attribute__((always_inline)) {
+        const int kt = tile(i);
+        char* dst = lring + stage * TL::LBYTES;
+        if (kt < c.nkt0)
+            dma_tile<TL::BM, LW0, LWN>(L0, kt * TKB, dst, wave, TKB);
+        else
+            dma_tile<TL::BM, LW0, LWN>(L1, (kt - c.nkt0) * TKB, dst, wave, TKB);
+    };
+    auto issue_right = [&](int i, int stage) __attribute__((always_inline)) {
+        const int kt = tile(i);
+        char* dst = rring + stage * TL::RBYTES;
+        if (kt < c.nkt0)
+            dma_tile<TL::BN, RW0, RWN>(R0, kt * TKB, dst, wave, TKB);
+        else
+            dma_tile<TL::BN, RW0, RWN>(R1, (kt - c.nkt0) * TKB, dst, wave, TKB);
+    };
+    auto compute = [&](const char* Lt, const char* Rt, bool base) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < TL::BK / 32; ++ks) {
+            typename M::frag_t a[MT], b[NT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) a[mt] = M::load_frag_swz(Lt + lrow[mt] * 128, ks, q, lsw[mt]);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) b[nt] = M::load_frag_swz(Rt + rrow[nt] * 128, ks, q, rsw[nt]);
+            if (base) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    if (mt % WN == wn) bs[mt] += M::frag_sumsq(a[mt]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) M::mma(acc[mt][nt], a[mt], b[nt]);
+        }
+    };
+
+    // Per k-tile j: wait for this thread's DMA of tiles <= j (only left(j+1)
+    // may still be in flight), barrier (every thread's DMA landed, and the
+    // stages of tile j-1 are free), enqueue right(j+1) and left(j+2), then
+    // MFMA over tile j.  Left runs 3 stages deep, right 2.
+    if (n > 0) {
+        issue_left(0, 0);
+        issue_right(0, 0);
+        if (n > 1) issue_left(1, 1);
+        int ls = 0, rs = 0;   // stages holding the tile of step j
+        for (int j = 0; j < n; ++j) {
+            // this wave's DMA of tile j is done; only its left(j+1) may be pending
+            const bool left_issuer = wave >= LW0 && wave < LW0 + LWN;
+            if (j + 1 < n && left_issuer)
+                wait_vmcnt<ROLES ? LPI : TL::LPW>();
+            else
+                wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+            const int rs_next = rs ^ 1;
+            const int ls_next2 = ls == 0 ? 2 : ls - 1;   // (ls + 2) % 3
+            if (j + 1 < n) issue_right(j + 1, rs_next);
+            if (j + 2 < n) issue_left(j + 2, ls_next2);
+            compute(lring + ls * TL::LBYTES, rring + rs * TL::RBYTES, base_dst != nullptr && tile(j) < c.nkt0);
+            ls = ls == 2 ? 0 : ls + 1;
+            rs = rs_next;
+        }
+    }
+    __builtin_amdgcn_s_barrier();   // LDS is free for the caller's epilogue
+    if (base_dst) {
+        // lanes l, l+16, l+32, l+48 hold the four chunk columns of one row
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if (mt % WN != wn) continue;
+            float v = bs[mt];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            const int64_t m = m0 + wm * MT * 16 + mt * 16 + lane;
+            if (lane < 16 && m < d_out) base_dst[m] = v;
+        }
+    }
+}
+
+// Buffer load of 16 bytes per lane into registers; offsets at or beyond the
+// buffer's size read zeros.
+__device__ i32x4_t raw_buffer_load_b128(i32x4_t rsrc, int voffset, int soffset, int aux) __asm(
+    "llvm.amdgcn.raw.buffer.load.v4i32");
+
+// One operand of one phase as seen by direct-to-register fragment loads: a
+// buffer starting at the first of the 16-row blocks this wave reads.  Lane l
+// reads row l % 16 of a block, K elements 8 (l / 16) .. 8 (l / 16) + 7 of a
+// 32-element k-step (FL packets of 16 bytes).
+struct FragSrc {
+    i32x4_t rsrc;
+    int ld_bytes, kmax_bytes, lane_off, kq_bytes;
+};
+
+template <typename E>
+__device__ __forceinline__ FragSrc make_frag_src(const Operand& o, int64_t row0, int lane) {
+    FragSrc f;
+    const int64_t ldb = o.ld * (int64_t)sizeof(E);
+    const uint64_t addr = reinterpret_cast<uint64_t>(static_cast<const char*>(o.p) + row0 * ldb);
+    int64_t bytes = (o.rows - row0) * ldb;
+    if (bytes < 0) bytes = 0;
+    if (bytes > 0x7ffffff0) bytes = 0x7ffffff0;
+    f.rsrc[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+    f.rsrc[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32));
+    f.rsrc[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    f.rsrc[3] = 0x00020000;
+    f.ld_bytes = (int)ldb;
+    f.kmax_bytes = (int)(o.kmax * (int64_t)sizeof(E));
+    f.kq_bytes = (lane >> 4) * 8 * (int)sizeof(E);
+    f.lane_off = (lane & 15) * (int)ldb + f.kq_bytes;
+    return f;
+}
+
+// Load the fragments of NB consecutive 16-row blocks for every k-step of the
+// k-tile starting at element k0: regs[(ks * NB + b) * FL + h].
+template <typename E, int NB>
+__device__ __forceinline__ void load_frags(const FragSrc& f, int64_t k0, u32x4_t* regs) {
+    typedef Mma<E> M;
+    constexpr int FR = M::BK / 32, FL = M::FL;
+#pragma unroll
+    for (int ks = 0; ks < FR; ++ks) {
+        const int kb = (int)((k0 + ks * 32) * (int64_t)sizeof(E));
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+            for (int h = 0; h < FL; ++h) {
+                const bool ok = kb + f.kq_bytes + h * 16 < f.kmax_bytes;
+                const int voff = ok ? f.lane_off + b * 16 * f.ld_bytes + kb + h * 16 : kOutOfRange;
+                regs[(ks * NB + b) * FL + h] =
+                    __builtin_bit_cast(u32x4_t, raw_buffer_load_b128(f.rsrc, voff, 0, 0));
+            }
+        }
+    }
+}
+
+// W0 pass main loop, narrow form (small r: 4 waves stacked along d_out, MT
+// blocks each, all NT blocks of r per wave).  Nothing is shared between
+// waves, so both operands are loaded straight into registers, four register
+// sets deep (three tiles in flight), with no LDS and no barrier.  K-walk
+// rotated as in the wide form.
+template <typename E, int MT, int NT>
+__device__ __forceinline__ void mainloop_w0_narrow(const Contraction& c, int64_t m0, int64_t n0, int kt_begin,
+                                                   int kt_end, int rot, float* base_dst, int64_t d_out,
+                                                   f32x4_t (&acc)[MT][NT]) {
+    typedef Mma<E> M;
+    constexpr int FR = M::BK / 32, FL = M::FL;
+    constexpr int NLW = FR * MT * FL, NRW = FR * NT * FL;   // loads per wave per tile
+    constexpr int PER = NLW + NRW;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = kt_end - kt_begin;
+    if (n <= 0) return;
+    const int64_t mrow0 = m0 + wave * MT * 16;
+    const FragSrc L0 = make_frag_src<E>(c.left0, mrow0, lane);
+    const FragSrc L1 = make_frag_src<E>(c.left1, mrow0, lane);
+    const FragSrc R0 = make_frag_src<E>(c.right0, n0, lane);
+    const FragSrc R1 = make_frag_src<E>(c.right1, n0, lane);
+    float bs[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) bs[mt] = 0.0f;
+
+    auto tile = [&](int i) __attribute__((always_inline)) {
+        int t = i + rot;
+        if (t >= n) t -= n;
+        return kt_begin + t;
+    };
+    auto load = [&](int i, u32x4_t* regs) __attribute__((always_inline)) {
+        const int kt = tile(i);
+        if (kt < c.nkt0) {
+            load_frags<E, MT>(L0, (int64_t)kt * M::BK, regs);
+            load_frags<E, NT>(R0, (int64_t)kt * M::BK, regs + NLW);
+        } else {
+            load_frags<E, MT>(L1, (int64_t)(kt - c.nkt0) * M::BK, regs);
+            load_frags<E, NT>(R1, (int64_t)(kt - c.nkt0) * M::BK, regs + NLW);
+        }
+    };
+    auto compute = [&](const u32x4_t* regs, bool base) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < FR; ++ks) {
+            typename M::frag_t a[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                a[mt] = M::frag_from_regs(regs + (ks * MT + mt) * FL);
+                if (base) bs[mt] += M::frag_sumsq(a[mt]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const typename M::frag_t b = M::frag_from_regs(regs + NLW + (ks * NT + nt) * FL);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) M::mma(acc[mt][nt], a[mt], b);
+            }
+        }
+    };
+    auto step = [&](int i, u32x4_t* cur, u32x4_t* nxt3) __attribute__((always_inline)) {
+        if (i + 2 < n)
+            wait_vmcnt<2 * PER>();
+        else if (i + 1 < n)
+            wait_vmcnt<PER>();
+        else
+            wait_vmcnt<0>();
+        if (i + 3 < n) load(i + 3, nxt3);   // set of tile i - 1, already consumed
+        compute(cur, base_dst != nullptr && tile(i) < c.nkt0);
+    };
+
+    u32x4_t s0[PER], s1[PER], s2[PER], s3[PER];
+    load(0, s0);
+    if (n > 1) load(1, s1);
+    if (n > 2) load(2, s2);
+    for (int i = 0; i < n; i += 4) {
+        step(i, s0, s3);
+        if (i + 1 >= n) break;
+        step(i + 1, s1, s0);
+        if (i + 2 >= n) break;
+        step(i + 2, s2, s1);
+        if (i + 3 >= n) break;
+        step(i + 3, s3, s2);
+    }
+    if (base_dst) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            float v = bs[mt];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            const int64_t m = mrow0 + mt * 16 + lane;
+            if (lane < 16 && m < d_out) base_dst[m] = v;
+        }
+    }
+}
+
+template <typename E, int WM, int WN, int MT, int NT, bool ALIGNED>
+__device__ __forceinline__ void mainloop(const Contraction& c, int64_t m0, int64_t n0, int kt_begin, int kt_end,
+                                         int rot, float* base_dst, int64_t d_out, f32x4_t (&acc)[MT][NT],
+                                         char* smem) {
+    if constexpr (ALIGNED)
+        mainloop_dma<E, WM, WN, MT, NT, false>(c, m0, n0, kt_begin, kt_end, rot, base_dst, d_out, acc, smem);
+    else
+        mainloop_staged<E, WM, WN, MT, NT>(c, m0, n0, kt_begin, kt_end, base_dst, d_out, acc, smem);
 }
 
 // ------------------------------------------------------------- W0 pass
@@ -224,11 +682,26 @@ struct W0PassArgs {
     float* part_cross;      // [n_ntiles * ksplit][d_out]
 };
 
+template <int WM, int WN, int MT, int NT, bool ALIGNED>
+struct W0Form {
+    static constexpr bool WIDE = ALIGNED && WM == 1 && WN == 4 && MT == 8;
+    static constexpr bool NARROW = ALIGNED && WN == 1;
+};
+
 template <typename E, int WM, int WN, int MT, int NT, bool ALIGNED>
 __global__ __launch_bounds__(WM * WN * 64) void w0_pass(W0PassArgs a) {
     typedef Tile<E, WM, WN, MT, NT> TL;
-    __shared__ __attribute__((aligned(16))) char smem[TL::LDS_BYTES];
-    E* lds = reinterpret_cast<E*>(smem);
+    typedef W0Form<WM, WN, MT, NT, ALIGNED> F;
+    static_assert(!ALIGNED || F::WIDE || F::NARROW, "aligned W0 pass needs the wide or narrow form");
+    constexpr int RED_BYTES = WN * TL::BM * 4;
+    // epilogue staging of the workgroup's B tile: rows padded by 16 bytes so
+    // that the four row groups one fragment read touches use distinct banks
+    constexpr int B_SLOTS = TL::BN * (int)sizeof(E) / 16 + 1;   // 16-byte slots per row
+    constexpr int B_PITCH = B_SLOTS * 16;
+    constexpr int B_BYTES = ALIGNED ? TL::BM * B_PITCH : 0;
+    constexpr int EPI = B_BYTES + RED_BYTES;
+    constexpr int MAIN = F::WIDE ? TL::DMA_BYTES : (F::NARROW ? 0 : TL::STAGED_BYTES);
+    __shared__ __attribute__((aligned(1024))) char smem[MAIN > EPI ? MAIN : EPI];
 
     // Workgroup -> (m-tile, n-tile, k-chunk).  Workgroups are handed to the 8
     // XCDs round-robin; when possible all workgroups of one XCD share the same
@@ -258,54 +731,92 @@ __global__ __launch_bounds__(WM * WN * 64) void w0_pass(W0PassArgs a) {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float bsum[TL::LCH];
-#pragma unroll
-    for (int j = 0; j < TL::LCH; ++j) bsum[j] = 0.0f;
 
-    mainloop<E, WM, WN, MT, NT, ALIGNED>(a.c, m0, n0, kt_begin, kt_end, base_rows, acc, bsum, lds);
+    float* base_dst = base_rows ? a.part_base + (int64_t)kc * a.d_out : nullptr;
+    // rotated start of the K walk (see mainloop_dma)
+    const int nk = kt_end - kt_begin;
+    const int rot = nk > 0 ? (int)(((unsigned)id * 7u + ((unsigned)id >> 3) * 3u) % (unsigned)nk) : 0;
+    if constexpr (F::WIDE)
+        mainloop_dma<E, WM, WN, MT, NT, false>(a.c, m0, n0, kt_begin, kt_end, rot, base_dst, a.d_out, acc, smem);
+    else if constexpr (F::NARROW)
+        mainloop_w0_narrow<E, MT, NT>(a.c, m0, n0, kt_begin, kt_end, rot, base_dst, a.d_out, acc);
+    else
+        mainloop_staged<E, WM, WN, MT, NT>(a.c, m0, n0, kt_begin, kt_end, base_dst, a.d_out, acc, smem);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 
-    // base partial: the 8 threads of a row hold the 8 chunk columns
-    if (base_rows) {
-#pragma unroll
-        for (int j = 0; j < TL::LCH; ++j) {
-            float v = bsum[j];
-            v += __shfl_xor(v, 1);
-            v += __shfl_xor(v, 2);
-            v += __shfl_xor(v, 4);
-            const int ch = tid + j * TL::NTH;
-            const int64_t m = m0 + ch / TL::CPR;
-            if ((tid % TL::CPR) == 0 && ch < TL::BM * TL::CPR && m < a.d_out)
-                a.part_base[(int64_t)kc * a.d_out + m] = v;
-        }
-    }
-
     // cross partial: sum_n B[m][n] * acc[m][n] over this workgroup's columns.
     // acc[mt][nt][j] is row wm*MT*16 + mt*16 + 4*(lane/16) + j, column
     // wn*NT*16 + nt*16 + lane%16 of the tile.
-    const E* Bp = static_cast<const E*>(a.B);
-    float* red = reinterpret_cast<float*>(smem);   // [WN][BM], LDS is free after the main loop
+    float* red = reinterpret_cast<float*>(smem + B_BYTES);   // [WN][BM]
+    if constexpr (ALIGNED) {
+        // Stage B[m0 .., n0 ..] (BM x BN) in LDS with one coalesced DMA pass;
+        // rows past d_out and columns past r read zeros.
+        const int64_t rb = a.r * (int64_t)sizeof(E);
+        const uint64_t addr = reinterpret_cast<uint64_t>(static_cast<const char*>(a.B) + m0 * rb);
+        int64_t bytes = (a.d_out - m0) * rb;
+        if (bytes > 0x7ffffff0) bytes = 0x7ffffff0;
+        i32x4_t rs;
+        rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+        rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32));
+        rs[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+        rs[3] = 0x00020000;
+        const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+        const int colb0 = (int)(n0 * (int64_t)sizeof(E));
+        constexpr int NINS = (TL::BM * B_SLOTS + 63) / 64;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = wm * MT * 16 + mt * 16 + 4 * (lane >> 4) + j;
-            const int64_t m = m0 + row;
-            float v = 0.0f;
-            if (m < a.d_out) {
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const int64_t n = n0 + wn * NT * 16 + nt * 16 + (lane & 15);
-                    if (n < a.r) v = fmaf(Cvt<E>::to_f(Bp[m * a.r + n]), acc[mt][nt][j], v);
-                }
+        for (int k = 0; k < (NINS + TL::NW - 1) / TL::NW; ++k) {
+            const int ins = wave_u + k * TL::NW;
+            if (NINS % TL::NW == 0 || ins < NINS) {
+                const int slot = ins * 64 + lane;
+                const int row = slot / B_SLOTS, ch = slot % B_SLOTS;
+                const int colb = colb0 + ch * 16;
+                const bool ok = ch < B_SLOTS - 1 && row < TL::BM && colb < (int)rb;
+                const int voff = ok ? row * (int)rb + colb : kOutOfRange;
+                raw_buffer_load_lds(rs, (lds_void_t*)(smem + ins * 1024), 16, voff, 0, 0, 0);
             }
-            v += __shfl_xor(v, 1);
-            v += __shfl_xor(v, 2);
-            v += __shfl_xor(v, 4);
-            v += __shfl_xor(v, 8);
-            if ((lane & 15) == 0) red[wn * TL::BM + row] = v;
+        }
+        wait_vmcnt<0>();
+        __syncthreads();
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = wm * MT * 16 + mt * 16 + 4 * (lane >> 4) + j;
+                const E* brow = reinterpret_cast<const E*>(smem + row * B_PITCH) + wn * NT * 16 + (lane & 15);
+                float v = 0.0f;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) v = fmaf(Cvt<E>::to_f(brow[nt * 16]), acc[mt][nt][j], v);
+                v += __shfl_xor(v, 1);
+                v += __shfl_xor(v, 2);
+                v += __shfl_xor(v, 4);
+                v += __shfl_xor(v, 8);
+                if ((lane & 15) == 0) red[wn * TL::BM + row] = v;
+            }
+        }
+    } else {
+        const E* Bp = static_cast<const E*>(a.B);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = wm * MT * 16 + mt * 16 + 4 * (lane >> 4) + j;
+                const int64_t m = m0 + row;
+                float v = 0.0f;
+                if (m < a.d_out) {
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const int64_t n = n0 + wn * NT * 16 + nt * 16 + (lane & 15);
+                        if (n < a.r) v = fmaf(Cvt<E>::to_f(Bp[m * a.r + n]), acc[mt][nt][j], v);
+                    }
+                }
+                v += __shfl_xor(v, 1);
+                v += __shfl_xor(v, 2);
+                v += __shfl_xor(v, 4);
+                v += __shfl_xor(v, 8);
+                if ((lane & 15) == 0) red[wn * TL::BM + row] = v;
+            }
         }
     }
     __syncthreads();
@@ -327,13 +838,13 @@ struct GramArgs {
     Contraction c;     // left0 = right0 = A
     int ntiles, nsplit, nupper;
     int64_t rnp;       // ntiles * 64
-    float* part;       // [nsplit][rnp][rnp], upper tiles only
+    float* part;       // [nsplit][rnp][rnp], full symmetric partials
 };
 
 template <typename E, bool ALIGNED>
 __global__ __launch_bounds__(256) void gram_partial(GramArgs a) {
     typedef Tile<E, 2, 2, 2, 2> TL;
-    __shared__ __attribute__((aligned(16))) char smem[TL::LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[ALIGNED ? TL::DMA_BYTES : TL::STAGED_BYTES];
     const int id = blockIdx.x;
     const int split = id / a.nupper;
     int u = id % a.nupper, ti = 0;
@@ -350,12 +861,13 @@ __global__ __launch_bounds__(256) void gram_partial(GramArgs a) {
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float bsum[TL::LCH];
     mainloop<E, 2, 2, 2, 2, ALIGNED>(a.c, (int64_t)ti * kGramTile, (int64_t)tj * kGramTile, kt_begin, kt_end,
-                                     false, acc, bsum, reinterpret_cast<E*>(smem));
+                                     0, nullptr, 0, acc, smem);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / 2, wn = wave % 2;
     float* out = a.part + (int64_t)split * a.rnp * a.rnp;
+    // Off-diagonal tiles are also written transposed, so the partial buffer
+    // holds the full symmetric matrix and the finalize reads it row-wise.
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -365,11 +877,12 @@ __global__ __launch_bounds__(256) void gram_partial(GramArgs a) {
                 const int64_t i = (int64_t)ti * kGramTile + wm * 32 + mt * 16 + 4 * (lane >> 4) + j;
                 const int64_t k = (int64_t)tj * kGramTile + wn * 32 + nt * 16 + (lane & 15);
                 out[i * a.rnp + k] = acc[mt][nt][j];
+                if (ti != tj) out[k * a.rnp + i] = acc[mt][nt][j];
             }
 }
 
 // Gs[i][j] = (s/2) * sum_split G[i][j] for i < r, j < r; zero for r <= j < ldg.
-// Only upper tiles were computed; the lower ones are read transposed.
+// The split partials are summed in split order.
 template <typename E>
 __global__ __launch_bounds__(256) void gram_finalize(const float* __restrict__ part, int nsplit, int64_t rnp,
                                                      int64_t r, int64_t ldg, float half_s, E* __restrict__ gs) {
@@ -378,10 +891,19 @@ __global__ __launch_bounds__(256) void gram_finalize(const float* __restrict__ p
     const int64_t i = idx / ldg, j = idx % ldg;
     float v = 0.0f;
     if (j < r) {
-        const bool upper = (i / kGramTile) <= (j / kGramTile);
-        const int64_t off = upper ? i * rnp + j : j * rnp + i;
+        const float* p = part + i * rnp + j;
+        const int64_t stride = rnp * rnp;
         float sum = 0.0f;
-        for (int sp = 0; sp < nsplit; ++sp) sum += part[(int64_t)sp * rnp * rnp + off];
+        int sp = 0;
+        for (; sp + 4 <= nsplit; sp += 4) {
+            const float x0 = p[(sp + 0) * stride], x1 = p[(sp + 1) * stride];
+            const float x2 = p[(sp + 2) * stride], x3 = p[(sp + 3) * stride];
+            sum += x0;
+            sum += x1;
+            sum += x2;
+            sum += x3;
+        }
+        for (; sp < nsplit; ++sp) sum += p[sp * stride];
         v = half_s * sum;
     }
     gs[idx] = Cvt<E>::from_f(v);
@@ -419,7 +941,9 @@ __global__ __launch_bounds__(256) void norm_finalize(const float* __restrict__ p
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= d_out) return;
     float base = 0.0f, cd = 0.0f;
+#pragma unroll 8
     for (int c = 0; c < nbase; ++c) base += pbase[(int64_t)c * d_out + i];
+#pragma unroll 8
     for (int c = 0; c < ncross; ++c) cd += pcross[(int64_t)c * d_out + i];
     const float n2 = fmaxf(fmaf(two_s, cd, base), 0.0f);
     const float wn = sqrtf(n2);
@@ -433,12 +957,12 @@ struct TileCfg {
 };
 // Ordered by the width BN of the slice of r a workgroup covers.
 constexpr TileCfg kCfgs[] = {
-    {4, 1, 2, 1},    // BM 128, BN 16
-    {2, 2, 4, 1},    // BM 128, BN 32
-    {2, 2, 4, 2},    // BM 128, BN 64
-    {2, 2, 4, 4},    // BM 128, BN 128
-    {2, 2, 4, 6},    // BM 128, BN 192
-    {2, 2, 4, 12},   // BM 128, BN 384
+    {4, 1, 2, 1},    // narrow, BM 128, BN 16
+    {4, 1, 2, 2},    // narrow, BM 128, BN 32
+    {4, 1, 2, 4},    // narrow, BM 128, BN 64
+    {1, 4, 8, 2},    // wide,   BM 128, BN 128
+    {1, 4, 8, 3},    // wide,   BM 128, BN 192
+    {1, 4, 8, 6},    // wide,   BM 128, BN 384
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -488,7 +1012,10 @@ hipError_t norm_typed(const NormPlan& p, const void* W0, const void* A, const vo
     E* gs = reinterpret_cast<E*>(w + p.off_gs);
     float* gpart = reinterpret_cast<float*>(w + p.off_gpart);
     float* pcross = reinterpret_cast<float*>(w + p.off_pcross);
-    const bool al = d_in % VEC == 0 && r % VEC == 0 && al16(W0) && al16(A) && al16(B);
+    // LDS-DMA path: 16-byte aligned rows, and byte offsets inside one tile of
+    // rows that fit the 31-bit buffer offsets.
+    const int64_t span = (int64_t)(p.bm > p.bn ? p.bm : p.bn) * (d_in > p.ldg ? d_in : p.ldg) * (int64_t)sizeof(E);
+    const bool al = d_in % VEC == 0 && r % VEC == 0 && al16(W0) && al16(A) && al16(B) && span < (1LL << 30);
 
     // 1. Gs = (s/2) A A^T
     GramArgs ga;
@@ -576,9 +1103,17 @@ NormPlan plan_norm(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool base_
     p.nkt_w0 = (int)((d_in + p.bk - 1) / p.bk);
     p.nkt_g = (int)((r + p.bk - 1) / p.bk);
     const int nkt = p.nkt_w0 + p.nkt_g;
-    // k-split: smallest power of two that fills the CUs, keeping >= 4 k-tiles per chunk
+    // k-split: W0 is cut into ks K-stripes per m-tile.  Workgroup ids place
+    // stripe c on XCD c % 8, and streaming W0 measures near the HBM roofline
+    // when every XCD owns its own stripe (ks a multiple of 8) but ~40% lower
+    // with 4 stripes; beyond that, split further only to give >= 2 workgroups
+    // per CU.  Every stripe keeps >= 8 k-tiles.
     int ks = 1;
-    while (ks < kNumXCD && (int64_t)p.n_mtiles * p.n_ntiles * ks < kNumCU && nkt / (2 * ks) >= 4) ks *= 2;
+    while (ks < kNumXCD && nkt / (2 * ks) >= 8) ks *= 2;
+    while (ks < 64 && (int64_t)p.n_mtiles * p.n_ntiles * ks < 2 * kNumCU && nkt / (2 * ks) >= 8) ks *= 2;
+#ifdef DORA_W0_FORCE_KSPLIT
+    ks = DORA_W0_FORCE_KSPLIT;   // tile sweeps only
+#endif
     p.ksplit = ks;
     // Gram
     p.gram_tiles = (int)((r + kGramTile - 1) / kGramTile);
