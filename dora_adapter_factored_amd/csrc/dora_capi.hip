@@ -65,7 +65,7 @@ int dora_factored_norm_workspace_size(int64_t d_out, int64_t d_in, int64_t r, in
     if (!dtype_ok(dtype)) return fail(DORA_ERR_INVALID_ARG, "unknown dtype code %d", dtype);
     if (dtype == DORA_F16) return fail(DORA_ERR_UNSUPPORTED, "factored norm supports bf16 and fp32 inputs");
     // The s == 0 path needs less; the query reports the general size.
-    *bytes = dora::plan_norm(d_out, d_in, r, dtype, false).bytes;
+    *bytes = dora::plan_norm(d_out, d_in, r, dtype, false).bytes_needed;
     return ok();
 }
 
@@ -83,10 +83,11 @@ int dora_factored_norm(const void* W0, const void* A, const void* B, const float
     if (!std::isfinite(s)) return fail(DORA_ERR_INVALID_ARG, "s must be finite");
     if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(DORA_ERR_INVALID_ARG, "eps must be finite and >= 0");
     const dora::NormPlan plan = dora::plan_norm(d_out, d_in, r, dtype, s == 0.0f);
-    if (plan.bytes > 0) {
-        if (!workspace) return fail(DORA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", plan.bytes);
-        if (workspace_bytes < plan.bytes)
-            return fail(DORA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, plan.bytes);
+    if (plan.bytes_needed > 0) {
+        if (!workspace) return fail(DORA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", plan.bytes_needed);
+        if (workspace_bytes < plan.bytes_needed)
+            return fail(DORA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                        plan.bytes_needed);
         if (!aligned256(workspace)) return fail(DORA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     }
     hipError_t e = dora::launch_norm(plan, W0, A, B, m, s, eps, wnorm, g, workspace,

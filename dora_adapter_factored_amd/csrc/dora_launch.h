@@ -23,6 +23,7 @@ struct NormPlan {
     int64_t d_out, d_in, r;
     // W0 pass
     int cfg;            // tile configuration index (see norm.hip)
+    bool big;           // 256 x 384 tiles (bf16, 16-byte aligned operands)
     int bm, bn, bk;     // rows of W0 per workgroup, columns of r per workgroup, K per tile
     int n_mtiles, n_ntiles;
     int nkt_w0, nkt_g;  // K tiles over d_in, then over the Gram block (r)
@@ -33,6 +34,7 @@ struct NormPlan {
     int64_t ldg;        // leading dimension of the scaled Gram operand
     // workspace layout (byte offsets)
     size_t off_gs, off_gpart, off_pbase, off_pcross, bytes;
+    size_t bytes_needed;   // workspace to request: covers this plan and its unaligned fallback
     bool base_only;     // s == 0: only the base term is needed
 };
 

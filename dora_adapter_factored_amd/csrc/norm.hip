@@ -583,8 +583,16 @@ __device__ __forceinline__ void mainloop_w0_narrow(const Contraction& c, int64_t
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = kt_end - kt_begin;
-    if (n <= 0) return;
     const int64_t mrow0 = m0 + wave * MT * 16;
+    if (n <= 0) {
+        // an empty K-chunk still owns its base partials
+        if (base_dst)
+            for (int mt = 0; mt < MT; ++mt) {
+                const int64_t m = mrow0 + mt * 16 + lane;
+                if (lane < 16 && m < d_out) base_dst[m] = 0.0f;
+            }
+        return;
+    }
     const FragSrc L0 = make_frag_src<E>(c.left0, mrow0, lane);
     const FragSrc L1 = make_frag_src<E>(c.left1, mrow0, lane);
     const FragSrc R0 = make_frag_src<E>(c.right0, n0, lane);
@@ -661,6 +669,145 @@ __device__ __forceinline__ void mainloop_w0_narrow(const Contraction& c, int64_t
     }
 }
 
+// W0 pass main loop, wide form with the right operand in registers.  The
+// left operand (W0, then B) is shared by the WN waves of the workgroup and
+// goes global -> LDS by DMA into a ring of LS = P + 2 stages; each wave loads
+// the right-operand fragments it alone uses (its NT blocks of A, then Gs)
+// straight into registers in MFMA operand layout, P tiles ahead.  Only the
+// left tile crosses LDS, which halves LDS traffic per k-tile compared with
+// staging both operands.  Per step a wave issues right(j + P), then
+// left(j + P + 1): vector-memory loads complete in issue order, so waiting for
+// right(j) also covers left(j) (issued one step earlier) while left(j + 1)
+// and the later steps stay in flight.  Per k-tile j:
+//   wait for this wave's loads of tile j, barrier (every wave's DMA share of
+//   left(j) landed, and the stage of tile j-1 is free), enqueue right(j + P)
+//   and left(j + P + 1), MFMA over tile j.
+// The K walk is rotated as in mainloop_dma; the base term is summed from the
+// left fragments.
+template <typename E, int WN, int MT, int NT, int P>
+__device__ __forceinline__ void mainloop_adirect(const Contraction& c, int64_t m0, int64_t n0, int kt_begin,
+                                                 int kt_end, int rot, float* base_dst, int64_t d_out,
+                                                 f32x4_t (&acc)[MT][NT], char* smem) {
+    typedef Tile<E, 1, WN, MT, NT> TL;
+    typedef Mma<E> M;
+    constexpr int LS = P + 2;
+    constexpr int FR = M::BK / 32, FL = M::FL;
+    constexpr int NRW = FR * NT * FL;   // right loads per wave per tile
+    constexpr int LPW = TL::LPW;        // left DMA instructions per wave per tile
+    constexpr int TKB = TL::BK * (int)sizeof(E);
+    static_assert(TL::NW % 2 == 0, "DMA lane offsets assume an even wave count");
+    static_assert(LPW + (P - 1) * (NRW + LPW) < 64, "vmcnt range");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = wave;
+    const int q = lane >> 4;
+    const int n = kt_end - kt_begin;
+    if (n <= 0) {
+        // an empty K-chunk still owns its base partials
+        if (base_dst)
+            for (int mt = wn; mt < MT; mt += WN) {
+                const int64_t m = m0 + mt * 16 + lane;
+                if (lane < 16 && m < d_out) base_dst[m] = 0.0f;
+            }
+        return;
+    }
+
+    const DmaSrc L0 = make_dma_src<E>(c.left0, m0, lane);
+    const DmaSrc L1 = make_dma_src<E>(c.left1, m0, lane);
+    const FragSrc R0 = make_frag_src<E>(c.right0, n0 + wn * NT * 16, lane);
+    const FragSrc R1 = make_frag_src<E>(c.right1, n0 + wn * NT * 16, lane);
+
+    int lrow[MT], lsw[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        lrow[mt] = mt * 16 + (lane & 15);
+        lsw[mt] = swz(lrow[mt]);
+    }
+    float bs[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) bs[mt] = 0.0f;
+
+    auto tile = [&](int i) __attribute__((always_inline)) {
+        int t = i + rot;
+        if (t >= n) t -= n;
+        return kt_begin + t;
+    };
+    auto issue_left = [&](int i) __attribute__((always_inline)) {
+        const int kt = tile(i);
+        char* dst = smem + (i % LS) * TL::LBYTES;
+        if (kt < c.nkt0)
+            dma_tile<TL::BM, 0, TL::NW>(L0, kt * TKB, dst, wave, TKB);
+        else
+            dma_tile<TL::BM, 0, TL::NW>(L1, (kt - c.nkt0) * TKB, dst, wave, TKB);
+    };
+    auto issue_right = [&](int i, u32x4_t* regs) __attribute__((always_inline)) {
+        const int kt = tile(i);
+        if (kt < c.nkt0)
+            load_frags<E, NT>(R0, (int64_t)kt * M::BK, regs);
+        else
+            load_frags<E, NT>(R1, (int64_t)(kt - c.nkt0) * M::BK, regs);
+    };
+    auto compute = [&](int i, const u32x4_t* regs) __attribute__((always_inline)) {
+        const char* Lt = smem + (i % LS) * TL::LBYTES;
+        const bool base = base_dst != nullptr && tile(i) < c.nkt0;
+#pragma unroll
+        for (int ks = 0; ks < FR; ++ks) {
+            typename M::frag_t a[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) a[mt] = M::load_frag_swz(Lt + lrow[mt] * 128, ks, q, lsw[mt]);
+            if (base) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    if (mt % WN == wn) bs[mt] += M::frag_sumsq(a[mt]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const typename M::frag_t b = M::frag_from_regs(regs + (ks * NT + nt) * FL);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) M::mma(acc[mt][nt], a[mt], b);
+            }
+        }
+    };
+    // one step; cur holds right(i), nxt receives right(i + P)
+    auto step = [&](int i, const u32x4_t* cur, u32x4_t* nxt) __attribute__((always_inline)) {
+        if (i + P < n)
+            wait_vmcnt<LPW + (P - 1) * (NRW + LPW)>();
+        else
+            wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (i + P < n) issue_right(i + P, nxt);
+        if (i + P + 1 < n) issue_left(i + P + 1);
+        compute(i, cur);
+    };
+
+    static_assert(P == 2, "register sets are rotated three ways");
+    u32x4_t s0[NRW], s1[NRW], s2[NRW];
+    issue_left(0);
+    issue_right(0, s0);
+    if (n > 1) issue_left(1);
+    if (n > 1) issue_right(1, s1);
+    if (n > 2) issue_left(2);
+    for (int i = 0; i < n; i += 3) {
+        step(i, s0, s2);
+        if (i + 1 >= n) break;
+        step(i + 1, s1, s0);
+        if (i + 2 >= n) break;
+        step(i + 2, s2, s1);
+    }
+    __builtin_amdgcn_s_barrier();   // LDS is free for the caller's epilogue
+    if (base_dst) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if (mt % WN != wn) continue;
+            float v = bs[mt];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            const int64_t m = m0 + mt * 16 + lane;
+            if (lane < 16 && m < d_out) base_dst[m] = v;
+        }
+    }
+}
+
 template <typename E, int WM, int WN, int MT, int NT, bool ALIGNED>
 __device__ __forceinline__ void mainloop(const Contraction& c, int64_t m0, int64_t n0, int kt_begin, int kt_end,
                                          int rot, float* base_dst, int64_t d_out, f32x4_t (&acc)[MT][NT],
@@ -684,7 +831,7 @@ struct W0PassArgs {
 
 template <int WM, int WN, int MT, int NT, bool ALIGNED>
 struct W0Form {
-    static constexpr bool WIDE = ALIGNED && WM == 1 && WN == 4 && MT == 8;
+    static constexpr bool WIDE = ALIGNED && WM == 1 && WN >= 4 && MT == 8;
     static constexpr bool NARROW = ALIGNED && WN == 1;
 };
 
@@ -700,7 +847,12 @@ __global__ __launch_bounds__(WM * WN * 64) void w0_pass(W0PassArgs a) {
     constexpr int B_PITCH = B_SLOTS * 16;
     constexpr int B_BYTES = ALIGNED ? TL::BM * B_PITCH : 0;
     constexpr int EPI = B_BYTES + RED_BYTES;
-    constexpr int MAIN = F::WIDE ? TL::DMA_BYTES : (F::NARROW ? 0 : TL::STAGED_BYTES);
+#ifdef DORA_W0_ADIRECT
+    constexpr int WIDE_BYTES = 4 * TL::LBYTES;
+#else
+    constexpr int WIDE_BYTES = TL::DMA_BYTES;
+#endif
+    constexpr int MAIN = F::WIDE ? WIDE_BYTES : (F::NARROW ? 0 : TL::STAGED_BYTES);
     __shared__ __attribute__((aligned(1024))) char smem[MAIN > EPI ? MAIN : EPI];
 
     // Workgroup -> (m-tile, n-tile, k-chunk).  Workgroups are handed to the 8
@@ -737,7 +889,11 @@ __global__ __launch_bounds__(WM * WN * 64) void w0_pass(W0PassArgs a) {
     const int nk = kt_end - kt_begin;
     const int rot = nk > 0 ? (int)(((unsigned)id * 7u + ((unsigned)id >> 3) * 3u) % (unsigned)nk) : 0;
     if constexpr (F::WIDE)
+#ifdef DORA_W0_ADIRECT
+        mainloop_adirect<E, WN, MT, NT, 2>(a.c, m0, n0, kt_begin, kt_end, rot, base_dst, a.d_out, acc, smem);
+#else
         mainloop_dma<E, WM, WN, MT, NT, false>(a.c, m0, n0, kt_begin, kt_end, rot, base_dst, a.d_out, acc, smem);
+#endif
     else if constexpr (F::NARROW)
         mainloop_w0_narrow<E, MT, NT>(a.c, m0, n0, kt_begin, kt_end, rot, base_dst, a.d_out, acc);
     else
@@ -826,6 +982,399 @@ __global__ __launch_bounds__(WM * WN * 64) void w0_pass(W0PassArgs a) {
             float v = red[row];
 #pragma unroll
             for (int w = 1; w < WN; ++w) v += red[w * TL::BM + row];
+            a.part_cross[((int64_t)ntile * a.ksplit + kc) * a.d_out + m] = v;
+        }
+    }
+}
+
+// ------------------------------------------------------------- W0 pass, 256 x 384 tiles
+// Large-tile form of the W0 pass for bf16 operands, used when r > 192.  A
+// workgroup owns 256 rows of W0 and 384 columns of r: every A tile that
+// crosses L2 feeds twice as many MFMAs as with 128-row tiles, which halves
+// the L2 -> CU traffic of A, the larger of the two streams per k-tile.
+// Eight waves in a 2 x 4 grid each accumulate a 128 x 96 block with 32x32x16
+// MFMAs (4 x 3 blocks of 32 x 32, 192 accumulators per lane); one 16-deep
+// step of K needs only 7 operand registers per lane, so two waves fit on
+// every SIMD and cover each other's LDS and memory waits.  Tiles are 32
+// elements of K (64-byte rows): W0 (then B) runs in an LDS ring of LS = 4
+// stages, A (then Gs) in RS = 3 stages, all moved by LDS DMA.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
+struct Big {
+    static constexpr int BM = 256, BN = 384, BK = 32;
+    static constexpr int WM = 2, WN = 4, NW = WM * WN, NTH = NW * 64;
+    static constexpr int MT = 4, NT = 3;   // 32 x 32 blocks per wave
+    static constexpr int LS = 4, RS = 3;
+    static constexpr int ROWB = BK * 2;    // bytes of K per tile row
+    static constexpr int LBYTES = BM * ROWB, RBYTES = BN * ROWB;
+    static constexpr int RING = LS * LBYTES + RS * RBYTES;
+    static constexpr int LPW = BM / 16 / NW, RPW = BN / 16 / NW;   // DMA instructions per wave per tile
+    // epilogue: one half (128 rows) of the B tile, rows padded by 16 bytes
+    static constexpr int EB_ROWS = BM / WM;
+    static constexpr int EB_SLOTS = BN * 2 / 16 + 1;
+    static constexpr int EB_PITCH = EB_SLOTS * 16;
+    static constexpr int EB_BYTES = EB_ROWS * EB_PITCH;
+    static constexpr int RED_BYTES = WN * BM * 4;
+    static constexpr int LDS_BYTES = RING > EB_BYTES + RED_BYTES ? RING : EB_BYTES + RED_BYTES;
+    static_assert(BM / 16 % NW == 0 && BN / 16 % NW == 0, "DMA groups split evenly across waves");
+    static_assert(MT == WN, "each wave sums the base term of one 32-row block");
+};
+
+// Chunk swizzle of 64-byte rows: logical chunk c of row i sits in slot
+// c ^ swz64(i).  For a fixed chunk, the 16 rows of any aligned 16-row block
+// map to 16 distinct (row mod 4, slot) pairs and the even (odd) rows of any
+// aligned 8 rows to 4 distinct slots, so 16-lane (64-bank) and 8-lane
+// (32-bank) phases of a fragment read are conflict-free.  It depends only on
+// the row modulo 16, the height of one DMA group.
+__device__ __forceinline__ int swz64(int row) { return ((row >> 2) & 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 1); }
+
+// One operand as the 64-byte-row DMA sees it; lane l moves slot l % 4 of row
+// l / 4 of a 16-row group (1 KiB per instruction).  The row and K offsets of
+// an instruction are wave-uniform, so they move the buffer's base address
+// (scalar registers) while the per-lane part stays one fixed VGPR; the
+// buffer is shrunk by the same amount, so rows past the operand still read
+// zeros.
+struct Dma64 {
+    uint32_t base_lo, base_hi;     // address of the workgroup's first row
+    int bytes;                     // bytes from there to the operand's end (clamped to 31 bits)
+    int ld_bytes, kmax_bytes;
+};
+
+__device__ __forceinline__ Dma64 make_dma64(const Operand& o, int64_t row0) {
+    Dma64 d;
+    const int64_t ldb = o.ld * 2;
+    const uint64_t base = reinterpret_cast<uint64_t>(static_cast<const char*>(o.p) + row0 * ldb);
+    int64_t bytes = (o.rows - row0) * ldb;
+    if (bytes < 0) bytes = 0;
+    if (bytes > 0x7ffffff0) bytes = 0x7ffffff0;
+    d.base_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    d.base_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
+    d.bytes = __builtin_amdgcn_readfirstlane((int)bytes);
+    d.ld_bytes = __builtin_amdgcn_readfirstlane((int)ldb);
+    d.kmax_bytes = __builtin_amdgcn_readfirstlane((int)(o.kmax * 2));
+    return d;
+}
+
+// Enqueue rows [0, ROWS) of a 64-byte K slab into LDS at dst.  `d` is the
+// phase's operand (scalar fields), k0b the slab's byte offset along K.  Lane
+// l moves slot l % 4 of row l / 4 of each 16-row group: lane_off =
+// (l / 4) * ld_bytes + chunk_b, where chunk_b is the byte offset of the
+// logical chunk that slot holds; a lane_off of kOutOfRange turns the whole
+// load into zeros.  Chunks past the operand's K extent read zeros.  Row and
+// K offsets fit 31 bits: a workgroup's rows of any operand span less than
+// 2^30 bytes.
+template <int ROWS>
+__device__ __forceinline__ void dma64_tile(const Dma64& d, int lane_off, int chunk_b, int k0b, char* dst,
+                                           int wave) {
+    constexpr int PER = ROWS / 16 / Big::NW;
+    const int ldb = d.ld_bytes, bytes = d.bytes, kmax = d.kmax_bytes;
+    const uint64_t base = ((uint64_t)d.base_hi << 32) | d.base_lo;
+    const bool full = k0b + Big::ROWB <= kmax;
+    const int voff = full ? lane_off : (chunk_b < kmax - k0b ? lane_off : kOutOfRange);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int grp = wave + q * Big::NW;
+        const int off = grp * 16 * ldb + k0b;
+        const int left = bytes > off ? bytes - off : 0;
+        const uint64_t addr = base + (uint32_t)off;
+        i32x4_t rs;
+        rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+        rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32));
+        rs[2] = __builtin_amdgcn_readfirstlane(left);
+        rs[3] = 0x00020000;
+        raw_buffer_load_lds(rs, (lds_void_t*)(dst + grp * 1024), 16, voff, 0, 0, 0);
+    }
+}
+
+__global__ __launch_bounds__(Big::NTH) void w0_pass_big(W0PassArgs a) {
+    typedef Big G;
+    __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / G::WN, wn = wave % G::WN;
+
+    // workgroup -> (m-tile, n-tile, k-chunk), K-chunks mapped to XCDs
+    const int Q = a.n_ntiles * a.ksplit;
+    const int id = blockIdx.x;
+    int q, mtile;
+    if (a.xcd_map) {
+        const int xcd = id % kNumXCD, slot = id / kNumXCD;
+        q = xcd % Q;
+        mtile = slot * (kNumXCD / Q) + xcd / Q;
+    } else {
+        q = id % Q;
+        mtile = id / Q;
+    }
+    if (mtile >= a.n_mtiles) return;
+    const int ntile = q / a.ksplit, kc = q % a.ksplit;
+    const int64_t m0 = (int64_t)mtile * G::BM, n0 = (int64_t)ntile * G::BN;
+    const Contraction& c = a.c;
+    const int nkt = c.nkt0 + c.nkt1;
+    const int kt_begin = (int)((int64_t)kc * nkt / a.ksplit);
+    const int kt_end = (int)((int64_t)(kc + 1) * nkt / a.ksplit);
+    const int n = kt_end - kt_begin;
+    float* base_dst = ntile == 0 ? a.part_base + (int64_t)kc * a.d_out : nullptr;
+    const int rot = n > 0 ? (int)(((unsigned)id * 7u + ((unsigned)id >> 3) * 3u) % (unsigned)n) : 0;
+
+    f32x16_t acc[G::MT][G::NT];
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < G::NT; ++nt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[mt][nt][e] = 0.0f;
+    float bs = 0.0f;
+
+    char* lring = smem;
+    char* rring = smem + G::LS * G::LBYTES;
+    if (n > 0) {
+        const Dma64 L0 = make_dma64(c.left0, m0);
+        const Dma64 L1 = make_dma64(c.left1, m0);
+        const Dma64 R0 = make_dma64(c.right0, n0);
+        const Dma64 R1 = make_dma64(c.right1, n0);
+        // per-lane DMA offsets; the two operands of a phase share a row pitch
+        // (W0 and A: d_in; B and Gs: r, a multiple of 8 on this path)
+        const int dchunk = ((lane & 3) ^ swz64(lane >> 2)) * 16;
+        const int doff0 = (lane >> 2) * L0.ld_bytes + dchunk;
+        const int doff1 = (lane >> 2) * L1.ld_bytes + dchunk;
+        // fragment byte offsets inside a tile: row (l % 32) of a 32-row block,
+        // logical chunk 2 ks + l / 32 for k16-step ks
+        const int sw = swz64(lane & 31);
+        const int h = (lane >> 5) ^ sw;
+        const int fo0 = (lane & 31) * G::ROWB + (h << 4);
+        const int fo1 = (lane & 31) * G::ROWB + ((h ^ 2) << 4);
+        const int lrow0 = wm * 128 * G::ROWB, rrow0 = wn * 96 * G::ROWB;
+        const float base_on = base_dst != nullptr ? 1.0f : 0.0f;
+
+        // k-tile visited at step i (the walk starts at a rotated tile)
+        auto tile = [&](int i) __attribute__((always_inline)) {
+            int t = i + rot;
+            if (t >= n) t -= n;
+            return kt_begin + t;
+        };
+        // Loads of step i; steps past the last tile still issue (reading
+        // zeros into a stage no one reads), so the number of loads in flight
+        // is the same at every step and the loop carries no branches.
+        auto issue = [&](int i, auto rows, char* ring, int stage_bytes, int stages, const Dma64& P0,
+                         const Dma64& P1) __attribute__((always_inline)) {
+            const bool valid = i < n;
+            const int kt = tile(valid ? i : 0);
+            const bool ph0 = kt < c.nkt0;
+            Dma64 d;
+            d.base_lo = ph0 ? P0.base_lo : P1.base_lo;
+            d.base_hi = ph0 ? P0.base_hi : P1.base_hi;
+            d.bytes = ph0 ? P0.bytes : P1.bytes;
+            d.ld_bytes = ph0 ? P0.ld_bytes : P1.ld_bytes;
+            d.kmax_bytes = ph0 ? P0.kmax_bytes : P1.kmax_bytes;
+            const int lo = valid ? (ph0 ? doff0 : doff1) : kOutOfRange;
+            const int k0b = (ph0 ? kt : kt - c.nkt0) * G::ROWB;
+            dma64_tile<decltype(rows)::value>(d, lo, dchunk, k0b, ring + (i % stages) * stage_bytes, wave);
+        };
+        auto issue_left = [&](int i) __attribute__((always_inline)) {
+            issue(i, IntC<G::BM>{}, lring, G::LBYTES, G::LS, L0, L1);
+        };
+        auto issue_right = [&](int i) __attribute__((always_inline)) {
+            issue(i, IntC<G::BN>{}, rring, G::RBYTES, G::RS, R0, R1);
+        };
+        auto read = [&](int i, int fo, bf16x8_t (&av)[G::MT], bf16x8_t (&bv)[G::NT]) __attribute__((always_inline)) {
+            const char* Lt = lring + (i % G::LS) * G::LBYTES + lrow0 + fo;
+            const char* Rt = rring + (i % G::RS) * G::RBYTES + rrow0 + fo;
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt) av[mt] = *reinterpret_cast<const bf16x8_t*>(Lt + mt * 32 * G::ROWB);
+#pragma unroll
+            for (int nt = 0; nt < G::NT; ++nt) bv[nt] = *reinterpret_cast<const bf16x8_t*>(Rt + nt * 32 * G::ROWB);
+        };
+        // MFMAs over blocks (mt, nt) with lo <= mt * NT + nt < hi
+        auto mma = [&](const bf16x8_t (&av)[G::MT], const bf16x8_t (&bv)[G::NT], int lo, int hi)
+            __attribute__((always_inline)) {
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt) {
+#pragma unroll
+                for (int nt = 0; nt < G::NT; ++nt) {
+                    const int k = mt * G::NT + nt;
+                    if (k < lo || k >= hi) continue;
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+                }
+            }
+        };
+        // ||W0_i||^2 from the left fragments: wave wn sums block wn of its
+        // rows (a compile-time copy of the loop per wave column); on = 0 for
+        // k-tiles of the B | Gs phase or workgroups that own no base rows
+        auto base_sum = [&](auto wnc, const bf16x8_t (&av)[G::MT], float on) __attribute__((always_inline)) {
+            bs = fmaf(on, Mma<bf16_t>::frag_sumsq(av[decltype(wnc)::value]), bs);
+        };
+        auto base_on_at = [&](int i) __attribute__((always_inline)) {
+            return tile(i) < c.nkt0 ? base_on : 0.0f;
+        };
+
+        // Software pipeline over k-tiles.  Tile j: MFMAs of k16-step 0 and
+        // its base term; fragments of step 1; MFMAs of step 1 except the last
+        // HOLD, and its base term.  Then wait for tile j + 1 (this wave's
+        // loads; this wave's fragment reads of tile j are complete), barrier
+        // (every wave's loads of tile j + 1 landed, every wave is done with
+        // tile j's stages), enqueue right(j + 3) and left(j + 4) into those
+        // stages, read tile j + 1's step-0 fragments, and only then issue the
+        // held-back MFMAs, which keep the matrix pipe busy across the barrier
+        // and the LDS latency.  Loads complete in issue order, so waiting for
+        // right(j + 1) covers left(j + 1), while left(j + 2), right(j + 2)
+        // and left(j + 3) stay in flight.
+        constexpr int HOLD = 2;
+        constexpr int ALL = G::MT * G::NT;
+        constexpr int INFLIGHT = G::LPW + (G::RS - 2) * (G::RPW + G::LPW);
+        auto main_loop = [&](auto wnc) __attribute__((always_inline)) {
+            bf16x8_t a0[G::MT], b0[G::NT], a1[G::MT], b1[G::NT];
+            issue_left(0);
+            issue_right(0);
+            issue_left(1);
+            issue_right(1);
+            issue_left(2);
+            wait_vmcnt<INFLIGHT>();
+            __builtin_amdgcn_s_barrier();
+            issue_right(2);
+            issue_left(3);
+            read(0, fo0, a0, b0);
+            for (int j = 0; j < n - 1; ++j) {
+                const float on = base_on_at(j);
+                mma(a0, b0, 0, ALL);
+                base_sum(wnc, a0, on);
+                __builtin_amdgcn_sched_barrier(0);   // step-1 fragments reuse step 0's registers
+                read(j, fo1, a1, b1);
+                mma(a1, b1, 0, ALL - HOLD);
+                base_sum(wnc, a1, on);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vmcnt<INFLIGHT>();
+                __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+                __builtin_amdgcn_s_barrier();
+                issue_right(j + 3);
+                issue_left(j + 4);
+                read(j + 1, fo0, a0, b0);
+                __builtin_amdgcn_sched_barrier(0);
+                mma(a1, b1, ALL - HOLD, ALL);
+            }
+            {
+                const float on = base_on_at(n - 1);
+                mma(a0, b0, 0, ALL);
+                base_sum(wnc, a0, on);
+                __builtin_amdgcn_sched_barrier(0);
+                read(n - 1, fo1, a1, b1);
+                mma(a1, b1, 0, ALL);
+                base_sum(wnc, a1, on);
+            }
+            wait_vmcnt<0>();   // trailing zero loads land before LDS is reused
+        };
+        switch (wn) {
+            case 0: main_loop(IntC<0>{}); break;
+            case 1: main_loop(IntC<1>{}); break;
+            case 2: main_loop(IntC<2>{}); break;
+            default: main_loop(IntC<3>{}); break;
+        }
+    }
+    __syncthreads();   // ring free for the epilogue
+
+    // base partial: lanes l and l + 32 hold the two K halves of row l % 32 of
+    // block wn of this wave's 128 rows
+    if (base_dst) {
+        const float v = bs + __shfl_xor(bs, 32);
+        const int64_t m = m0 + wm * 128 + wn * 32 + lane;
+        if (lane < 32 && m < a.d_out) base_dst[m] = v;
+    }
+
+    // cross partial: sum_n B[m][n] acc[m][n] over this workgroup's columns.
+    // acc[mt][nt][e] is row mt*32 + 8 (e/4) + 4 (l/32) + e%4 of the wave's
+    // block and column nt*32 + l%32.  The B tile is staged in LDS one 128-row
+    // half at a time.
+    float* red = reinterpret_cast<float*>(smem + G::EB_BYTES);   // [WN][BM]
+    const int64_t rb = a.r * 2;
+    const int colb0 = (int)(n0 * 2);
+#pragma unroll 1
+    for (int hf = 0; hf < G::WM; ++hf) {
+        {
+            const int64_t rowh = m0 + hf * G::EB_ROWS;
+            const uint64_t addr = reinterpret_cast<uint64_t>(static_cast<const char*>(a.B) + rowh * rb);
+            int64_t bytes = (a.d_out - rowh) * rb;
+            if (bytes < 0) bytes = 0;
+            if (bytes > 0x7ffffff0) bytes = 0x7ffffff0;
+            i32x4_t rs;
+            rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+            rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32));
+            rs[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+            rs[3] = 0x00020000;
+            constexpr int NINS = (G::EB_ROWS * G::EB_SLOTS + 63) / 64;
+#pragma unroll
+            for (int k = 0; k < (NINS + G::NW - 1) / G::NW; ++k) {
+                const int ins = wave + k * G::NW;
+                if (ins < NINS) {
+                    const int slot = ins * 64 + lane;
+                    const int row = slot / G::EB_SLOTS, ch = slot % G::EB_SLOTS;
+                    const int colb = colb0 + ch * 16;
+                    const bool ok = ch < G::EB_SLOTS - 1 && row < G::EB_ROWS && colb < (int)rb;
+                    const int voff = ok ? row * (int)rb + colb : kOutOfRange;
+                    raw_buffer_load_lds(rs, (lds_void_t*)(smem + ins * 1024), 16, voff, 0, 0, 0);
+                }
+            }
+            wait_vmcnt<0>();
+        }
+        __syncthreads();
+        if (wm == hf) {
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt) {
+                float v[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = mt * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    const bf16_t* brow = reinterpret_cast<const bf16_t*>(smem + row * G::EB_PITCH) + wn * 96 +
+                                         (lane & 31);
+                    float x = 0.0f;
+#pragma unroll
+                    for (int nt = 0; nt < G::NT; ++nt) x = fmaf(static_cast<float>(brow[nt * 32]), acc[mt][nt][e], x);
+                    v[e] = x;
+                }
+                // sum each row over the 32 lanes that share l / 32, halving the
+                // number of rows a lane carries at every exchange
+                const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const float send = b4 ? v[s] : v[s + 8];
+                    const float keep = b4 ? v[s + 8] : v[s];
+                    v[s] = keep + __shfl_xor(send, 16);
+                }
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const float send = b3 ? v[s] : v[s + 4];
+                    const float keep = b3 ? v[s + 4] : v[s];
+                    v[s] = keep + __shfl_xor(send, 8);
+                }
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const float send = b2 ? v[s] : v[s + 2];
+                    const float keep = b2 ? v[s + 2] : v[s];
+                    v[s] = keep + __shfl_xor(send, 4);
+                }
+                {
+                    const float send = b1 ? v[0] : v[1];
+                    const float keep = b1 ? v[1] : v[0];
+                    v[0] = keep + __shfl_xor(send, 2);
+                }
+                v[0] += __shfl_xor(v[0], 1);
+                // lane l now holds the row with e = (l >> 1) & 15
+                const int e = (lane >> 1) & 15;
+                const int row = mt * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if ((lane & 1) == 0) red[wn * G::BM + hf * G::EB_ROWS + row] = v[0];
+            }
+        }
+        __syncthreads();
+    }
+    for (int row = threadIdx.x; row < G::BM; row += G::NTH) {
+        const int64_t m = m0 + row;
+        if (m < a.d_out) {
+            float v = red[row];
+#pragma unroll
+            for (int w = 1; w < G::WN; ++w) v += red[w * G::BM + row];
             a.part_cross[((int64_t)ntile * a.ksplit + kc) * a.d_out + m] = v;
         }
     }
@@ -962,7 +1511,11 @@ constexpr TileCfg kCfgs[] = {
     {4, 1, 2, 4},    // narrow, BM 128, BN 64
     {1, 4, 8, 2},    // wide,   BM 128, BN 128
     {1, 4, 8, 3},    // wide,   BM 128, BN 192
+#ifdef DORA_W0_WN8
+    {1, 8, 8, 3},    // wide,   BM 128, BN 384, 8 waves
+#else
     {1, 4, 8, 6},    // wide,   BM 128, BN 384
+#endif
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
@@ -989,6 +1542,16 @@ hipError_t launch_w0(int cfg, const W0PassArgs& a, int grid, hipStream_t st) {
 
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// LDS-DMA paths: 16-byte aligned rows, and byte offsets inside one tile of
+// rows that fit the 31-bit buffer offsets.
+template <typename E>
+bool operands_aligned(const NormPlan& p, const void* W0, const void* A, const void* B) {
+    constexpr int VEC = Mma<E>::VEC;
+    const int64_t span =
+        (int64_t)(p.bm > p.bn ? p.bm : p.bn) * (p.d_in > p.ldg ? p.d_in : p.ldg) * (int64_t)sizeof(E);
+    return p.d_in % VEC == 0 && p.r % VEC == 0 && al16(W0) && al16(A) && al16(B) && span < (1LL << 30);
+}
+
 template <typename E>
 hipError_t norm_typed(const NormPlan& p, const void* W0, const void* A, const void* B, const float* m, float s,
                       float eps, float* wnorm, float* g, void* ws, hipStream_t st) {
@@ -1012,17 +1575,15 @@ hipError_t norm_typed(const NormPlan& p, const void* W0, const void* A, const vo
     E* gs = reinterpret_cast<E*>(w + p.off_gs);
     float* gpart = reinterpret_cast<float*>(w + p.off_gpart);
     float* pcross = reinterpret_cast<float*>(w + p.off_pcross);
-    // LDS-DMA path: 16-byte aligned rows, and byte offsets inside one tile of
-    // rows that fit the 31-bit buffer offsets.
-    const int64_t span = (int64_t)(p.bm > p.bn ? p.bm : p.bn) * (d_in > p.ldg ? d_in : p.ldg) * (int64_t)sizeof(E);
-    const bool al = d_in % VEC == 0 && r % VEC == 0 && al16(W0) && al16(A) && al16(B) && span < (1LL << 30);
+    const bool al = operands_aligned<E>(p, W0, A, B);
+    if (p.big && !al) return hipErrorInvalidValue;   // the caller runs the fallback plan
 
     // 1. Gs = (s/2) A A^T
     GramArgs ga;
     ga.c.left0 = Operand{A, d_in, r, d_in};
     ga.c.right0 = ga.c.left0;
     ga.c.left1 = ga.c.right1 = Operand{nullptr, 0, 0, 0};
-    ga.c.nkt0 = (int)((d_in + p.bk - 1) / p.bk);
+    ga.c.nkt0 = (int)((d_in + Mma<E>::BK - 1) / Mma<E>::BK);
     ga.c.nkt1 = 0;
     ga.ntiles = p.gram_tiles;
     ga.nsplit = p.gram_split;
@@ -1064,7 +1625,16 @@ hipError_t norm_typed(const NormPlan& p, const void* W0, const void* A, const vo
     } else {
         grid = Q * p.n_mtiles;
     }
-    e = al ? launch_w0<E, true>(p.cfg, wa, grid, st) : launch_w0<E, false>(p.cfg, wa, grid, st);
+    if constexpr (sizeof(E) == 2) {
+        if (p.big) {
+            w0_pass_big<<<grid, Big::NTH, 0, st>>>(wa);
+            e = hipGetLastError();
+        } else {
+            e = al ? launch_w0<E, true>(p.cfg, wa, grid, st) : launch_w0<E, false>(p.cfg, wa, grid, st);
+        }
+    } else {
+        e = al ? launch_w0<E, true>(p.cfg, wa, grid, st) : launch_w0<E, false>(p.cfg, wa, grid, st);
+    }
     if (e != hipSuccess) return e;
 
     // 3. assemble
@@ -1075,7 +1645,19 @@ hipError_t norm_typed(const NormPlan& p, const void* W0, const void* A, const vo
 
 }  // namespace
 
-NormPlan plan_norm(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool base_only) {
+namespace {
+
+// Rounds of 256 CUs a grid of `wgs` one-per-CU workgroups takes, and how full
+// they are; a k-split is scored on both (fewer rounds pay fewer prologue and
+// epilogue latencies), with a bonus when every XCD can own one K-chunk.
+double ksplit_score(int64_t wgs, int q) {
+    const int64_t rounds = (wgs + kNumCU - 1) / kNumCU;
+    const double fill = (double)wgs / (double)(rounds * kNumCU);
+    const bool xcd = q <= kNumXCD && kNumXCD % q == 0;
+    return fill - 0.02 * (double)(rounds - 1) + (xcd ? 0.03 : 0.0);
+}
+
+NormPlan plan_norm_impl(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool base_only, bool allow_big) {
     NormPlan p{};
     p.dtype = dtype;
     p.d_out = d_out;
@@ -1084,42 +1666,71 @@ NormPlan plan_norm(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool base_
     p.base_only = base_only;
     const int esz = (int)dtype_size(dtype);
     const int vec = 16 / esz;
-    p.bk = dtype == kF32 ? Mma<float>::BK : Mma<bf16_t>::BK;
+    const int gram_bk = dtype == kF32 ? Mma<float>::BK : Mma<bf16_t>::BK;
     if (base_only) {
         p.off_pbase = 0;
         p.bytes = align_up((size_t)d_out * 4, 256);
         return p;
     }
-    // widest configuration this dtype instantiates (fp32 fragments double the
-    // register footprint, so fp32 stops at BN = 192)
-    const int max_cfg = dtype == kF32 ? 4 : kNumCfgs - 1;
-    int cfg = 0;
-    while (cfg < max_cfg && kCfgs[cfg].wn * kCfgs[cfg].nt * 16 < r) ++cfg;
-    p.cfg = cfg;
-    p.bm = kCfgs[cfg].wm * kCfgs[cfg].mt * 16;
-    p.bn = kCfgs[cfg].wn * kCfgs[cfg].nt * 16;
-    p.n_mtiles = (int)((d_out + p.bm - 1) / p.bm);
-    p.n_ntiles = (int)((r + p.bn - 1) / p.bn);
-    p.nkt_w0 = (int)((d_in + p.bk - 1) / p.bk);
-    p.nkt_g = (int)((r + p.bk - 1) / p.bk);
-    const int nkt = p.nkt_w0 + p.nkt_g;
-    // k-split: W0 is cut into ks K-stripes per m-tile.  Workgroup ids place
-    // stripe c on XCD c % 8, and streaming W0 measures near the HBM roofline
-    // when every XCD owns its own stripe (ks a multiple of 8) but ~40% lower
-    // with 4 stripes; beyond that, split further only to give >= 2 workgroups
-    // per CU.  Every stripe keeps >= 8 k-tiles.
+#ifdef DORA_W0_NO_BIG
+    allow_big = false;
+#endif
+    p.big = allow_big && dtype == kBF16 && r > 192;
     int ks = 1;
-    while (ks < kNumXCD && nkt / (2 * ks) >= 8) ks *= 2;
-    while (ks < 64 && (int64_t)p.n_mtiles * p.n_ntiles * ks < 2 * kNumCU && nkt / (2 * ks) >= 8) ks *= 2;
+    if (p.big) {
+        p.cfg = -1;
+        p.bm = Big::BM;
+        p.bn = Big::BN;
+        p.bk = Big::BK;
+        p.n_mtiles = (int)((d_out + p.bm - 1) / p.bm);
+        p.n_ntiles = (int)((r + p.bn - 1) / p.bn);
+        p.nkt_w0 = (int)((d_in + p.bk - 1) / p.bk);
+        p.nkt_g = (int)((r + p.bk - 1) / p.bk);
+        const int nkt = p.nkt_w0 + p.nkt_g;
+        // one 136 KB workgroup per CU: pick the split with the best-filled
+        // rounds, keeping >= 8 k-tiles per workgroup
+        const int64_t tiles = (int64_t)p.n_mtiles * p.n_ntiles;
+        double best = -1.0;
+        for (int k = 1; k <= 64 && nkt / k >= 8; ++k) {
+            const double sc = ksplit_score(tiles * k, p.n_ntiles * k);
+            if (sc > best + 1e-9) {
+                best = sc;
+                ks = k;
+            }
+        }
+    } else {
+        // widest configuration this dtype instantiates (fp32 fragments double
+        // the register footprint, so fp32 stops at BN = 192)
+        const int max_cfg = dtype == kF32 ? 4 : kNumCfgs - 1;
+        int cfg = 0;
+        while (cfg < max_cfg && kCfgs[cfg].wn * kCfgs[cfg].nt * 16 < r) ++cfg;
+        p.cfg = cfg;
+        p.bm = kCfgs[cfg].wm * kCfgs[cfg].mt * 16;
+        p.bn = kCfgs[cfg].wn * kCfgs[cfg].nt * 16;
+        p.bk = gram_bk;
+        p.n_mtiles = (int)((d_out + p.bm - 1) / p.bm);
+        p.n_ntiles = (int)((r + p.bn - 1) / p.bn);
+        p.nkt_w0 = (int)((d_in + p.bk - 1) / p.bk);
+        p.nkt_g = (int)((r + p.bk - 1) / p.bk);
+        const int nkt = p.nkt_w0 + p.nkt_g;
+        // k-split: W0 is cut into ks K-stripes per m-tile.  Workgroup ids
+        // place stripe c on XCD c % 8, and streaming W0 measures near the HBM
+        // roofline when every XCD owns its own stripe (ks a multiple of 8) but
+        // ~40% lower with 4 stripes; beyond that, split further only to give
+        // >= 2 workgroups per CU.  Every stripe keeps >= 8 k-tiles.
+        while (ks < kNumXCD && nkt / (2 * ks) >= 8) ks *= 2;
+        while (ks < 64 && (int64_t)p.n_mtiles * p.n_ntiles * ks < 2 * kNumCU && nkt / (2 * ks) >= 8) ks *= 2;
+    }
 #ifdef DORA_W0_FORCE_KSPLIT
     ks = DORA_W0_FORCE_KSPLIT;   // tile sweeps only
 #endif
     p.ksplit = ks;
     // Gram
+    const int gram_nkt = (int)((d_in + gram_bk - 1) / gram_bk);
     p.gram_tiles = (int)((r + kGramTile - 1) / kGramTile);
     const int nupper = p.gram_tiles * (p.gram_tiles + 1) / 2;
     int gs = (kNumCU + nupper - 1) / nupper;
-    const int max_split = p.nkt_w0 / 4 > 1 ? p.nkt_w0 / 4 : 1;
+    const int max_split = gram_nkt / 4 > 1 ? gram_nkt / 4 : 1;
     if (gs > max_split) gs = max_split;
     if (gs < 1) gs = 1;
     p.gram_split = gs;
@@ -1138,9 +1749,27 @@ NormPlan plan_norm(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool base_
     return p;
 }
 
+}  // namespace
+
+// The large-tile plan needs 16-byte aligned operands; calls whose pointers
+// are not aligned run the fallback plan, so the workspace covers both.
+NormPlan plan_norm(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool base_only) {
+    NormPlan p = plan_norm_impl(d_out, d_in, r, dtype, base_only, true);
+    p.bytes_needed = p.bytes;
+    if (p.big) {
+        const NormPlan f = plan_norm_impl(d_out, d_in, r, dtype, base_only, false);
+        if (f.bytes > p.bytes_needed) p.bytes_needed = f.bytes;
+    }
+    return p;
+}
+
 hipError_t launch_norm(const NormPlan& p, const void* W0, const void* A, const void* B, const float* m, float s,
                        float eps, float* wnorm, float* g, void* workspace, hipStream_t stream) {
     if (p.dtype == kF32) return norm_typed<float>(p, W0, A, B, m, s, eps, wnorm, g, workspace, stream);
+    if (p.big && !operands_aligned<bf16_t>(p, W0, A, B)) {
+        const NormPlan f = plan_norm_impl(p.d_out, p.d_in, p.r, p.dtype, p.base_only, false);
+        return norm_typed<bf16_t>(f, W0, A, B, m, s, eps, wnorm, g, workspace, stream);
+    }
     return norm_typed<bf16_t>(p, W0, A, B, m, s, eps, wnorm, g, workspace, stream);
 }
 
