@@ -1014,13 +1014,12 @@ struct Big {
     static constexpr int LBYTES = BM * ROWB, RBYTES = BN * ROWB;
     static constexpr int RING = LS * LBYTES + RS * RBYTES;
     static constexpr int LPW = BM / 16 / NW, RPW = BN / 16 / NW;   // DMA instructions per wave per tile
-    // epilogue: one half (128 rows) of the B tile, rows padded by 16 bytes
-    static constexpr int EB_ROWS = BM / WM;
+    // epilogue: two staging buffers of 64 B rows (rows padded by 16 bytes)
+    // and the per-row partials of two rounds
     static constexpr int EB_SLOTS = BN * 2 / 16 + 1;
     static constexpr int EB_PITCH = EB_SLOTS * 16;
-    static constexpr int EB_BYTES = EB_ROWS * EB_PITCH;
-    static constexpr int RED_BYTES = WN * BM * 4;
-    static constexpr int LDS_BYTES = RING > EB_BYTES + RED_BYTES ? RING : EB_BYTES + RED_BYTES;
+    static constexpr int EPI_BYTES = 2 * 64 * EB_PITCH + 2 * WN * 64 * 4;
+    static constexpr int LDS_BYTES = RING > EPI_BYTES ? RING : EPI_BYTES;
     static_assert(BM / 16 % NW == 0 && BN / 16 % NW == 0, "DMA groups split evenly across waves");
     static_assert(MT == WN, "each wave sums the base term of one 32-row block");
 };
@@ -1286,97 +1285,107 @@ __global__ __launch_bounds__(Big::NTH) void w0_pass_big(W0PassArgs a) {
 
     // cross partial: sum_n B[m][n] acc[m][n] over this workgroup's columns.
     // acc[mt][nt][e] is row mt*32 + 8 (e/4) + 4 (l/32) + e%4 of the wave's
-    // block and column nt*32 + l%32.  The B tile is staged in LDS one 128-row
-    // half at a time.
-    float* red = reinterpret_cast<float*>(smem + G::EB_BYTES);   // [WN][BM]
-    const int64_t rb = a.r * 2;
-    const int colb0 = (int)(n0 * 2);
-#pragma unroll 1
-    for (int hf = 0; hf < G::WM; ++hf) {
-        {
-            const int64_t rowh = m0 + hf * G::EB_ROWS;
-            const uint64_t addr = reinterpret_cast<uint64_t>(static_cast<const char*>(a.B) + rowh * rb);
-            int64_t bytes = (a.d_out - rowh) * rb;
-            if (bytes < 0) bytes = 0;
-            if (bytes > 0x7ffffff0) bytes = 0x7ffffff0;
-            i32x4_t rs;
-            rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
-            rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32));
-            rs[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-            rs[3] = 0x00020000;
-            constexpr int NINS = (G::EB_ROWS * G::EB_SLOTS + 63) / 64;
+    // 128 rows and column nt*32 + l%32 of its 96.  Round mt handles row block
+    // mt of both row halves (64 rows): its B rows are staged in LDS (double
+    // buffered, the next round's DMA overlaps this round's dots), every wave
+    // dots its accumulators with them, sums each row over its 32 lanes, and
+    // the four column waves' partials are added in order.
+    {
+        const int64_t rb = a.r * 2;
+        const int colb0 = (int)(n0 * 2);
+        const uint64_t baddr = reinterpret_cast<uint64_t>(static_cast<const char*>(a.B) + m0 * rb);
+        int64_t bbytes = (a.d_out - m0) * rb;
+        if (bbytes < 0) bbytes = 0;
+        if (bbytes > 0x7ffffff0) bbytes = 0x7ffffff0;
+        i32x4_t brs;
+        brs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)baddr);
+        brs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(baddr >> 32));
+        brs[2] = __builtin_amdgcn_readfirstlane((int)bbytes);
+        brs[3] = 0x00020000;
+        constexpr int ER = 64;                                // rows per round
+        constexpr int EBUF = ER * G::EB_PITCH;                // one staging buffer
+        float* red = reinterpret_cast<float*>(smem + 2 * EBUF);   // [2][WN][ER]
+        // staged row r of round mt is tile row (r / 32) * 128 + mt * 32 + r % 32
+        auto stage_b = [&](int mt, char* buf) __attribute__((always_inline)) {
+            constexpr int NINS = (ER * G::EB_SLOTS + 63) / 64;
 #pragma unroll
             for (int k = 0; k < (NINS + G::NW - 1) / G::NW; ++k) {
                 const int ins = wave + k * G::NW;
                 if (ins < NINS) {
                     const int slot = ins * 64 + lane;
                     const int row = slot / G::EB_SLOTS, ch = slot % G::EB_SLOTS;
+                    const int trow = (row >> 5) * 128 + mt * 32 + (row & 31);
                     const int colb = colb0 + ch * 16;
-                    const bool ok = ch < G::EB_SLOTS - 1 && row < G::EB_ROWS && colb < (int)rb;
-                    const int voff = ok ? row * (int)rb + colb : kOutOfRange;
-                    raw_buffer_load_lds(rs, (lds_void_t*)(smem + ins * 1024), 16, voff, 0, 0, 0);
+                    const bool ok = ch < G::EB_SLOTS - 1 && row < ER && colb < (int)rb;
+                    const int voff = ok ? trow * (int)rb + colb : kOutOfRange;
+                    raw_buffer_load_lds(brs, (lds_void_t*)(buf + ins * 1024), 16, voff, 0, 0, 0);
                 }
             }
+        };
+        auto store_round = [&](int mt) __attribute__((always_inline)) {
+            const float* rd = red + (mt & 1) * G::WN * ER;
+            for (int t = threadIdx.x; t < ER; t += G::NTH) {
+                const int64_t m = m0 + (t >> 5) * 128 + mt * 32 + (t & 31);
+                if (m < a.d_out) {
+                    float v = rd[t];
+#pragma unroll
+                    for (int w = 1; w < G::WN; ++w) v += rd[w * ER + t];
+                    a.part_cross[((int64_t)ntile * a.ksplit + kc) * a.d_out + m] = v;
+                }
+            }
+        };
+        stage_b(0, smem);
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) {
             wait_vmcnt<0>();
-        }
-        __syncthreads();
-        if (wm == hf) {
+            __syncthreads();   // round mt's B landed; round mt - 1's readers are done
+            if (mt + 1 < G::MT) stage_b(mt + 1, smem + ((mt + 1) & 1) * EBUF);
+            if (mt > 0) store_round(mt - 1);
+            const char* buf = smem + (mt & 1) * EBUF;
+            float v[16];
 #pragma unroll
-            for (int mt = 0; mt < G::MT; ++mt) {
-                float v[16];
+            for (int e = 0; e < 16; ++e) {
+                const int row = wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const bf16_t* brow = reinterpret_cast<const bf16_t*>(buf + row * G::EB_PITCH) + wn * 96 + (lane & 31);
+                float x = 0.0f;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int row = mt * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    const bf16_t* brow = reinterpret_cast<const bf16_t*>(smem + row * G::EB_PITCH) + wn * 96 +
-                                         (lane & 31);
-                    float x = 0.0f;
-#pragma unroll
-                    for (int nt = 0; nt < G::NT; ++nt) x = fmaf(static_cast<float>(brow[nt * 32]), acc[mt][nt][e], x);
-                    v[e] = x;
-                }
-                // sum each row over the 32 lanes that share l / 32, halving the
-                // number of rows a lane carries at every exchange
-                const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const float send = b4 ? v[s] : v[s + 8];
-                    const float keep = b4 ? v[s + 8] : v[s];
-                    v[s] = keep + __shfl_xor(send, 16);
-                }
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const float send = b3 ? v[s] : v[s + 4];
-                    const float keep = b3 ? v[s + 4] : v[s];
-                    v[s] = keep + __shfl_xor(send, 8);
-                }
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const float send = b2 ? v[s] : v[s + 2];
-                    const float keep = b2 ? v[s + 2] : v[s];
-                    v[s] = keep + __shfl_xor(send, 4);
-                }
-                {
-                    const float send = b1 ? v[0] : v[1];
-                    const float keep = b1 ? v[1] : v[0];
-                    v[0] = keep + __shfl_xor(send, 2);
-                }
-                v[0] += __shfl_xor(v[0], 1);
-                // lane l now holds the row with e = (l >> 1) & 15
-                const int e = (lane >> 1) & 15;
-                const int row = mt * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                if ((lane & 1) == 0) red[wn * G::BM + hf * G::EB_ROWS + row] = v[0];
+                for (int nt = 0; nt < G::NT; ++nt) x = fmaf(static_cast<float>(brow[nt * 32]), acc[mt][nt][e], x);
+                v[e] = x;
             }
+            // sum each row over the 32 lanes that share l / 32, halving the
+            // number of rows a lane carries at every exchange
+            const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float send = b4 ? v[q] : v[q + 8];
+                const float keep = b4 ? v[q + 8] : v[q];
+                v[q] = keep + __shfl_xor(send, 16);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float send = b3 ? v[q] : v[q + 4];
+                const float keep = b3 ? v[q + 4] : v[q];
+                v[q] = keep + __shfl_xor(send, 8);
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const float send = b2 ? v[q] : v[q + 2];
+                const float keep = b2 ? v[q + 2] : v[q];
+                v[q] = keep + __shfl_xor(send, 4);
+            }
+            {
+                const float send = b1 ? v[0] : v[1];
+                const float keep = b1 ? v[1] : v[0];
+                v[0] = keep + __shfl_xor(send, 2);
+            }
+            v[0] += __shfl_xor(v[0], 1);
+            // lane l now holds the row with e = (l >> 1) & 15
+            const int e = (lane >> 1) & 15;
+            const int row = wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            if ((lane & 1) == 0) red[(mt & 1) * G::WN * ER + wn * ER + row] = v[0];
         }
         __syncthreads();
-    }
-    for (int row = threadIdx.x; row < G::BM; row += G::NTH) {
-        const int64_t m = m0 + row;
-        if (m < a.d_out) {
-            float v = red[row];
-#pragma unroll
-            for (int w = 1; w < G::WN; ++w) v += red[w * G::BM + row];
-            a.part_cross[((int64_t)ntile * a.ksplit + kc) * a.d_out + m] = v;
-        }
+        store_round(G::MT - 1);
     }
 }
 
