@@ -31,6 +31,7 @@ struct NormPlan {
     // Gram
     int gram_tiles;     // tiles per side (64 wide)
     int gram_split;
+    bool gram_xcd;      // bf16 split-per-XCD Gram kernel (aligned operands)
     int64_t ldg;        // leading dimension of the scaled Gram operand
     // workspace layout (byte offsets)
     size_t off_gs, off_gpart, off_pbase, off_pcross, bytes;

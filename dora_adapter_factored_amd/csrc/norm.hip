@@ -517,6 +517,7 @@ __device__ __forceinline__ void mainloop_dma(const Contraction& c, int64_t m0, i
 __device__ i32x4_t raw_buffer_load_b128(i32x4_t rsrc, int voffset, int soffset, int aux) __asm(
     "llvm.amdgcn.raw.buffer.load.v4i32");
 
+
 // One operand of one phase as seen by direct-to-register fragment loads: a
 // buffer starting at the first of the 16-row blocks this wave reads.  Lane l
 // reads row l % 16 of a block, K elements 8 (l / 16) .. 8 (l / 16) + 7 of a
@@ -1009,16 +1010,21 @@ struct Big {
     static constexpr int BM = 256, BN = 384, BK = 32;
     static constexpr int WM = 2, WN = 4, NW = WM * WN, NTH = NW * 64;
     static constexpr int MT = 4, NT = 3;   // 32 x 32 blocks per wave
-    static constexpr int LS = 4, RS = 3;
+#ifndef DORA_BIG_LS
+#define DORA_BIG_LS 4
+#define DORA_BIG_RS 3
+#endif
+    static constexpr int LS = DORA_BIG_LS, RS = DORA_BIG_RS;   // ring stages (left W0 | B, right A | Gs)
+    static_assert(LS > RS && RS >= 2, "left tiles are issued before right tiles of the same step");
     static constexpr int ROWB = BK * 2;    // bytes of K per tile row
     static constexpr int LBYTES = BM * ROWB, RBYTES = BN * ROWB;
     static constexpr int RING = LS * LBYTES + RS * RBYTES;
     static constexpr int LPW = BM / 16 / NW, RPW = BN / 16 / NW;   // DMA instructions per wave per tile
     // epilogue: two staging buffers of 64 B rows (rows padded by 16 bytes)
-    // and the per-row partials of two rounds
+    // and the per-row partials of all four rounds
     static constexpr int EB_SLOTS = BN * 2 / 16 + 1;
     static constexpr int EB_PITCH = EB_SLOTS * 16;
-    static constexpr int EPI_BYTES = 2 * 64 * EB_PITCH + 2 * WN * 64 * 4;
+    static constexpr int EPI_BYTES = 2 * 64 * EB_PITCH + MT * WN * 64 * 4;
     static constexpr int LDS_BYTES = RING > EPI_BYTES ? RING : EPI_BYTES;
     static_assert(BM / 16 % NW == 0 && BN / 16 % NW == 0, "DMA groups split evenly across waves");
     static_assert(MT == WN, "each wave sums the base term of one 32-row block");
@@ -1216,26 +1222,29 @@ __global__ __launch_bounds__(Big::NTH) void w0_pass_big(W0PassArgs a) {
         // HOLD, and its base term.  Then wait for tile j + 1 (this wave's
         // loads; this wave's fragment reads of tile j are complete), barrier
         // (every wave's loads of tile j + 1 landed, every wave is done with
-        // tile j's stages), enqueue right(j + 3) and left(j + 4) into those
+        // tile j's stages), enqueue right(j + RS) and left(j + LS) into those
         // stages, read tile j + 1's step-0 fragments, and only then issue the
         // held-back MFMAs, which keep the matrix pipe busy across the barrier
-        // and the LDS latency.  Loads complete in issue order, so waiting for
-        // right(j + 1) covers left(j + 1), while left(j + 2), right(j + 2)
-        // and left(j + 3) stay in flight.
+        // and the LDS latency.  Loads complete in issue order and every left
+        // tile is issued one step or more before the right tile of the same
+        // index, so waiting for right(j + 1) covers left(j + 1); what may stay
+        // in flight is the left tile issued with right(j + 1) and everything
+        // issued at the RS - 2 later steps.
         constexpr int HOLD = 2;
         constexpr int ALL = G::MT * G::NT;
         constexpr int INFLIGHT = G::LPW + (G::RS - 2) * (G::RPW + G::LPW);
         auto main_loop = [&](auto wnc) __attribute__((always_inline)) {
             bf16x8_t a0[G::MT], b0[G::NT], a1[G::MT], b1[G::NT];
-            issue_left(0);
-            issue_right(0);
-            issue_left(1);
-            issue_right(1);
-            issue_left(2);
+            // the steps before tile 0, in the steady-state issue order
+#pragma unroll
+            for (int t = 0; t < G::LS - 1; ++t) {
+                if (t >= G::LS - G::RS) issue_right(t - (G::LS - G::RS));
+                issue_left(t);
+            }
             wait_vmcnt<INFLIGHT>();
             __builtin_amdgcn_s_barrier();
-            issue_right(2);
-            issue_left(3);
+            issue_right(G::RS - 1);
+            issue_left(G::LS - 1);
             read(0, fo0, a0, b0);
             for (int j = 0; j < n - 1; ++j) {
                 const float on = base_on_at(j);
@@ -1249,8 +1258,8 @@ __global__ __launch_bounds__(Big::NTH) void w0_pass_big(W0PassArgs a) {
                 wait_vmcnt<INFLIGHT>();
                 __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
                 __builtin_amdgcn_s_barrier();
-                issue_right(j + 3);
-                issue_left(j + 4);
+                issue_right(j + G::RS);
+                issue_left(j + G::LS);
                 read(j + 1, fo0, a0, b0);
                 __builtin_amdgcn_sched_barrier(0);
                 mma(a1, b1, ALL - HOLD, ALL);
@@ -1277,11 +1286,7 @@ __global__ __launch_bounds__(Big::NTH) void w0_pass_big(W0PassArgs a) {
 
     // base partial: lanes l and l + 32 hold the two K halves of row l % 32 of
     // block wn of this wave's 128 rows
-    if (base_dst) {
-        const float v = bs + __shfl_xor(bs, 32);
-        const int64_t m = m0 + wm * 128 + wn * 32 + lane;
-        if (lane < 32 && m < a.d_out) base_dst[m] = v;
-    }
+    const float base_part = bs + __shfl_xor(bs, 32);   // row l % 32 of block wn, lanes < 32
 
     // cross partial: sum_n B[m][n] acc[m][n] over this workgroup's columns.
     // acc[mt][nt][e] is row mt*32 + 8 (e/4) + 4 (l/32) + e%4 of the wave's
@@ -1304,7 +1309,7 @@ __global__ __launch_bounds__(Big::NTH) void w0_pass_big(W0PassArgs a) {
         brs[3] = 0x00020000;
         constexpr int ER = 64;                                // rows per round
         constexpr int EBUF = ER * G::EB_PITCH;                // one staging buffer
-        float* red = reinterpret_cast<float*>(smem + 2 * EBUF);   // [2][WN][ER]
+        float* red = reinterpret_cast<float*>(smem + 2 * EBUF);   // [MT][WN][ER]
         // staged row r of round mt is tile row (r / 32) * 128 + mt * 32 + r % 32
         auto stage_b = [&](int mt, char* buf) __attribute__((always_inline)) {
             constexpr int NINS = (ER * G::EB_SLOTS + 63) / 64;
@@ -1322,25 +1327,12 @@ __global__ __launch_bounds__(Big::NTH) void w0_pass_big(W0PassArgs a) {
                 }
             }
         };
-        auto store_round = [&](int mt) __attribute__((always_inline)) {
-            const float* rd = red + (mt & 1) * G::WN * ER;
-            for (int t = threadIdx.x; t < ER; t += G::NTH) {
-                const int64_t m = m0 + (t >> 5) * 128 + mt * 32 + (t & 31);
-                if (m < a.d_out) {
-                    float v = rd[t];
-#pragma unroll
-                    for (int w = 1; w < G::WN; ++w) v += rd[w * ER + t];
-                    a.part_cross[((int64_t)ntile * a.ksplit + kc) * a.d_out + m] = v;
-                }
-            }
-        };
         stage_b(0, smem);
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt) {
             wait_vmcnt<0>();
             __syncthreads();   // round mt's B landed; round mt - 1's readers are done
             if (mt + 1 < G::MT) stage_b(mt + 1, smem + ((mt + 1) & 1) * EBUF);
-            if (mt > 0) store_round(mt - 1);
             const char* buf = smem + (mt & 1) * EBUF;
             float v[16];
 #pragma unroll
@@ -1382,10 +1374,31 @@ __global__ __launch_bounds__(Big::NTH) void w0_pass_big(W0PassArgs a) {
             // lane l now holds the row with e = (l >> 1) & 15
             const int e = (lane >> 1) & 15;
             const int row = wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            if ((lane & 1) == 0) red[(mt & 1) * G::WN * ER + wn * ER + row] = v[0];
+            if ((lane & 1) == 0) red[mt * G::WN * ER + wn * ER + row] = v[0];
         }
         __syncthreads();
-        store_round(G::MT - 1);
+    }
+
+    // Publish this workgroup's partials: the base term of rows
+    // wm*128 + wn*32 + l (l < 32), and for every row the sum of the four
+    // column waves' dots, in wave order.
+    {
+        const float* red = reinterpret_cast<const float*>(smem + 2 * 64 * G::EB_PITCH);
+        if (base_dst) {
+            const int64_t mrow = m0 + wm * 128 + wn * 32 + lane;
+            if (lane < 32 && mrow < a.d_out) base_dst[mrow] = base_part;
+        }
+        for (int t = threadIdx.x; t < G::BM; t += G::NTH) {
+            const int mt = t >> 6, r = t & 63;
+            const int64_t mrow = m0 + (r >> 5) * 128 + mt * 32 + (r & 31);
+            if (mrow < a.d_out) {
+                const float* rd = red + mt * G::WN * 64;
+                float v = rd[r];
+#pragma unroll
+                for (int w = 1; w < G::WN; ++w) v += rd[w * 64 + r];
+                a.part_cross[((int64_t)ntile * a.ksplit + kc) * a.d_out + mrow] = v;
+            }
+        }
     }
 }
 
@@ -1439,6 +1452,100 @@ __global__ __launch_bounds__(256) void gram_partial(GramArgs a) {
             }
 }
 
+// Gram partials for bf16 operands with 16-byte aligned rows.  Split s of the
+// K range runs on XCD s % 8 (workgroup ids are dealt to XCDs round-robin), so
+// each XCD streams only its own K-slices of A and the whole of A crosses HBM
+// once.  Each workgroup walks its slice through an LDS ring of kGramStages
+// stages (left and right 64-row tiles), kGramStages - 1 tiles ahead.
+constexpr int kGramStages = 8;
+
+__global__ __launch_bounds__(256) void gram_split_bf16(GramArgs a) {
+    typedef Tile<bf16_t, 2, 2, 2, 2> TL;
+    typedef Mma<bf16_t> M;
+    constexpr int NS = kGramStages;
+    constexpr int STAGE = TL::LBYTES + TL::RBYTES;   // 8 KB + 8 KB
+    constexpr int LPW = 2 * (TL::BM / 8 / TL::NW);   // DMA instructions per wave per tile (left + right)
+    static_assert(LPW * (NS - 2) < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+    const int id = blockIdx.x;
+    const int xcd = id % kNumXCD, slot = id / kNumXCD;
+    const int split = xcd + kNumXCD * (slot / a.nupper);
+    if (split >= a.nsplit) return;
+    int u = slot % a.nupper, ti = 0;
+    while (u >= a.ntiles - ti) {
+        u -= a.ntiles - ti;
+        ++ti;
+    }
+    const int tj = ti + u;
+    const int nkt = a.c.nkt0;
+    const int kt_begin = (int)((int64_t)split * nkt / a.nsplit);
+    const int n = (int)((int64_t)(split + 1) * nkt / a.nsplit) - kt_begin;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / 2, wn = wave % 2;
+    const int q = lane >> 4;
+    const DmaSrc L = make_dma_src<bf16_t>(a.c.left0, (int64_t)ti * kGramTile, lane);
+    const DmaSrc R = make_dma_src<bf16_t>(a.c.left0, (int64_t)tj * kGramTile, lane);
+    constexpr int TKB = 128;
+    auto issue = [&](int i) __attribute__((always_inline)) {
+        char* st = smem + (i % NS) * STAGE;
+        const int k0b = (kt_begin + i) * TKB;
+        dma_tile<TL::BM, 0, TL::NW>(L, k0b, st, wave, TKB);
+        dma_tile<TL::BN, 0, TL::NW>(R, k0b, st + TL::LBYTES, wave, TKB);
+    };
+    int lrow[2], lsw[2], rrow[2], rsw[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        lrow[t] = wm * 32 + t * 16 + (lane & 15);
+        lsw[t] = swz(lrow[t]);
+        rrow[t] = wn * 32 + t * 16 + (lane & 15);
+        rsw[t] = swz(rrow[t]);
+    }
+    f32x4_t acc[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NS - 1 && i < n; ++i) issue(i);
+    for (int j = 0; j < n; ++j) {
+        if (j + NS - 2 < n)
+            wait_vmcnt<LPW * (NS - 2)>();
+        else
+            wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();   // tile j landed; the stage of tile j - 1 is free
+        if (j + NS - 1 < n) issue(j + NS - 1);
+        const char* Lt = smem + (j % NS) * STAGE;
+        const char* Rt = Lt + TL::LBYTES;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            M::frag_t av[2], bv[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                av[t] = M::load_frag_swz(Lt + lrow[t] * 128, ks, q, lsw[t]);
+                bv[t] = M::load_frag_swz(Rt + rrow[t] * 128, ks, q, rsw[t]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) M::mma(acc[mt][nt], av[mt], bv[nt]);
+        }
+    }
+    float* out = a.part + (int64_t)split * a.rnp * a.rnp;
+    // off-diagonal tiles are also written transposed: the partial buffer
+    // holds the full symmetric matrix, read row-wise by the finalize
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int64_t i = (int64_t)ti * kGramTile + wm * 32 + mt * 16 + 4 * (lane >> 4) + jj;
+                const int64_t k = (int64_t)tj * kGramTile + wn * 32 + nt * 16 + (lane & 15);
+                out[i * a.rnp + k] = acc[mt][nt][jj];
+                if (ti != tj) out[k * a.rnp + i] = acc[mt][nt][jj];
+            }
+}
+
 // Gs[i][j] = (s/2) * sum_split G[i][j] for i < r, j < r; zero for r <= j < ldg.
 // The split partials are summed in split order.
 template <typename E>
@@ -1453,13 +1560,12 @@ __global__ __launch_bounds__(256) void gram_finalize(const float* __restrict__ p
         const int64_t stride = rnp * rnp;
         float sum = 0.0f;
         int sp = 0;
-        for (; sp + 4 <= nsplit; sp += 4) {
-            const float x0 = p[(sp + 0) * stride], x1 = p[(sp + 1) * stride];
-            const float x2 = p[(sp + 2) * stride], x3 = p[(sp + 3) * stride];
-            sum += x0;
-            sum += x1;
-            sum += x2;
-            sum += x3;
+        for (; sp + 8 <= nsplit; sp += 8) {
+            float x[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) x[t] = p[(sp + t) * stride];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) sum += x[t];
         }
         for (; sp < nsplit; ++sp) sum += p[sp * stride];
         v = half_s * sum;
@@ -1599,11 +1705,16 @@ hipError_t norm_typed(const NormPlan& p, const void* W0, const void* A, const vo
     ga.nupper = p.gram_tiles * (p.gram_tiles + 1) / 2;
     ga.rnp = (int64_t)p.gram_tiles * kGramTile;
     ga.part = gpart;
-    const unsigned ggrid = (unsigned)(ga.nupper * ga.nsplit);
-    if (al)
-        gram_partial<E, true><<<ggrid, 256, 0, st>>>(ga);
-    else
-        gram_partial<E, false><<<ggrid, 256, 0, st>>>(ga);
+    if (sizeof(E) == 2 && al && p.gram_xcd) {
+        const unsigned ggrid = (unsigned)(kNumXCD * ((ga.nsplit + kNumXCD - 1) / kNumXCD) * ga.nupper);
+        gram_split_bf16<<<ggrid, 256, 0, st>>>(ga);
+    } else {
+        const unsigned ggrid = (unsigned)(ga.nupper * ga.nsplit);
+        if (al)
+            gram_partial<E, true><<<ggrid, 256, 0, st>>>(ga);
+        else
+            gram_partial<E, false><<<ggrid, 256, 0, st>>>(ga);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     gram_finalize<E><<<(unsigned)((r * p.ldg + 255) / 256), 256, 0, st>>>(gpart, ga.nsplit, ga.rnp, r, p.ldg,
                                                                           0.5f * s, gs);
@@ -1742,6 +1853,16 @@ NormPlan plan_norm_impl(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool 
     const int max_split = gram_nkt / 4 > 1 ? gram_nkt / 4 : 1;
     if (gs > max_split) gs = max_split;
     if (gs < 1) gs = 1;
+    // bf16: splits in whole multiples of the XCD count, one K-slice per XCD
+    // (at most 256 / nupper workgroups' worth, each >= 4 k-tiles)
+    p.gram_xcd = false;
+    if (dtype == kBF16 && gram_nkt >= 4 * kNumXCD) {
+        int x = kNumXCD;
+        while (x + kNumXCD <= 64 && (int64_t)(x + kNumXCD) * nupper <= kNumCU && gram_nkt / (x + kNumXCD) >= 4)
+            x += kNumXCD;
+        gs = x;
+        p.gram_xcd = true;
+    }
     p.gram_split = gs;
     p.ldg = (int64_t)align_up((size_t)r, (size_t)vec);
     const size_t rnp = (size_t)p.gram_tiles * kGramTile;

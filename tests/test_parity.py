@@ -82,6 +82,8 @@ EDGE_SHAPES = [
     (300, 136, 384, "f32"),      # fp32 with two slices of r
     (129, 256, 32, "bf16"), (129, 256, 64, "bf16"), (129, 256, 192, "bf16"), (129, 256, 384, "bf16"),
     (64, 48, 8, "f32"), (64, 48, 8, "bf16"),
+    (300, 1000, 384, "bf16"),    # 256-row tiles: ragged rows, K tail inside a 32-wide tile
+    (520, 8200, 200, "bf16"),    # 256-row tiles with r < 384 (ragged slice of r)
 ]
 
 
@@ -91,6 +93,23 @@ def test_norm_edge_shapes(d_out, d_in, r, dt):
     spec = DI.custom_spec(d_out, d_in, r, 1, dtype=dt, s=1.5, b_std=0.05)
     L = DI.make_layer(spec, 17 + d_out + r, device=DEV, activations=False)
     wn, g = gpu_norm(L)
+    ref_wn, ref_g = oracle_norm(L)
+    check_rel(host64(wn), ref_wn, NORM_RTOL[L.W0.dtype], "wnorm")
+    check_rel(host64(g), ref_g, NORM_RTOL[L.W0.dtype], "g")
+
+
+def test_norm_unaligned_operands_take_the_fallback_plan():
+    # a W0 that is not 16-byte aligned cannot use the LDS-DMA tiles; the call
+    # runs the register-staged plan inside the same workspace size
+    say("[parity] norm unaligned W0, r=384 bf16")
+    spec = DI.custom_spec(300, 520, 384, 1, dtype="bf16", s=1.5, b_std=0.05)
+    L = DI.make_layer(spec, 23, device=DEV, activations=False)
+    buf = torch.empty(L.W0.numel() + 1, dtype=L.W0.dtype, device=DEV)
+    W0u = buf[1:].view_as(L.W0)
+    W0u.copy_(L.W0)
+    assert W0u.data_ptr() % 16 != 0
+    wn, g = D.factored_norm(W0u, L.A, L.B, spec.s, L.m)
+    torch.cuda.synchronize()
     ref_wn, ref_g = oracle_norm(L)
     check_rel(host64(wn), ref_wn, NORM_RTOL[L.W0.dtype], "wnorm")
     check_rel(host64(g), ref_g, NORM_RTOL[L.W0.dtype], "g")
