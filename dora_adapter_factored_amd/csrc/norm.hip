@@ -1767,16 +1767,6 @@ hipError_t norm_typed(const NormPlan& p, const void* W0, const void* A, const vo
 
 namespace {
 
-// Rounds of 256 CUs a grid of `wgs` one-per-CU workgroups takes, and how full
-// they are; a k-split is scored on both (fewer rounds pay fewer prologue and
-// epilogue latencies), with a bonus when every XCD can own one K-chunk.
-double ksplit_score(int64_t wgs, int q) {
-    const int64_t rounds = (wgs + kNumCU - 1) / kNumCU;
-    const double fill = (double)wgs / (double)(rounds * kNumCU);
-    const bool xcd = q <= kNumXCD && kNumXCD % q == 0;
-    return fill - 0.02 * (double)(rounds - 1) + (xcd ? 0.03 : 0.0);
-}
-
 NormPlan plan_norm_impl(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool base_only, bool allow_big) {
     NormPlan p{};
     p.dtype = dtype;
@@ -1807,17 +1797,14 @@ NormPlan plan_norm_impl(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool 
         p.nkt_w0 = (int)((d_in + p.bk - 1) / p.bk);
         p.nkt_g = (int)((r + p.bk - 1) / p.bk);
         const int nkt = p.nkt_w0 + p.nkt_g;
-        // one 136 KB workgroup per CU: pick the split with the best-filled
-        // rounds, keeping >= 8 k-tiles per workgroup
+        // One 136 KB workgroup fits a CU.  Measured: a single round of
+        // workgroups beats several, whose every round pays the cold start and
+        // the epilogue again; so split K as far as one round allows (at most
+        // 256 workgroups), keeping >= 8 k-tiles per workgroup.
         const int64_t tiles = (int64_t)p.n_mtiles * p.n_ntiles;
-        double best = -1.0;
-        for (int k = 1; k <= 64 && nkt / k >= 8; ++k) {
-            const double sc = ksplit_score(tiles * k, p.n_ntiles * k);
-            if (sc > best + 1e-9) {
-                best = sc;
-                ks = k;
-            }
-        }
+        ks = tiles >= kNumCU ? 1 : (int)(kNumCU / tiles);
+        if (ks > 64) ks = 64;
+        while (ks > 1 && nkt / ks < 8) --ks;
     } else {
         // widest configuration this dtype instantiates (fp32 fragments double
         // the register footprint, so fp32 stops at BN = 192)
