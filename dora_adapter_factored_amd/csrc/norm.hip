@@ -1487,9 +1487,15 @@ __global__ __launch_bounds__(256) void gram_split_bf16(GramArgs a) {
     const DmaSrc L = make_dma_src<bf16_t>(a.c.left0, (int64_t)ti * kGramTile, lane);
     const DmaSrc R = make_dma_src<bf16_t>(a.c.left0, (int64_t)tj * kGramTile, lane);
     constexpr int TKB = 128;
+    // the K walk starts at a tile that differs between the workgroups of a
+    // split, so that the six tiles sharing a row block do not request the
+    // same lines at the same time
+    const int rot = n > 0 ? (int)((unsigned)(slot * 5) % (unsigned)n) : 0;
     auto issue = [&](int i) __attribute__((always_inline)) {
         char* st = smem + (i % NS) * STAGE;
-        const int k0b = (kt_begin + i) * TKB;
+        int t = i + rot;
+        if (t >= n) t -= n;
+        const int k0b = (kt_begin + t) * TKB;
         dma_tile<TL::BM, 0, TL::NW>(L, k0b, st, wave, TKB);
         dma_tile<TL::BN, 0, TL::NW>(R, k0b, st + TL::LBYTES, wave, TKB);
     };
@@ -1506,44 +1512,85 @@ __global__ __launch_bounds__(256) void gram_split_bf16(GramArgs a) {
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < NS - 1 && i < n; ++i) issue(i);
-    for (int j = 0; j < n; ++j) {
-        if (j + NS - 2 < n)
-            wait_vmcnt<LPW * (NS - 2)>();
+    // Tiles move in groups of GT = NS / 2: group g + 1 loads while group g
+    // is computed, with two barriers per group.
+    constexpr int GT = NS / 2;
+    const int ngroups = (n + GT - 1) / GT;
+    auto issue_group = [&](int grp) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < GT; ++t)
+            if (grp * GT + t < n) issue(grp * GT + t);
+    };
+    issue_group(0);
+    issue_group(1);
+    for (int grp = 0; grp < ngroups; ++grp) {
+        // group grp landed (only group grp + 1, if full, may be in flight)
+        if ((grp + 2) * GT <= n)
+            wait_vmcnt<LPW * GT>();
         else
             wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();   // tile j landed; the stage of tile j - 1 is free
-        if (j + NS - 1 < n) issue(j + NS - 1);
-        const char* Lt = smem + (j % NS) * STAGE;
-        const char* Rt = Lt + TL::LBYTES;
+        __builtin_amdgcn_s_barrier();
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            M::frag_t av[2], bv[2];
+        for (int t = 0; t < GT; ++t) {
+            const int jj = grp * GT + t;
+            if (jj >= n) break;
+            const char* Lt = smem + (jj % NS) * STAGE;
+            const char* Rt = Lt + TL::LBYTES;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                av[t] = M::load_frag_swz(Lt + lrow[t] * 128, ks, q, lsw[t]);
-                bv[t] = M::load_frag_swz(Rt + rrow[t] * 128, ks, q, rsw[t]);
+            for (int ks = 0; ks < 2; ++ks) {
+                M::frag_t av[2], bv[2];
+#pragma unroll
+                for (int q2 = 0; q2 < 2; ++q2) {
+                    av[q2] = M::load_frag_swz(Lt + lrow[q2] * 128, ks, q, lsw[q2]);
+                    bv[q2] = M::load_frag_swz(Rt + rrow[q2] * 128, ks, q, rsw[q2]);
+                }
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) M::mma(acc[mt][nt], av[mt], bv[nt]);
             }
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) M::mma(acc[mt][nt], av[mt], bv[nt]);
         }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's reads of group grp are done
+        __builtin_amdgcn_s_barrier();         // every wave's are: the group's stages are free
+        issue_group(grp + 2);
     }
-    float* out = a.part + (int64_t)split * a.rnp * a.rnp;
-    // off-diagonal tiles are also written transposed: the partial buffer
-    // holds the full symmetric matrix, read row-wise by the finalize
+
+    // Write the partial tile, and its transpose for off-diagonal tiles, as
+    // coalesced 16-byte row segments staged through LDS (the ring is free).
+    float* tl = reinterpret_cast<float*>(smem);   // [64][TP]
+    constexpr int TP = kGramTile + 4;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int64_t i = (int64_t)ti * kGramTile + wm * 32 + mt * 16 + 4 * (lane >> 4) + jj;
-                const int64_t k = (int64_t)tj * kGramTile + wn * 32 + nt * 16 + (lane & 15);
-                out[i * a.rnp + k] = acc[mt][nt][jj];
-                if (ti != tj) out[k * a.rnp + i] = acc[mt][nt][jj];
+                const int ii = wm * 32 + mt * 16 + 4 * (lane >> 4) + jj;
+                const int kk = wn * 32 + nt * 16 + (lane & 15);
+                tl[ii * TP + kk] = acc[mt][nt][jj];
             }
+    __syncthreads();
+    float* out = a.part + (int64_t)split * a.rnp * a.rnp;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int rep = 0; rep < 4; ++rep) {
+        const int e = rep * 256 + tid;        // 1024 segments of 4 floats
+        const int row = e >> 4, c4 = (e & 15) * 4;
+        f32x4_t v;
+        v[0] = tl[row * TP + c4];
+        v[1] = tl[row * TP + c4 + 1];
+        v[2] = tl[row * TP + c4 + 2];
+        v[3] = tl[row * TP + c4 + 3];
+        *reinterpret_cast<f32x4_t*>(out + ((int64_t)ti * kGramTile + row) * a.rnp + (int64_t)tj * kGramTile + c4) = v;
+        if (ti != tj) {
+            f32x4_t w;
+            w[0] = tl[(c4 + 0) * TP + row];
+            w[1] = tl[(c4 + 1) * TP + row];
+            w[2] = tl[(c4 + 2) * TP + row];
+            w[3] = tl[(c4 + 3) * TP + row];
+            *reinterpret_cast<f32x4_t*>(out + ((int64_t)tj * kGramTile + row) * a.rnp + (int64_t)ti * kGramTile + c4) = w;
+        }
+    }
 }
 
 // Gs[i][j] = (s/2) * sum_split G[i][j] for i < r, j < r; zero for r <= j < ldg.
@@ -1844,7 +1891,11 @@ NormPlan plan_norm_impl(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool 
     // (at most 256 / nupper workgroups' worth, each >= 4 k-tiles)
     p.gram_xcd = false;
     if (dtype == kBF16 && gram_nkt >= 4 * kNumXCD) {
+#ifdef DORA_GRAM_SPLIT
+        int x = DORA_GRAM_SPLIT;   // tuning sweeps only
+#else
         int x = kNumXCD;
+#endif
         while (x + kNumXCD <= 64 && (int64_t)(x + kNumXCD) * nupper <= kNumCU && gram_nkt / (x + kNumXCD) >= 4)
             x += kNumXCD;
         gs = x;
