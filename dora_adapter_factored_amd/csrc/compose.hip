@@ -24,17 +24,19 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTC = 64;          // packets along d_out per workgroup
 constexpr int kTR = 4;           // row lanes per workgroup
-constexpr int kRPT = 4;          // rows per thread per step (loads in flight)
-constexpr int kFwdRowsPerBlock = kTR * kRPT;
-constexpr int kBwdTokenBlock = 32;   // rows summed into one d_m partial row
-constexpr int kMaxParts = 1024;      // cap on d_m partial rows (grid-strides beyond)
+constexpr int kMaxParts = 1024;  // cap on d_m partial rows (grid-strides beyond)
+// Rows per thread per step (loads in flight) and rows per d_m partial are
+// template parameters chosen per shape from measurements on MI355X: wide
+// activations run fastest with more, smaller workgroups (RPT 2 forward,
+// 16-row token blocks backward), narrow ones with more rows in flight.
 constexpr int kMaxGridY = 65535;
 
-template <typename T, bool DELTA>
+template <typename T, bool DELTA, int kRPT>
 __global__ __launch_bounds__(kThreads) void compose_fwd_vec(const T* base, const T* __restrict__ lora,
                                                             const float* __restrict__ g, float s,
                                                             int64_t nrows, int64_t d_out, T* y) {
     constexpr int N = Pack<T>::N;
+    constexpr int kFwdRowsPerBlock = kTR * kRPT;
     const int tc = threadIdx.x % kTC, tr = threadIdx.x / kTC;
     const int64_t col = ((int64_t)blockIdx.x * kTC + tc) * N;
     if (col >= d_out) return;
@@ -88,13 +90,14 @@ __global__ __launch_bounds__(kThreads) void compose_fwd_scalar(const T* base, co
     }
 }
 
-template <typename T, bool DELTA, bool DM, bool DB, bool DL>
+template <typename T, bool DELTA, bool DM, bool DB, bool DL, int kRPT, int kBwdTokenBlock>
 __global__ __launch_bounds__(kThreads) void compose_bwd_vec(const T* dy, const T* __restrict__ base,
                                                             const T* __restrict__ lora,
                                                             const float* __restrict__ g, float s,
                                                             int64_t nrows, int64_t d_out, T* d_base,
                                                             T* d_lora, float* __restrict__ dm_part) {
     constexpr int N = Pack<T>::N;
+    static_assert(kBwdTokenBlock % (kTR * kRPT) == 0, "token block is whole steps");
     constexpr int kSteps = kBwdTokenBlock / (kTR * kRPT);
     __shared__ float red[kTR - 1][kTC * N];
     const int tc = threadIdx.x % kTC, tr = threadIdx.x / kTC;
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void compose_bwd_vec(const T* dy, const T
     }
 }
 
-template <typename T, bool DELTA, bool DM, bool DB, bool DL>
+template <typename T, bool DELTA, bool DM, bool DB, bool DL, int kBwdTokenBlock>
 __global__ __launch_bounds__(kThreads) void compose_bwd_scalar(const T* dy, const T* __restrict__ base,
                                                                const T* __restrict__ lora,
                                                                const float* __restrict__ g, float s,
@@ -220,8 +223,14 @@ __global__ __launch_bounds__(kThreads) void dm_finalize(const float* __restrict_
 
 inline bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-int bwd_parts(int64_t T) {
-    int64_t p = (T + kBwdTokenBlock - 1) / kBwdTokenBlock;
+// Backward tiling for a shape: narrow activations keep 8 rows per thread in
+// flight over 32-row token blocks, wide ones 4 rows over 16-row blocks.
+bool bwd_narrow(int64_t d_out) { return d_out <= 4096; }
+int bwd_token_block(int64_t d_out) { return bwd_narrow(d_out) ? 32 : 16; }
+
+int bwd_parts(int64_t T, int64_t d_out) {
+    const int tb = bwd_token_block(d_out);
+    int64_t p = (T + tb - 1) / tb;
     return (int)(p < kMaxParts ? p : kMaxParts);
 }
 
@@ -235,13 +244,22 @@ hipError_t fwd_typed(const void* base, const void* lora, const float* g, float s
     if (d_out % N == 0 && aligned16(base) && aligned16(lora) && aligned16(y)) {
         const int64_t nvec = d_out / N;
         const int64_t gx = (nvec + kTC - 1) / kTC;
-        int64_t gy = (nrows + kFwdRowsPerBlock - 1) / kFwdRowsPerBlock;
+        const bool wide = d_out >= 8192;
+        const int rpb = kTR * (wide ? 2 : 4);
+        int64_t gy = (nrows + rpb - 1) / rpb;
         if (gy > kMaxGridY) gy = kMaxGridY;
         dim3 grid((unsigned)gx, (unsigned)gy);
-        if (delta)
-            compose_fwd_vec<T, true><<<grid, kThreads, 0, st>>>(b, l, g, s, nrows, d_out, o);
-        else
-            compose_fwd_vec<T, false><<<grid, kThreads, 0, st>>>(b, l, g, s, nrows, d_out, o);
+        if (wide) {
+            if (delta)
+                compose_fwd_vec<T, true, 2><<<grid, kThreads, 0, st>>>(b, l, g, s, nrows, d_out, o);
+            else
+                compose_fwd_vec<T, false, 2><<<grid, kThreads, 0, st>>>(b, l, g, s, nrows, d_out, o);
+        } else {
+            if (delta)
+                compose_fwd_vec<T, true, 4><<<grid, kThreads, 0, st>>>(b, l, g, s, nrows, d_out, o);
+            else
+                compose_fwd_vec<T, false, 4><<<grid, kThreads, 0, st>>>(b, l, g, s, nrows, d_out, o);
+        }
     } else {
         const int64_t n = nrows * d_out;
         int64_t gx = (n + kThreads - 1) / kThreads;
@@ -257,16 +275,25 @@ hipError_t fwd_typed(const void* base, const void* lora, const float* g, float s
 template <typename T, bool DELTA, bool DM, bool DB, bool DL>
 void bwd_launch(bool vec, const T* dy, const T* b, const T* l, const float* g, float s, int64_t nrows,
                 int64_t d_out, T* db, T* dl, float* part, int nparts, hipStream_t st) {
+    const bool narrow = bwd_narrow(d_out);
     if (vec) {
         constexpr int N = Pack<T>::N;
         const int64_t gx = (d_out / N + kTC - 1) / kTC;
         dim3 grid((unsigned)gx, (unsigned)nparts);
-        compose_bwd_vec<T, DELTA, DM, DB, DL><<<grid, kThreads, 0, st>>>(dy, b, l, g, s, nrows, d_out, db,
-                                                                        dl, part);
+        if (narrow)
+            compose_bwd_vec<T, DELTA, DM, DB, DL, 8, 32><<<grid, kThreads, 0, st>>>(dy, b, l, g, s, nrows, d_out,
+                                                                                   db, dl, part);
+        else
+            compose_bwd_vec<T, DELTA, DM, DB, DL, 4, 16><<<grid, kThreads, 0, st>>>(dy, b, l, g, s, nrows, d_out,
+                                                                                   db, dl, part);
     } else {
         dim3 grid((unsigned)((d_out + kThreads - 1) / kThreads), (unsigned)nparts);
-        compose_bwd_scalar<T, DELTA, DM, DB, DL><<<grid, kThreads, 0, st>>>(dy, b, l, g, s, nrows, d_out,
-                                                                           db, dl, part);
+        if (narrow)
+            compose_bwd_scalar<T, DELTA, DM, DB, DL, 32><<<grid, kThreads, 0, st>>>(dy, b, l, g, s, nrows, d_out,
+                                                                                   db, dl, part);
+        else
+            compose_bwd_scalar<T, DELTA, DM, DB, DL, 16><<<grid, kThreads, 0, st>>>(dy, b, l, g, s, nrows, d_out,
+                                                                                   db, dl, part);
     }
 }
 
@@ -300,14 +327,15 @@ hipError_t bwd_typed(const void* dy, const void* base, const void* lora, const f
                          (!want_dm || (aligned16(base) && aligned16(lora)));
         float* part = static_cast<float*>(ws);
         if (want_dm) {
-            const int nparts = bwd_parts(nrows);
+            const int nparts = bwd_parts(nrows, d_out);
             if (delta)
                 bwd_dispatch_outputs<T, true, true>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
             else
                 bwd_dispatch_outputs<T, false, true>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
         } else {
             // frozen magnitude: only dy is read; the token grid needs no partials
-            int64_t gy = (nrows + kBwdTokenBlock - 1) / kBwdTokenBlock;
+            const int tb = bwd_token_block(d_out);
+            int64_t gy = (nrows + tb - 1) / tb;
             const int nblk = (int)(gy < kMaxGridY ? gy : kMaxGridY);
             if (delta)
                 bwd_dispatch_outputs<T, true, false>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, nullptr, nblk, st);
@@ -318,7 +346,7 @@ hipError_t bwd_typed(const void* dy, const void* base, const void* lora, const f
         if (e != hipSuccess) return e;
     }
     if (want_dm) {
-        const int nparts = nrows > 0 ? bwd_parts(nrows) : 0;
+        const int nparts = nrows > 0 ? bwd_parts(nrows, d_out) : 0;
         dm_finalize<<<(unsigned)((d_out + kFinCols - 1) / kFinCols), kThreads, 0, st>>>(
             static_cast<const float*>(ws), nparts, wnorm, eps, d_out, d_m);
         return hipGetLastError();
@@ -330,7 +358,7 @@ hipError_t bwd_typed(const void* dy, const void* base, const void* lora, const f
 
 size_t compose_bwd_workspace_bytes(int64_t T, int64_t d_out) {
     if (T <= 0) return 0;
-    return align_up((size_t)bwd_parts(T) * (size_t)d_out * sizeof(float), 256);
+    return align_up((size_t)bwd_parts(T, d_out) * (size_t)d_out * sizeof(float), 256);
 }
 
 hipError_t launch_compose_fwd(const void* base, const void* lora, const float* g, float s, int64_t T,

@@ -52,8 +52,14 @@ def test_workspace_queries(lib):
     assert lib.dora_factored_norm_workspace_size(64, 48, 8, 7, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
     assert lib.dora_factored_norm_workspace_size(64, 48, 8, 2, ctypes.byref(n)) == Bn.DORA_ERR_UNSUPPORTED
     assert lib.dora_factored_norm_workspace_size(64, 48, 8, 1, None) == Bn.DORA_ERR_INVALID_ARG
+    # d_m partial rows: one per token block (16 rows for d_out > 4096, else
+    # 32), at most 1024 rows, fp32
     assert lib.dora_compose_backward_workspace_size(2048, 8192, ctypes.byref(n)) == 0
-    assert n.value == 64 * 8192 * 4
+    assert n.value == 128 * 8192 * 4
+    assert lib.dora_compose_backward_workspace_size(2048, 4096, ctypes.byref(n)) == 0
+    assert n.value == 64 * 4096 * 4
+    assert lib.dora_compose_backward_workspace_size(1 << 20, 8192, ctypes.byref(n)) == 0
+    assert n.value == 1024 * 8192 * 4
     assert lib.dora_compose_backward_workspace_size(0, 8192, ctypes.byref(n)) == 0 and n.value == 0
     assert lib.dora_compose_backward_workspace_size(-1, 8192, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
 
