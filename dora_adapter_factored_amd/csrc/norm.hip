@@ -1651,11 +1651,27 @@ __global__ __launch_bounds__(256) void norm_finalize(const float* __restrict__ p
                                                      float* __restrict__ wnorm, float* __restrict__ g) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= d_out) return;
+    // partials are loaded in batches of 16 (both kinds together) before they
+    // are summed, each kind in partial order
     float base = 0.0f, cd = 0.0f;
-#pragma unroll 8
-    for (int c = 0; c < nbase; ++c) base += pbase[(int64_t)c * d_out + i];
-#pragma unroll 8
-    for (int c = 0; c < ncross; ++c) cd += pcross[(int64_t)c * d_out + i];
+    const int total = nbase + ncross;
+    for (int c0 = 0; c0 < total; c0 += 16) {
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int c = c0 + t;
+            x[t] = c < nbase ? pbase[(int64_t)c * d_out + i]
+                             : (c < total ? pcross[(int64_t)(c - nbase) * d_out + i] : 0.0f);
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int c = c0 + t;
+            if (c < nbase)
+                base += x[t];
+            else if (c < total)
+                cd += x[t];
+        }
+    }
     const float n2 = fmaxf(fmaf(two_s, cd, base), 0.0f);
     const float wn = sqrtf(n2);
     wnorm[i] = wn;
