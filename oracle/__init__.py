@@ -11,6 +11,8 @@ from .dora_oracle import (  # noqa: F401
     magnitude_scale,
     compose_forward,
     compose_backward,
+    compose_forward_inner,
+    compose_backward_inner,
     dora_linear_forward,
     merged_weight,
 )

@@ -133,6 +133,37 @@ def compose_forward(base_out, lora_out, g, s, delta_only=False) -> np.ndarray:
     return g * (base + s * lora)
 
 
+def compose_forward_inner(base_out, lora_out, g, s, delta_only=False):
+    """Dual-output forward of the training tier ([ScalingDoRA] §4, Tier 1:
+    one kernel produces the layer output and the inner term together).
+
+    Returns (y, inner) with inner_tj = base_tj + s * lora_tj, the factor
+    that g multiplies (y = g * inner) and the only activation the magnitude
+    gradient needs; y is compose_forward's output (or the delta).
+    """
+    base, lora = as_f64(base_out), as_f64(lora_out)
+    inner = base + float(s) * lora
+    return compose_forward(base_out, lora_out, g, s, delta_only=delta_only), inner
+
+
+def compose_backward_inner(dy, inner, g, wnorm, s, eps, delta_only=False):
+    """Backward of the training tier from (dy, inner) alone, norm detached.
+
+    With y = g * inner and inner = base + s lora ([ScalingDoRA] §4, Tier 1;
+    the norm detached as in [DoRA-wiki] and [ScalingDoRA] Data Availability):
+      d_base = g * dy          (delta_only: (g - 1) * dy)
+      d_lora = g * s * dy
+      d_m_j  = sum_t dy_tj * inner_tj / max(wnorm_j, eps)
+    Returns (d_base, d_lora, d_m).
+    """
+    dy, inner, g, wnorm = as_f64(dy), as_f64(inner), as_f64(g), as_f64(wnorm)
+    s = float(s)
+    d_base = ((g - 1.0) if delta_only else g) * dy
+    d_lora = (g * s) * dy
+    d_m = np.sum(dy * inner, axis=0) / np.maximum(wnorm, eps)
+    return d_base, d_lora, d_m
+
+
 def compose_backward(dy, base_out, lora_out, g, wnorm, s, eps, delta_only=False):
     """Gradients of compose_forward with the norm detached.
 

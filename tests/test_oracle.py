@@ -91,6 +91,43 @@ def test_compose_small_forward_backward():
     np.testing.assert_array_equal(dm2, dm)
 
 
+def test_compose_inner_small():
+    # the dual-output forward and the (dy, inner) backward on a hand-worked layer
+    c = load("compose_inner_small.json")
+    y, inner = oracle.compose_forward_inner(c["base_out"], c["lora_out"], c["g"], c["s"])
+    np.testing.assert_array_equal(inner, arr(c["inner"]))
+    np.testing.assert_array_equal(y, arr(c["y"]))
+    db, dl, dm = oracle.compose_backward_inner(c["dy"], c["inner"], c["g"], c["wnorm"], c["s"], c["eps"])
+    np.testing.assert_array_equal(db, arr(c["d_base"]))
+    np.testing.assert_array_equal(dl, arr(c["d_lora"]))
+    np.testing.assert_array_equal(dm, arr(c["d_m"]))
+    db2, _, _ = oracle.compose_backward_inner(c["dy"], c["inner"], c["g"], c["wnorm"], c["s"], c["eps"],
+                                              delta_only=True)
+    np.testing.assert_array_equal(db2, arr(c["d_base_delta"]))
+
+
+def test_inner_backward_finite_differences():
+    # L = sum(dy * (m / max(wnorm, eps)) * inner), wnorm fixed: d_m by central
+    # differences in m; d_base and d_lora through inner = base + s lora
+    rng = np.random.default_rng(21)
+    T, d_out, s, eps = 6, 5, 1.3, 1e-12
+    base, lora, dy = (rng.standard_normal((T, d_out)) for _ in range(3))
+    wnorm, m = rng.uniform(0.5, 2.0, d_out), rng.uniform(0.5, 2.0, d_out)
+
+    def loss(b, l, mm):
+        return float(np.sum(dy * (mm / np.maximum(wnorm, eps)) * (b + s * l)))
+
+    db, dl, dm = oracle.compose_backward_inner(dy, base + s * lora, m / wnorm, wnorm, s, eps)
+    h = 1e-6
+    for j in range(d_out):
+        e = np.zeros(d_out); e[j] = h
+        assert abs((loss(base, lora, m + e) - loss(base, lora, m - e)) / (2 * h) - dm[j]) < 1e-7
+    for (i, j) in [(0, 0), (5, 4), (2, 3)]:
+        e = np.zeros((T, d_out)); e[i, j] = h
+        assert abs((loss(base + e, lora, m) - loss(base - e, lora, m)) / (2 * h) - db[i, j]) < 1e-7
+        assert abs((loss(base, lora + e, m) - loss(base, lora - e, m)) / (2 * h) - dl[i, j]) < 1e-7
+
+
 # ------------------------------------------------- special cases / closed forms
 
 @pytest.mark.parametrize("shape", [(7, 5, 3), (1, 9, 2), (12, 4, 6), (33, 17, 1)])
