@@ -58,6 +58,16 @@ def compose_bwd_bytes(T, d_out, esz):
     return 5 * T * d_out * esz + 3 * d_out * 4
 
 
+def compose_dual_bytes(T, d_out, esz):
+    # base, lora read; y and inner written; g read
+    return 4 * T * d_out * esz + d_out * 4
+
+
+def compose_bwd_inner_bytes(T, d_out, esz):
+    # dy, inner read; d_base, d_lora written; g, wnorm read; d_m written
+    return 4 * T * d_out * esz + 3 * d_out * 4
+
+
 COPY_CALIB_BYTES = 256 << 20
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 NORM_SOURCES = ("dora_adapter_factored_amd/csrc/norm.hip", "dora_adapter_factored_amd/csrc/dora_launch.h",
@@ -196,7 +206,7 @@ def main():
     eps = D.default_eps(dt)
 
     # rotating copies: one step touches its own set of inputs and outputs
-    step_bytes = (d_out * d_in + 2 * r * (d_in + d_out)) * esz + 6 * T * d_out * esz
+    step_bytes = (d_out * d_in + 2 * r * (d_in + d_out)) * esz + 7 * T * d_out * esz
     nsets = max(2, int(np.ceil(2 * MALL_BYTES / step_bytes)) + 1)
     sets = []
     for i in range(nsets):
@@ -204,7 +214,8 @@ def main():
         sets.append(dict(W0=c(layer.W0), A=c(layer.A), B=c(layer.B), m=c(layer.m), base=c(layer.base_out),
                          lora=c(layer.lora_out), dy=c(layer.dy),
                          wn=torch.empty(d_out, device=dev), g=torch.empty(d_out, device=dev),
-                         y=torch.empty_like(layer.base_out), db=torch.empty_like(layer.base_out),
+                         y=torch.empty_like(layer.base_out), inner=torch.empty_like(layer.base_out),
+                         db=torch.empty_like(layer.base_out),
                          dl=torch.empty_like(layer.base_out), dm=torch.empty(d_out, device=dev)))
     ws_norm = torch.empty(D.norm_workspace_size(d_out, d_in, r, dt), dtype=torch.uint8, device=dev)
     ws_bwd = torch.empty(max(1, D.compose_backward_workspace_size(T, d_out)), dtype=torch.uint8, device=dev)
@@ -219,6 +230,13 @@ def main():
     def run_bwd(st):
         D.compose_backward(st["dy"], st["base"], st["lora"], st["g"], st["wn"], s, eps,
                            d_base=st["db"], d_lora=st["dl"], d_m=st["dm"], ws=ws_bwd)
+
+    def run_dual(st):
+        D.compose_dual(st["base"], st["lora"], st["g"], s, out=st["y"], inner=st["inner"])
+
+    def run_bwd_inner(st):
+        D.compose_backward_inner(st["dy"], st["inner"], st["g"], st["wn"], s, eps,
+                                 d_base=st["db"], d_lora=st["dl"], d_m=st["dm"], ws=ws_bwd)
 
     def step(st):
         run_norm(st)
@@ -272,6 +290,10 @@ def main():
     t_norm = per_call(run_norm)
     t_fwd = per_call(run_fwd)
     t_bwd = per_call(run_bwd)
+    # the training tier (one saved activation): measured beside the step
+    t_dual = per_call(run_dual)
+    t_bwdi = per_call(run_bwd_inner)
+    db_, bib = compose_dual_bytes(T, d_out, esz), compose_bwd_inner_bytes(T, d_out, esz)
     F = norm_flops(d_out, d_in, r)
     nb = norm_bytes(d_out, d_in, r, esz)
     fb, bb = compose_fwd_bytes(T, d_out, esz), compose_bwd_bytes(T, d_out, esz)
@@ -305,6 +327,11 @@ def main():
         "compose_bwd": {"ms": round(t_bwd * 1e3, 4), "GBps": round(bwd_gbs, 1),
                         "frac_hbm_peak": round(bwd_gbs / PEAK_HBM_GBS, 4),
                         "frac_measured_copy": round(bwd_gbs / calib["GBps"], 4), "algorithmic_bytes": bb},
+        "compose_dual": {"ms": round(t_dual * 1e3, 4), "GBps": round(db_ / t_dual / 1e9, 1),
+                         "frac_hbm_peak": round(db_ / t_dual / 1e9 / PEAK_HBM_GBS, 4), "algorithmic_bytes": db_},
+        "compose_bwd_inner": {"ms": round(t_bwdi * 1e3, 4), "GBps": round(bib / t_bwdi / 1e9, 1),
+                              "frac_hbm_peak": round(bib / t_bwdi / 1e9 / PEAK_HBM_GBS, 4),
+                              "algorithmic_bytes": bib},
         "copy_calibration": calib,
         "roofline": {"kernel": "dora_factored_norm (Gram partials, Gram finalize, W0 pass, norm finalize)",
                      "bound": "mfma", "achieved": round(norm_tflops, 2), "peak": peak_mm, "unit": "TFLOP/s",

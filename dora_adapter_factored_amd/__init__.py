@@ -8,9 +8,12 @@ first call does, and raises ImportError if it has not been built.
 from .binding import (  # noqa: F401
     DoraError,
     DoRACompose,
+    DoRAComposeInner,
     EXPORTED,
     compose,
     compose_backward,
+    compose_backward_inner,
+    compose_dual,
     compose_backward_workspace_size,
     default_eps,
     factored_norm,

@@ -35,6 +35,10 @@ _SIGNATURES = {
     "dora_compose_backward_workspace_size": (ctypes.c_int, [_i64, _i64, ctypes.POINTER(_sz)]),
     "dora_compose_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _f32, _i64, _i64, ctypes.c_int,
                                              ctypes.c_int, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "dora_compose_dual": (ctypes.c_int, [_vp, _vp, _vp, _f32, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp,
+                                         _vp]),
+    "dora_compose_backward_inner": (ctypes.c_int, [_vp, _vp, _vp, _vp, _f32, _f32, _i64, _i64, ctypes.c_int,
+                                                   ctypes.c_int, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -228,6 +232,68 @@ def compose_backward(dy, base_out, lora_out, g, wnorm, s: float, eps: float | No
     return (d_base if need_d_base else None, d_lora if need_d_lora else None, d_m if need_d_m else None)
 
 
+def compose_dual(base_out, lora_out, g, s: float, delta_only: bool = False, *, out=None, inner=None):
+    """(y, inner): the compose output and inner = base + s*lora from one pass."""
+    lib = load()
+    dev = base_out.device
+    T, d_out = base_out.shape
+    _need(base_out, "base_out", dev)
+    _need(lora_out, "lora_out", dev, base_out.dtype, (T, d_out))
+    _need(g, "g", dev, torch.float32, (d_out,))
+    if base_out.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {base_out.dtype}")
+    if out is None:
+        out = torch.empty_like(base_out)
+    if inner is None:
+        inner = torch.empty_like(base_out)
+    _need(out, "out", dev, base_out.dtype, (T, d_out))
+    _need(inner, "inner", dev, base_out.dtype, (T, d_out))
+    _check(lib.dora_compose_dual(_ptr(base_out), _ptr(lora_out), _ptr(g), float(s), T, d_out,
+                                 _DTYPE_CODE[base_out.dtype], int(bool(delta_only)), _ptr(out), _ptr(inner),
+                                 _stream(dev)),
+           "dora_compose_dual")
+    return out, inner
+
+
+def compose_backward_inner(dy, inner, g, wnorm, s: float, eps: float | None = None, delta_only: bool = False, *,
+                           need_d_base=True, need_d_lora=True, need_d_m=True, d_base=None, d_lora=None, d_m=None,
+                           ws=None):
+    """(d_base, d_lora, d_m) from (dy, inner) with the norm detached; unrequested ones are None."""
+    lib = load()
+    dev = dy.device
+    T, d_out = dy.shape
+    _need(dy, "dy", dev)
+    if dy.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {dy.dtype}")
+    _need(g, "g", dev, torch.float32, (d_out,))
+    if need_d_m:
+        _need(inner, "inner", dev, dy.dtype, (T, d_out))
+        _need(wnorm, "wnorm", dev, torch.float32, (d_out,))
+    eps = default_eps(dy.dtype) if eps is None else float(eps)
+    if need_d_base and d_base is None:
+        d_base = torch.empty_like(dy)
+    if need_d_lora and d_lora is None:
+        d_lora = torch.empty_like(dy)
+    if need_d_m and d_m is None:
+        d_m = torch.empty(d_out, dtype=torch.float32, device=dev)
+    for t, name in ((d_base, "d_base"), (d_lora, "d_lora")):
+        if t is not None:
+            _need(t, name, dev, dy.dtype, (T, d_out))
+    if d_m is not None:
+        _need(d_m, "d_m", dev, torch.float32, (d_out,))
+    if need_d_m and ws is None:
+        ws = workspace(compose_backward_workspace_size(T, d_out), dev)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.dora_compose_backward_inner(_ptr(dy), _ptr(inner) if need_d_m else None, _ptr(g),
+                                           _ptr(wnorm) if need_d_m else None, float(s), eps, T, d_out,
+                                           _DTYPE_CODE[dy.dtype], int(bool(delta_only)),
+                                           _ptr(d_base) if need_d_base else None,
+                                           _ptr(d_lora) if need_d_lora else None,
+                                           _ptr(d_m) if need_d_m else None, _ptr(ws), nbytes, _stream(dev)),
+           "dora_compose_backward_inner")
+    return (d_base if need_d_base else None, d_lora if need_d_lora else None, d_m if need_d_m else None)
+
+
 class DoRACompose(torch.autograd.Function):
     """Autograd wiring of the fused compose: inputs (base_out, lora_out, m) with
     the norm wnorm detached; g = m / max(wnorm, eps) comes from factored_norm.
@@ -248,4 +314,30 @@ class DoRACompose(torch.autograd.Function):
         nb, nl, nm = ctx.need
         d_base, d_lora, d_m = compose_backward(dy.contiguous(), base_out, lora_out, g, wnorm, ctx.s, ctx.eps,
                                                ctx.delta_only, need_d_base=nb, need_d_lora=nl, need_d_m=nm)
+        return d_base, d_lora, d_m, None, None, None, None, None
+
+
+class DoRAComposeInner(torch.autograd.Function):
+    """Training-tier autograd wiring: the forward writes y and inner = base +
+    s*lora in one pass and saves only inner (one activation instead of two);
+    the backward reads (dy, inner).  Same inputs and norm treatment as
+    DoRACompose.
+
+    forward(ctx, base_out, lora_out, m, g, wnorm, s, eps, delta_only)
+    """
+
+    @staticmethod
+    def forward(ctx, base_out, lora_out, m, g, wnorm, s, eps, delta_only=False):
+        y, inner = compose_dual(base_out, lora_out, g, s, delta_only)
+        ctx.save_for_backward(inner, g, wnorm)
+        ctx.s, ctx.eps, ctx.delta_only = float(s), float(eps), bool(delta_only)
+        ctx.need = (ctx.needs_input_grad[0], ctx.needs_input_grad[1], ctx.needs_input_grad[2])
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        inner, g, wnorm = ctx.saved_tensors
+        nb, nl, nm = ctx.need
+        d_base, d_lora, d_m = compose_backward_inner(dy.contiguous(), inner, g, wnorm, ctx.s, ctx.eps,
+                                                     ctx.delta_only, need_d_base=nb, need_d_lora=nl, need_d_m=nm)
         return d_base, d_lora, d_m, None, None, None, None, None

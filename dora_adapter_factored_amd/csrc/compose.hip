@@ -10,6 +10,11 @@
 // the workspace, then one finalize pass.  No atomics, so d_m is bitwise
 // reproducible.
 //
+// Training tier (§4, Tier 1): the dual-output forward also writes
+// inner = base + s * lora (2 reads + 2 writes), and the backward can take
+// (dy, inner) instead of (dy, base, lora): d_m_j = sum_t dy_tj * inner_tj /
+// max(wnorm_j, eps), 2 reads + 2 writes.
+//
 // Both kernels are HBM-bound streams over [T, d_out].  A workgroup owns a
 // strip of 64 sixteen-byte packets along d_out (one wave reads 1 KiB of a
 // row) and 4 row lanes; each thread keeps g for its packet in registers for
@@ -31,10 +36,10 @@ constexpr int kMaxParts = 1024;  // cap on d_m partial rows (grid-strides beyond
 // 16-row token blocks backward), narrow ones with more rows in flight.
 constexpr int kMaxGridY = 65535;
 
-template <typename T, bool DELTA, int kRPT>
-__global__ __launch_bounds__(kThreads) void compose_fwd_vec(const T* base, const T* __restrict__ lora,
+template <typename T, bool DELTA, int kRPT, bool DUAL>
+__global__ __launch_bounds__(kThreads) void compose_fwd_vec(const T* base, const T* lora,
                                                             const float* __restrict__ g, float s,
-                                                            int64_t nrows, int64_t d_out, T* y) {
+                                                            int64_t nrows, int64_t d_out, T* y, T* inner) {
     constexpr int N = Pack<T>::N;
     constexpr int kFwdRowsPerBlock = kTR * kRPT;
     const int tc = threadIdx.x % kTC, tr = threadIdx.x / kTC;
@@ -62,24 +67,26 @@ __global__ __launch_bounds__(kThreads) void compose_fwd_vec(const T* base, const
         for (int i = 0; i < kRPT; ++i) {
             const int64_t row = r0 + (int64_t)i * kTR;
             if (row < nrows) {
-                Pack<T> o;
+                Pack<T> o, in;
 #pragma unroll
                 for (int e = 0; e < N; ++e) {
                     const float bf = Cvt<T>::to_f(b[i].e[e]);
                     const float lf = Cvt<T>::to_f(l[i].e[e]);
                     const float d = fmaf(gm1[e], bf, gs[e] * lf);
                     o.e[e] = Cvt<T>::from_f(DELTA ? d : bf + d);
+                    if (DUAL) in.e[e] = Cvt<T>::from_f(fmaf(s, lf, bf));
                 }
                 store_pack_stream(y + row * d_out + col, o);
+                if (DUAL) store_pack_stream(inner + row * d_out + col, in);
             }
         }
     }
 }
 
-template <typename T, bool DELTA>
-__global__ __launch_bounds__(kThreads) void compose_fwd_scalar(const T* base, const T* __restrict__ lora,
+template <typename T, bool DELTA, bool DUAL>
+__global__ __launch_bounds__(kThreads) void compose_fwd_scalar(const T* base, const T* lora,
                                                                const float* __restrict__ g, float s,
-                                                               int64_t n, int64_t d_out, T* y) {
+                                                               int64_t n, int64_t d_out, T* y, T* inner) {
     for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * kThreads) {
         const float gv = g[i % d_out];
@@ -87,10 +94,12 @@ __global__ __launch_bounds__(kThreads) void compose_fwd_scalar(const T* base, co
         const float lf = Cvt<T>::to_f(lora[i]);
         const float d = fmaf(gv - 1.0f, bf, (gv * s) * lf);
         y[i] = Cvt<T>::from_f(DELTA ? d : bf + d);
+        if (DUAL) inner[i] = Cvt<T>::from_f(fmaf(s, lf, bf));
     }
 }
 
-template <typename T, bool DELTA, bool DM, bool DB, bool DL, int kRPT, int kBwdTokenBlock>
+// With INNER, `base` points at inner = base + s * lora and lora is unused.
+template <typename T, bool DELTA, bool DM, bool DB, bool DL, int kRPT, int kBwdTokenBlock, bool INNER>
 __global__ __launch_bounds__(kThreads) void compose_bwd_vec(const T* dy, const T* __restrict__ base,
                                                             const T* __restrict__ lora,
                                                             const float* __restrict__ g, float s,
@@ -125,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void compose_bwd_vec(const T* dy, const T
                         dv[i] = load_pack_stream(dy + off);
                         if (DM) {
                             bv[i] = load_pack_stream(base + off);
-                            lv[i] = load_pack_stream(lora + off);
+                            if (!INNER) lv[i] = load_pack_stream(lora + off);
                         }
                     }
                 }
@@ -141,8 +150,9 @@ __global__ __launch_bounds__(kThreads) void compose_bwd_vec(const T* dy, const T
                             if (DB) ob.e[e] = Cvt<T>::from_f(gb[e] * df);
                             if (DL) ol.e[e] = Cvt<T>::from_f(gl[e] * df);
                             if (DM) {
-                                const float inner = fmaf(s, Cvt<T>::to_f(lv[i].e[e]),
-                                                         Cvt<T>::to_f(bv[i].e[e]));
+                                const float inner = INNER ? Cvt<T>::to_f(bv[i].e[e])
+                                                          : fmaf(s, Cvt<T>::to_f(lv[i].e[e]),
+                                                                 Cvt<T>::to_f(bv[i].e[e]));
                                 acc[e] = fmaf(df, inner, acc[e]);
                             }
                         }
@@ -171,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void compose_bwd_vec(const T* dy, const T
     }
 }
 
-template <typename T, bool DELTA, bool DM, bool DB, bool DL, int kBwdTokenBlock>
+template <typename T, bool DELTA, bool DM, bool DB, bool DL, int kBwdTokenBlock, bool INNER>
 __global__ __launch_bounds__(kThreads) void compose_bwd_scalar(const T* dy, const T* __restrict__ base,
                                                                const T* __restrict__ lora,
                                                                const float* __restrict__ g, float s,
@@ -187,7 +197,9 @@ __global__ __launch_bounds__(kThreads) void compose_bwd_scalar(const T* dy, cons
         for (int64_t row = rb * kBwdTokenBlock; row < rend; ++row) {
             const int64_t off = row * d_out + col;
             const float df = Cvt<T>::to_f(dy[off]);
-            if (DM) acc = fmaf(df, fmaf(s, Cvt<T>::to_f(lora[off]), Cvt<T>::to_f(base[off])), acc);
+            if (DM)
+                acc = fmaf(df, INNER ? Cvt<T>::to_f(base[off]) : fmaf(s, Cvt<T>::to_f(lora[off]), Cvt<T>::to_f(base[off])),
+                           acc);
             if (DB) d_base[off] = Cvt<T>::from_f(gb * df);
             if (DL) d_lora[off] = Cvt<T>::from_f(gl * df);
         }
@@ -234,45 +246,52 @@ int bwd_parts(int64_t T, int64_t d_out) {
     return (int)(p < kMaxParts ? p : kMaxParts);
 }
 
+template <typename T, bool DELTA, bool DUAL>
+void fwd_launch(bool vec, bool wide, dim3 grid, unsigned sgrid, const T* b, const T* l, const float* g, float s,
+                int64_t nrows, int64_t d_out, T* o, T* in, hipStream_t st) {
+    if (!vec)
+        compose_fwd_scalar<T, DELTA, DUAL><<<sgrid, kThreads, 0, st>>>(b, l, g, s, nrows * d_out, d_out, o, in);
+    else if (wide)
+        compose_fwd_vec<T, DELTA, 2, DUAL><<<grid, kThreads, 0, st>>>(b, l, g, s, nrows, d_out, o, in);
+    else
+        compose_fwd_vec<T, DELTA, 4, DUAL><<<grid, kThreads, 0, st>>>(b, l, g, s, nrows, d_out, o, in);
+}
+
 template <typename T>
 hipError_t fwd_typed(const void* base, const void* lora, const float* g, float s, int64_t nrows,
-                     int64_t d_out, bool delta, void* y, hipStream_t st) {
+                     int64_t d_out, bool delta, void* y, void* inner, hipStream_t st) {
     constexpr int N = Pack<T>::N;
     const T* b = static_cast<const T*>(base);
     const T* l = static_cast<const T*>(lora);
     T* o = static_cast<T*>(y);
-    if (d_out % N == 0 && aligned16(base) && aligned16(lora) && aligned16(y)) {
-        const int64_t nvec = d_out / N;
-        const int64_t gx = (nvec + kTC - 1) / kTC;
-        const bool wide = d_out >= 8192;
+    T* in = static_cast<T*>(inner);
+    const bool dual = inner != nullptr;
+    const bool vec = d_out % N == 0 && aligned16(base) && aligned16(lora) && aligned16(y) && aligned16(inner);
+    const bool wide = d_out >= 8192;
+    dim3 grid(1, 1);
+    unsigned sgrid = 1;
+    if (vec) {
+        const int64_t gx = (d_out / N + kTC - 1) / kTC;
         const int rpb = kTR * (wide ? 2 : 4);
         int64_t gy = (nrows + rpb - 1) / rpb;
         if (gy > kMaxGridY) gy = kMaxGridY;
-        dim3 grid((unsigned)gx, (unsigned)gy);
-        if (wide) {
-            if (delta)
-                compose_fwd_vec<T, true, 2><<<grid, kThreads, 0, st>>>(b, l, g, s, nrows, d_out, o);
-            else
-                compose_fwd_vec<T, false, 2><<<grid, kThreads, 0, st>>>(b, l, g, s, nrows, d_out, o);
-        } else {
-            if (delta)
-                compose_fwd_vec<T, true, 4><<<grid, kThreads, 0, st>>>(b, l, g, s, nrows, d_out, o);
-            else
-                compose_fwd_vec<T, false, 4><<<grid, kThreads, 0, st>>>(b, l, g, s, nrows, d_out, o);
-        }
+        grid = dim3((unsigned)gx, (unsigned)gy);
     } else {
-        const int64_t n = nrows * d_out;
-        int64_t gx = (n + kThreads - 1) / kThreads;
+        int64_t gx = (nrows * d_out + kThreads - 1) / kThreads;
         if (gx > 65536) gx = 65536;
-        if (delta)
-            compose_fwd_scalar<T, true><<<(unsigned)gx, kThreads, 0, st>>>(b, l, g, s, n, d_out, o);
-        else
-            compose_fwd_scalar<T, false><<<(unsigned)gx, kThreads, 0, st>>>(b, l, g, s, n, d_out, o);
+        sgrid = (unsigned)gx;
+    }
+    if (delta) {
+        if (dual) fwd_launch<T, true, true>(vec, wide, grid, sgrid, b, l, g, s, nrows, d_out, o, in, st);
+        else fwd_launch<T, true, false>(vec, wide, grid, sgrid, b, l, g, s, nrows, d_out, o, in, st);
+    } else {
+        if (dual) fwd_launch<T, false, true>(vec, wide, grid, sgrid, b, l, g, s, nrows, d_out, o, in, st);
+        else fwd_launch<T, false, false>(vec, wide, grid, sgrid, b, l, g, s, nrows, d_out, o, in, st);
     }
     return hipGetLastError();
 }
 
-template <typename T, bool DELTA, bool DM, bool DB, bool DL>
+template <typename T, bool DELTA, bool DM, bool DB, bool DL, bool INNER>
 void bwd_launch(bool vec, const T* dy, const T* b, const T* l, const float* g, float s, int64_t nrows,
                 int64_t d_out, T* db, T* dl, float* part, int nparts, hipStream_t st) {
     const bool narrow = bwd_narrow(d_out);
@@ -281,40 +300,41 @@ void bwd_launch(bool vec, const T* dy, const T* b, const T* l, const float* g, f
         const int64_t gx = (d_out / N + kTC - 1) / kTC;
         dim3 grid((unsigned)gx, (unsigned)nparts);
         if (narrow)
-            compose_bwd_vec<T, DELTA, DM, DB, DL, 8, 32><<<grid, kThreads, 0, st>>>(dy, b, l, g, s, nrows, d_out,
-                                                                                   db, dl, part);
+            compose_bwd_vec<T, DELTA, DM, DB, DL, 8, 32, INNER><<<grid, kThreads, 0, st>>>(dy, b, l, g, s, nrows,
+                                                                                          d_out, db, dl, part);
         else
-            compose_bwd_vec<T, DELTA, DM, DB, DL, 4, 16><<<grid, kThreads, 0, st>>>(dy, b, l, g, s, nrows, d_out,
-                                                                                   db, dl, part);
+            compose_bwd_vec<T, DELTA, DM, DB, DL, 4, 16, INNER><<<grid, kThreads, 0, st>>>(dy, b, l, g, s, nrows,
+                                                                                          d_out, db, dl, part);
     } else {
         dim3 grid((unsigned)((d_out + kThreads - 1) / kThreads), (unsigned)nparts);
         if (narrow)
-            compose_bwd_scalar<T, DELTA, DM, DB, DL, 32><<<grid, kThreads, 0, st>>>(dy, b, l, g, s, nrows, d_out,
-                                                                                   db, dl, part);
+            compose_bwd_scalar<T, DELTA, DM, DB, DL, 32, INNER><<<grid, kThreads, 0, st>>>(dy, b, l, g, s, nrows,
+                                                                                          d_out, db, dl, part);
         else
-            compose_bwd_scalar<T, DELTA, DM, DB, DL, 16><<<grid, kThreads, 0, st>>>(dy, b, l, g, s, nrows, d_out,
-                                                                                   db, dl, part);
+            compose_bwd_scalar<T, DELTA, DM, DB, DL, 16, INNER><<<grid, kThreads, 0, st>>>(dy, b, l, g, s, nrows,
+                                                                                          d_out, db, dl, part);
     }
 }
 
-template <typename T, bool DELTA, bool DM>
+template <typename T, bool DELTA, bool DM, bool INNER>
 void bwd_dispatch_outputs(bool vec, const T* dy, const T* b, const T* l, const float* g, float s,
                           int64_t nrows, int64_t d_out, T* db, T* dl, float* part, int nparts,
                           hipStream_t st) {
     if (db && dl)
-        bwd_launch<T, DELTA, DM, true, true>(vec, dy, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
+        bwd_launch<T, DELTA, DM, true, true, INNER>(vec, dy, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
     else if (db)
-        bwd_launch<T, DELTA, DM, true, false>(vec, dy, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
+        bwd_launch<T, DELTA, DM, true, false, INNER>(vec, dy, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
     else if (dl)
-        bwd_launch<T, DELTA, DM, false, true>(vec, dy, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
+        bwd_launch<T, DELTA, DM, false, true, INNER>(vec, dy, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
     else
-        bwd_launch<T, DELTA, DM, false, false>(vec, dy, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
+        bwd_launch<T, DELTA, DM, false, false, INNER>(vec, dy, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
 }
 
+// inner_mode: `base` holds inner = base + s * lora and `lora` is unused.
 template <typename T>
 hipError_t bwd_typed(const void* dy, const void* base, const void* lora, const float* g,
                      const float* wnorm, float s, float eps, int64_t nrows, int64_t d_out, bool delta,
-                     void* d_base, void* d_lora, float* d_m, void* ws, hipStream_t st) {
+                     bool inner_mode, void* d_base, void* d_lora, float* d_m, void* ws, hipStream_t st) {
     constexpr int N = Pack<T>::N;
     const T* dyp = static_cast<const T*>(dy);
     const T* b = static_cast<const T*>(base);
@@ -324,23 +344,30 @@ hipError_t bwd_typed(const void* dy, const void* base, const void* lora, const f
     const bool want_dm = d_m != nullptr;
     if (nrows > 0 && (db || dl || want_dm)) {
         const bool vec = d_out % N == 0 && aligned16(dy) && aligned16(db) && aligned16(dl) &&
-                         (!want_dm || (aligned16(base) && aligned16(lora)));
+                         (!want_dm || (aligned16(base) && (inner_mode || aligned16(lora))));
         float* part = static_cast<float*>(ws);
         if (want_dm) {
             const int nparts = bwd_parts(nrows, d_out);
-            if (delta)
-                bwd_dispatch_outputs<T, true, true>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
-            else
-                bwd_dispatch_outputs<T, false, true>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
+            if (inner_mode) {
+                if (delta)
+                    bwd_dispatch_outputs<T, true, true, true>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
+                else
+                    bwd_dispatch_outputs<T, false, true, true>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
+            } else {
+                if (delta)
+                    bwd_dispatch_outputs<T, true, true, false>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
+                else
+                    bwd_dispatch_outputs<T, false, true, false>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, part, nparts, st);
+            }
         } else {
             // frozen magnitude: only dy is read; the token grid needs no partials
             const int tb = bwd_token_block(d_out);
             int64_t gy = (nrows + tb - 1) / tb;
             const int nblk = (int)(gy < kMaxGridY ? gy : kMaxGridY);
             if (delta)
-                bwd_dispatch_outputs<T, true, false>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, nullptr, nblk, st);
+                bwd_dispatch_outputs<T, true, false, false>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, nullptr, nblk, st);
             else
-                bwd_dispatch_outputs<T, false, false>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, nullptr, nblk, st);
+                bwd_dispatch_outputs<T, false, false, false>(vec, dyp, b, l, g, s, nrows, d_out, db, dl, nullptr, nblk, st);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -362,29 +389,29 @@ size_t compose_bwd_workspace_bytes(int64_t T, int64_t d_out) {
 }
 
 hipError_t launch_compose_fwd(const void* base, const void* lora, const float* g, float s, int64_t T,
-                              int64_t d_out, int dtype, bool delta_only, void* y, hipStream_t stream) {
+                              int64_t d_out, int dtype, bool delta_only, void* y, void* inner, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     switch (dtype) {
-        case kF32: return fwd_typed<float>(base, lora, g, s, T, d_out, delta_only, y, stream);
-        case kBF16: return fwd_typed<bf16_t>(base, lora, g, s, T, d_out, delta_only, y, stream);
-        default: return fwd_typed<f16_t>(base, lora, g, s, T, d_out, delta_only, y, stream);
+        case kF32: return fwd_typed<float>(base, lora, g, s, T, d_out, delta_only, y, inner, stream);
+        case kBF16: return fwd_typed<bf16_t>(base, lora, g, s, T, d_out, delta_only, y, inner, stream);
+        default: return fwd_typed<f16_t>(base, lora, g, s, T, d_out, delta_only, y, inner, stream);
     }
 }
 
 hipError_t launch_compose_bwd(const void* dy, const void* base, const void* lora, const float* g,
                               const float* wnorm, float s, float eps, int64_t T, int64_t d_out,
-                              int dtype, bool delta_only, void* d_base, void* d_lora, float* d_m,
-                              void* workspace, hipStream_t stream) {
+                              int dtype, bool delta_only, bool inner_mode, void* d_base, void* d_lora,
+                              float* d_m, void* workspace, hipStream_t stream) {
     switch (dtype) {
         case kF32:
-            return bwd_typed<float>(dy, base, lora, g, wnorm, s, eps, T, d_out, delta_only, d_base, d_lora,
-                                    d_m, workspace, stream);
+            return bwd_typed<float>(dy, base, lora, g, wnorm, s, eps, T, d_out, delta_only, inner_mode, d_base,
+                                    d_lora, d_m, workspace, stream);
         case kBF16:
-            return bwd_typed<bf16_t>(dy, base, lora, g, wnorm, s, eps, T, d_out, delta_only, d_base, d_lora,
-                                     d_m, workspace, stream);
+            return bwd_typed<bf16_t>(dy, base, lora, g, wnorm, s, eps, T, d_out, delta_only, inner_mode, d_base,
+                                     d_lora, d_m, workspace, stream);
         default:
-            return bwd_typed<f16_t>(dy, base, lora, g, wnorm, s, eps, T, d_out, delta_only, d_base, d_lora,
-                                    d_m, workspace, stream);
+            return bwd_typed<f16_t>(dy, base, lora, g, wnorm, s, eps, T, d_out, delta_only, inner_mode, d_base,
+                                    d_lora, d_m, workspace, stream);
     }
 }
 

@@ -107,9 +107,27 @@ int dora_compose(const void* base_out, const void* lora_out, const float* g, flo
     if (delta_only != 0 && delta_only != 1) return fail(DORA_ERR_INVALID_ARG, "delta_only must be 0 or 1");
     if (!std::isfinite(s)) return fail(DORA_ERR_INVALID_ARG, "s must be finite");
     if (T != 0 && y == lora_out) return fail(DORA_ERR_INVALID_ARG, "y may alias base_out only");
-    hipError_t e = dora::launch_compose_fwd(base_out, lora_out, g, s, T, d_out, dtype, delta_only != 0, y,
+    hipError_t e = dora::launch_compose_fwd(base_out, lora_out, g, s, T, d_out, dtype, delta_only != 0, y, nullptr,
                                             static_cast<hipStream_t>(stream));
     return hip_status(e, "dora_compose launch");
+}
+
+int dora_compose_dual(const void* base_out, const void* lora_out, const float* g, float s, int64_t T,
+                      int64_t d_out, int dtype, int delta_only, void* y, void* inner, void* stream) {
+    if (!g) return fail(DORA_ERR_INVALID_ARG, "g must be non-NULL");
+    if (T != 0 && (!base_out || !lora_out || !y || !inner))
+        return fail(DORA_ERR_INVALID_ARG, "base_out, lora_out, y and inner must be non-NULL when T > 0");
+    if (!dim_ok(d_out, 1) || T < 0 || T >= ((int64_t)1 << 40))
+        return fail(DORA_ERR_INVALID_ARG, "sizes must satisfy 1 <= d_out < 2^31, 0 <= T < 2^40 (got T=%lld, d_out=%lld)",
+                    (long long)T, (long long)d_out);
+    if (!dtype_ok(dtype)) return fail(DORA_ERR_INVALID_ARG, "unknown dtype code %d", dtype);
+    if (delta_only != 0 && delta_only != 1) return fail(DORA_ERR_INVALID_ARG, "delta_only must be 0 or 1");
+    if (!std::isfinite(s)) return fail(DORA_ERR_INVALID_ARG, "s must be finite");
+    if (T != 0 && (y == lora_out || inner == base_out || y == inner))
+        return fail(DORA_ERR_INVALID_ARG, "y may alias base_out only and inner lora_out only");
+    hipError_t e = dora::launch_compose_fwd(base_out, lora_out, g, s, T, d_out, dtype, delta_only != 0, y, inner,
+                                            static_cast<hipStream_t>(stream));
+    return hip_status(e, "dora_compose_dual launch");
 }
 
 int dora_compose_backward_workspace_size(int64_t T, int64_t d_out, size_t* bytes) {
@@ -148,9 +166,42 @@ int dora_compose_backward(const void* dy, const void* base_out, const void* lora
         }
     }
     hipError_t e = dora::launch_compose_bwd(dy, base_out, lora_out, g, wnorm, s, eps, T, d_out, dtype,
-                                            delta_only != 0, d_base, d_lora, d_m, workspace,
+                                            delta_only != 0, false, d_base, d_lora, d_m, workspace,
                                             static_cast<hipStream_t>(stream));
     return hip_status(e, "dora_compose_backward launch");
+}
+
+int dora_compose_backward_inner(const void* dy, const void* inner, const float* g, const float* wnorm, float s,
+                                float eps, int64_t T, int64_t d_out, int dtype, int delta_only, void* d_base,
+                                void* d_lora, float* d_m, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!g) return fail(DORA_ERR_INVALID_ARG, "g must be non-NULL");
+    if (T != 0 && !dy) return fail(DORA_ERR_INVALID_ARG, "dy must be non-NULL when T > 0");
+    if (d_m && !wnorm) return fail(DORA_ERR_INVALID_ARG, "wnorm must be non-NULL when d_m is requested");
+    if (d_m && T != 0 && !inner)
+        return fail(DORA_ERR_INVALID_ARG, "inner must be non-NULL when d_m is requested and T > 0");
+    if (!dim_ok(d_out, 1) || T < 0 || T >= ((int64_t)1 << 40))
+        return fail(DORA_ERR_INVALID_ARG, "sizes must satisfy 1 <= d_out < 2^31, 0 <= T < 2^40 (got T=%lld, d_out=%lld)",
+                    (long long)T, (long long)d_out);
+    if (!dtype_ok(dtype)) return fail(DORA_ERR_INVALID_ARG, "unknown dtype code %d", dtype);
+    if (delta_only != 0 && delta_only != 1) return fail(DORA_ERR_INVALID_ARG, "delta_only must be 0 or 1");
+    if (!std::isfinite(s)) return fail(DORA_ERR_INVALID_ARG, "s must be finite");
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(DORA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (T != 0 && d_base && d_lora && d_base == d_lora)
+        return fail(DORA_ERR_INVALID_ARG, "d_base and d_lora must differ");
+    if (T != 0 && d_m && (d_base == inner || d_lora == inner))
+        return fail(DORA_ERR_INVALID_ARG, "d_base and d_lora must not alias inner");
+    if (d_m) {
+        const size_t need = dora::compose_bwd_workspace_bytes(T, d_out);
+        if (need > 0) {
+            if (!workspace) return fail(DORA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+            if (workspace_bytes < need)
+                return fail(DORA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+            if (!aligned256(workspace)) return fail(DORA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        }
+    }
+    hipError_t e = dora::launch_compose_bwd(dy, inner, nullptr, g, wnorm, s, eps, T, d_out, dtype, delta_only != 0,
+                                            true, d_base, d_lora, d_m, workspace, static_cast<hipStream_t>(stream));
+    return hip_status(e, "dora_compose_backward_inner launch");
 }
 
 }  // extern "C"

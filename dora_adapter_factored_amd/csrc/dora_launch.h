@@ -49,13 +49,15 @@ hipError_t launch_norm(const NormPlan& p, const void* W0, const void* A, const v
 
 size_t compose_bwd_workspace_bytes(int64_t T, int64_t d_out);
 
+// inner may be nullptr; when set, inner = base + s * lora is written too.
 hipError_t launch_compose_fwd(const void* base, const void* lora, const float* g, float s,
                               int64_t T, int64_t d_out, int dtype, bool delta_only, void* y,
-                              hipStream_t stream);
+                              void* inner, hipStream_t stream);
 
+// inner_mode: `base` holds inner = base + s * lora and `lora` is unused.
 hipError_t launch_compose_bwd(const void* dy, const void* base, const void* lora,
                               const float* g, const float* wnorm, float s, float eps,
-                              int64_t T, int64_t d_out, int dtype, bool delta_only,
+                              int64_t T, int64_t d_out, int dtype, bool delta_only, bool inner_mode,
                               void* d_base, void* d_lora, float* d_m, void* workspace,
                               hipStream_t stream);
 

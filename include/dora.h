@@ -115,7 +115,29 @@ int dora_factored_norm(const void* W0, const void* A, const void* B, const float
 int dora_compose(const void* base_out, const void* lora_out, const float* g, float s,
                  int64_t T, int64_t d_out, int dtype, int delta_only, void* y, void* stream);
 
-/* Workspace bytes needed by dora_compose_backward when d_m != NULL. */
+/*
+ * Dual-output compose forward of the training tier, one pass: 2 reads + 2
+ * writes per element.
+ *
+ * [ScalingDoRA] §4 (Tier 1: the layer output and the inner term come from one
+ * kernel, so the backward needs no second forward pass):
+ *   y      exactly as dora_compose (delta_only selects y or the delta)
+ *   inner  = base + s*lora, in fp32, rounded once (round-to-nearest-even)
+ * inner is the only activation dora_compose_backward_inner needs besides dy.
+ *
+ *   base_out, lora_out  device [T, d_out], dtype; lora_out excludes s.
+ *   g                   device fp32 [d_out].
+ *   y, inner            device [T, d_out], dtype, outputs; y may alias base_out
+ *                       and inner may alias lora_out exactly (in-place); y and
+ *                       inner must differ; no partial overlaps.
+ * T == 0 is a no-op; the activation pointers may then be NULL.
+ */
+int dora_compose_dual(const void* base_out, const void* lora_out, const float* g, float s,
+                      int64_t T, int64_t d_out, int dtype, int delta_only, void* y, void* inner,
+                      void* stream);
+
+/* Workspace bytes needed by dora_compose_backward and
+ * dora_compose_backward_inner when d_m != NULL. */
 int dora_compose_backward_workspace_size(int64_t T, int64_t d_out, size_t* bytes);
 
 /*
@@ -148,6 +170,36 @@ int dora_compose_backward(const void* dy, const void* base_out, const void* lora
                           const float* g, const float* wnorm, float s, float eps, int64_t T,
                           int64_t d_out, int dtype, int delta_only, void* d_base, void* d_lora,
                           float* d_m, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Compose backward of the training tier from (dy, inner): 2 reads + 2 writes
+ * per element instead of 3 + 2.
+ *
+ * [ScalingDoRA] §4 (Tier 1) and §3 (backward kernel; magnitude gradient as a
+ * separate deterministic reduction), norm detached:
+ *   d_base = g*dy          (delta_only: (g - 1)*dy)
+ *   d_lora = (g*s)*dy
+ *   d_m_j  = sum_t dy_tj*inner_tj / max(wnorm_j, eps)
+ * with inner = base + s*lora as written by dora_compose_dual.  d_m is summed
+ * in a fixed order, so results are bitwise reproducible.
+ *
+ *   dy                  device [T, d_out], dtype.
+ *   inner               device [T, d_out], dtype; read only when d_m != NULL
+ *                       (may be NULL otherwise).
+ *   g, wnorm            as dora_compose_backward.
+ *   d_base, d_lora      device [T, d_out], dtype, outputs, each may be NULL;
+ *                       either may alias dy exactly, neither may alias inner.
+ *   d_m                 device fp32 [d_out], output (overwritten), or NULL
+ *                       when the magnitude is frozen.
+ *   workspace           needed only when d_m != NULL: at least
+ *                       dora_compose_backward_workspace_size() bytes,
+ *                       256-byte aligned, no initialisation needed.
+ * T == 0 writes zeros to d_m and nothing else.
+ */
+int dora_compose_backward_inner(const void* dy, const void* inner, const float* g,
+                                const float* wnorm, float s, float eps, int64_t T, int64_t d_out,
+                                int dtype, int delta_only, void* d_base, void* d_lora, float* d_m,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

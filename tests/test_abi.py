@@ -145,6 +145,59 @@ def test_compose_backward_validation(lib):
     assert _bwd(lib, ws=ctypes.c_void_p(0x100004)) == E.DORA_ERR_WORKSPACE
 
 
+def _dual(lib, **kw):
+    a = dict(base=FAKE, lora=ctypes.c_void_p(0x20000), g=FAKE, s=1.0, T=4, d_out=8, dtype=1, delta=0,
+             y=ctypes.c_void_p(0x30000), inner=ctypes.c_void_p(0x60000), stream=None)
+    a.update(kw)
+    return lib.dora_compose_dual(a["base"], a["lora"], a["g"], a["s"], a["T"], a["d_out"], a["dtype"], a["delta"],
+                                 a["y"], a["inner"], a["stream"])
+
+
+def test_compose_dual_validation(lib):
+    E = Bn
+    assert _dual(lib, base=None) == E.DORA_ERR_INVALID_ARG
+    assert _dual(lib, lora=None) == E.DORA_ERR_INVALID_ARG
+    assert _dual(lib, g=None) == E.DORA_ERR_INVALID_ARG
+    assert _dual(lib, y=None) == E.DORA_ERR_INVALID_ARG
+    assert _dual(lib, inner=None) == E.DORA_ERR_INVALID_ARG
+    assert _dual(lib, T=-1) == E.DORA_ERR_INVALID_ARG
+    assert _dual(lib, d_out=0) == E.DORA_ERR_INVALID_ARG
+    assert _dual(lib, dtype=3) == E.DORA_ERR_INVALID_ARG
+    assert _dual(lib, delta=2) == E.DORA_ERR_INVALID_ARG
+    assert _dual(lib, s=float("nan")) == E.DORA_ERR_INVALID_ARG
+    assert _dual(lib, y=ctypes.c_void_p(0x20000)) == E.DORA_ERR_INVALID_ARG       # y aliases lora_out
+    assert _dual(lib, inner=FAKE) == E.DORA_ERR_INVALID_ARG                       # inner aliases base_out
+    assert _dual(lib, inner=ctypes.c_void_p(0x30000)) == E.DORA_ERR_INVALID_ARG   # y == inner
+    assert _dual(lib, T=0, base=None, lora=None, y=None, inner=None) == E.DORA_OK
+
+
+def _bwd_inner(lib, **kw):
+    a = dict(dy=FAKE, inner=ctypes.c_void_p(0x70000), g=FAKE, wnorm=FAKE, s=1.0, eps=1e-6, T=64, d_out=8,
+             dtype=1, delta=0, db=ctypes.c_void_p(0x40000), dl=ctypes.c_void_p(0x50000), dm=FAKE, ws=FAKE_WS,
+             nbytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.dora_compose_backward_inner(a["dy"], a["inner"], a["g"], a["wnorm"], a["s"], a["eps"], a["T"],
+                                           a["d_out"], a["dtype"], a["delta"], a["db"], a["dl"], a["dm"], a["ws"],
+                                           a["nbytes"], a["stream"])
+
+
+def test_compose_backward_inner_validation(lib):
+    E = Bn
+    assert _bwd_inner(lib, dy=None) == E.DORA_ERR_INVALID_ARG
+    assert _bwd_inner(lib, g=None) == E.DORA_ERR_INVALID_ARG
+    assert _bwd_inner(lib, inner=None) == E.DORA_ERR_INVALID_ARG       # d_m requested
+    assert _bwd_inner(lib, wnorm=None) == E.DORA_ERR_INVALID_ARG
+    assert _bwd_inner(lib, T=-5) == E.DORA_ERR_INVALID_ARG
+    assert _bwd_inner(lib, dtype=9) == E.DORA_ERR_INVALID_ARG
+    assert _bwd_inner(lib, delta=3) == E.DORA_ERR_INVALID_ARG
+    assert _bwd_inner(lib, eps=float("nan")) == E.DORA_ERR_INVALID_ARG
+    assert _bwd_inner(lib, dl=ctypes.c_void_p(0x40000)) == E.DORA_ERR_INVALID_ARG   # d_base == d_lora
+    assert _bwd_inner(lib, db=ctypes.c_void_p(0x70000)) == E.DORA_ERR_INVALID_ARG   # d_base aliases inner
+    assert _bwd_inner(lib, ws=None) == E.DORA_ERR_WORKSPACE
+    assert _bwd_inner(lib, nbytes=8) == E.DORA_ERR_WORKSPACE
+    assert _bwd_inner(lib, ws=ctypes.c_void_p(0x100008)) == E.DORA_ERR_WORKSPACE
+
+
 def test_binding_rejects_bad_tensors_before_the_library():
     # host tensors are refused by the shape/device checks of the binding
     cpu = torch.zeros(4, 8, dtype=torch.bfloat16)
