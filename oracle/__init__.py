@@ -15,4 +15,5 @@ from .dora_oracle import (  # noqa: F401
     compose_backward_inner,
     dora_linear_forward,
     merged_weight,
+    merge_with_scale,
 )

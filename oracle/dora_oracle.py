@@ -209,3 +209,17 @@ def merged_weight(W0, A, B, m, s, eps) -> np.ndarray:
     Vp = adapted_weight_rows(W0, A, B, s)
     n = np.sqrt(np.sum(Vp * Vp, axis=1))
     return (as_f64(m) / np.maximum(n, float(eps)))[:, None] * Vp
+
+
+def merge_with_scale(W0, A, B, g, s, rows=None) -> np.ndarray:
+    """The merge step given the scale: W_merged = diag(g) (W0 + sBA).
+
+    With g = m / max(||W0 + sBA||_row, eps) this is merged_weight ([LoRA&DoRA]
+    §6; [ScalingDoRA] §4 computes g once from the factored norm, so a merge
+    for serving reuses it).  Restricted to `rows` when given (g is then
+    indexed by the same rows).
+    """
+    g = as_f64(g)
+    if rows is not None:
+        g = g[np.asarray(rows, dtype=np.int64)]
+    return g[:, None] * adapted_weight_rows(W0, A, B, s, rows=rows)

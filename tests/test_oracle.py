@@ -49,6 +49,8 @@ def test_arrow_example():
     np.testing.assert_allclose(g, c["g"], rtol=0, atol=1e-15)
     Wm = oracle.merged_weight(c["W0"], c["A"], c["B"], c["m"], c["s"], c["eps"])
     np.testing.assert_allclose(Wm, c["merged"], rtol=0, atol=1e-15)
+    Ws = oracle.merge_with_scale(c["W0"], c["A"], c["B"], c["g"], c["s"])
+    np.testing.assert_allclose(Ws, c["merged"], rtol=0, atol=1e-15)
     assert abs(np.linalg.norm(Wm[0]) - 2.0) < 1e-15  # length set by m
 
 
@@ -373,3 +375,25 @@ def test_pins_catch_planted_norm_mistakes(mutant):
         if not np.allclose(mutant(W0, A, B, 1.3), ref, rtol=1e-10):
             caught = True
     assert caught
+
+
+def test_merge_with_scale():
+    rng = np.random.default_rng(12)
+    d_out, d_in, r, s, eps = 20, 14, 4, 1.75, 1e-12
+    W0, A, B = rand_layer(rng, d_out, d_in, r, b_std=0.6)
+    m = rng.uniform(0.2, 2.0, d_out)
+    # with the scale the norm produces, the merge is the pinned merged weight
+    g = oracle.magnitude_scale(m, oracle.dense_row_norm(W0, A, B, s), eps)
+    Ws = oracle.merge_with_scale(W0, A, B, g, s)
+    np.testing.assert_allclose(Ws, oracle.merged_weight(W0, A, B, m, s, eps), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(np.linalg.norm(Ws, axis=1), m, rtol=1e-13)
+    # g = 1 and s = 0 reduce to the plain sum and to a row rescale of W0
+    np.testing.assert_array_equal(oracle.merge_with_scale(W0, A, B, np.ones(d_out), 0.0), W0)
+    np.testing.assert_allclose(oracle.merge_with_scale(W0, A, B, g, 0.0), g[:, None] * W0, rtol=1e-15)
+    # brute force, element by element, on one row subset
+    rows = [3, 0, 17]
+    sub = oracle.merge_with_scale(W0, A, B, g, s, rows=rows)
+    for a_, i in enumerate(rows):
+        for j in range(d_in):
+            v = W0[i, j] + s * sum(B[i, k] * A[k, j] for k in range(r))
+            assert abs(sub[a_, j] - g[i] * v) <= 1e-14 * max(1.0, abs(g[i] * v))
