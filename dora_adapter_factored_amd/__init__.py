@@ -19,5 +19,7 @@ from .binding import (  # noqa: F401
     factored_norm,
     library_path,
     load,
+    merge,
+    merge_workspace_size,
     norm_workspace_size,
 )

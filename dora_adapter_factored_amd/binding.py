@@ -35,6 +35,8 @@ _SIGNATURES = {
     "dora_compose_backward_workspace_size": (ctypes.c_int, [_i64, _i64, ctypes.POINTER(_sz)]),
     "dora_compose_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _f32, _i64, _i64, ctypes.c_int,
                                              ctypes.c_int, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "dora_merge_workspace_size": (ctypes.c_int, [_i64, _i64, ctypes.c_int, ctypes.POINTER(_sz)]),
+    "dora_merge": (ctypes.c_int, [_vp, _vp, _vp, _vp, _f32, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _sz, _vp]),
     "dora_compose_dual": (ctypes.c_int, [_vp, _vp, _vp, _f32, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp,
                                          _vp]),
     "dora_compose_backward_inner": (ctypes.c_int, [_vp, _vp, _vp, _vp, _f32, _f32, _i64, _i64, ctypes.c_int,
@@ -137,6 +139,13 @@ def compose_backward_workspace_size(T: int, d_out: int) -> int:
     return n.value
 
 
+def merge_workspace_size(d_in: int, r: int, dtype: torch.dtype) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().dora_merge_workspace_size(d_in, r, _DTYPE_CODE[dtype], ctypes.byref(n)),
+           "dora_merge_workspace_size")
+    return n.value
+
+
 # ------------------------------------------------------------ entry points
 def factored_norm(W0, A, B, s: float, m=None, eps: float | None = None, *, wnorm=None, g=None, ws=None):
     """wnorm = ||W0_i + s (BA)_i|| (factored, never forming BA) and g = m / max(wnorm, eps).
@@ -170,6 +179,33 @@ def factored_norm(W0, A, B, s: float, m=None, eps: float | None = None, *, wnorm
                                   float(s), eps, _ptr(wnorm), _ptr(g), _ptr(ws), nbytes, _stream(dev)),
            "dora_factored_norm")
     return wnorm, (g if m is not None else None)
+
+
+def merge(W0, A, B, g, s: float, *, out=None, ws=None):
+    """W = diag(g) (W0 + s B A), the adapter folded into one weight for serving.
+
+    g is fp32 [d_out] (the g of factored_norm).  out=W0 merges in place.
+    """
+    lib = load()
+    dev = W0.device
+    d_out, d_in = W0.shape
+    r = A.shape[0]
+    _need(W0, "W0", dev)
+    _need(A, "A", dev, W0.dtype, (r, d_in))
+    _need(B, "B", dev, W0.dtype, (d_out, r))
+    _need(g, "g", dev, torch.float32, (d_out,))
+    if W0.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {W0.dtype}")
+    if out is None:
+        out = torch.empty_like(W0)
+    _need(out, "out", dev, W0.dtype, (d_out, d_in))
+    if ws is None:
+        ws = workspace(merge_workspace_size(d_in, r, W0.dtype), dev)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.dora_merge(_ptr(W0), _ptr(A), _ptr(B), _ptr(g), float(s), d_out, d_in, r, _DTYPE_CODE[W0.dtype],
+                          _ptr(out), _ptr(ws), nbytes, _stream(dev)),
+           "dora_merge")
+    return out
 
 
 def compose(base_out, lora_out, g, s: float, delta_only: bool = False, *, out=None):

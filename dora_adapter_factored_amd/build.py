@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libdora_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ("dora_capi.hip", "compose.hip", "norm.hip")
+SOURCES = ("dora_capi.hip", "compose.hip", "norm.hip", "merge.hip")
 ARCH = "gfx950"
 
 # Packed-fp32 VALU ops are kept out of the device code.  MFMA results are

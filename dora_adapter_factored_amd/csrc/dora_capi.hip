@@ -38,6 +38,9 @@ bool dim_ok(int64_t v, int64_t lo) { return v >= lo && v < kMaxDim; }
 bool dtype_ok(int dt) { return dt == DORA_F32 || dt == DORA_BF16 || dt == DORA_F16; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255) == 0; }
 
+// the transpose of A runs one grid row per 64 values of r
+constexpr int64_t kMaxMergeRank = (int64_t)65535 * 64 - 64;
+
 }  // namespace
 
 extern "C" {
@@ -202,6 +205,39 @@ int dora_compose_backward_inner(const void* dy, const void* inner, const float* 
     hipError_t e = dora::launch_compose_bwd(dy, inner, nullptr, g, wnorm, s, eps, T, d_out, dtype, delta_only != 0,
                                             true, d_base, d_lora, d_m, workspace, static_cast<hipStream_t>(stream));
     return hip_status(e, "dora_compose_backward_inner launch");
+}
+
+int dora_merge_workspace_size(int64_t d_in, int64_t r, int dtype, size_t* bytes) {
+    if (!bytes) return fail(DORA_ERR_INVALID_ARG, "bytes is NULL");
+    if (!dim_ok(d_in, 1) || !dim_ok(r, 1) || r > kMaxMergeRank)
+        return fail(DORA_ERR_INVALID_ARG, "sizes must satisfy 1 <= d_in < 2^31, 1 <= r <= %lld",
+                    (long long)kMaxMergeRank);
+    if (!dtype_ok(dtype)) return fail(DORA_ERR_INVALID_ARG, "unknown dtype code %d", dtype);
+    if (dtype == DORA_F16) return fail(DORA_ERR_UNSUPPORTED, "merge supports bf16 and fp32 weights");
+    *bytes = dora::merge_workspace_bytes(d_in, r, dtype);
+    return ok();
+}
+
+int dora_merge(const void* W0, const void* A, const void* B, const float* g, float s, int64_t d_out, int64_t d_in,
+               int64_t r, int dtype, void* W, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!W0 || !A || !B || !g || !W) return fail(DORA_ERR_INVALID_ARG, "W0, A, B, g and W must be non-NULL");
+    if (!dim_ok(d_out, 1) || !dim_ok(d_in, 1) || !dim_ok(r, 1) || r > kMaxMergeRank)
+        return fail(DORA_ERR_INVALID_ARG, "sizes must satisfy 1 <= d_out, d_in < 2^31, 1 <= r <= %lld (got %lld, %lld, %lld)",
+                    (long long)kMaxMergeRank, (long long)d_out, (long long)d_in, (long long)r);
+    if (((d_out + 127) / 128) * ((d_in + 127) / 128) >= ((int64_t)1 << 30))
+        return fail(DORA_ERR_INVALID_ARG, "d_out x d_in too large (%lld x %lld)", (long long)d_out, (long long)d_in);
+    if (!dtype_ok(dtype)) return fail(DORA_ERR_INVALID_ARG, "unknown dtype code %d", dtype);
+    if (dtype == DORA_F16) return fail(DORA_ERR_UNSUPPORTED, "merge supports bf16 and fp32 weights");
+    if (!std::isfinite(s)) return fail(DORA_ERR_INVALID_ARG, "s must be finite");
+    if (W == A || W == B || W == static_cast<const void*>(g) || W == workspace)
+        return fail(DORA_ERR_INVALID_ARG, "W may alias W0 only");
+    const size_t need = dora::merge_workspace_bytes(d_in, r, dtype);
+    if (!workspace) return fail(DORA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need) return fail(DORA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if (!aligned256(workspace)) return fail(DORA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    hipError_t e = dora::launch_merge(W0, A, B, g, s, d_out, d_in, r, dtype, W, workspace,
+                                      static_cast<hipStream_t>(stream));
+    return hip_status(e, "dora_merge launch");
 }
 
 }  // extern "C"

@@ -61,4 +61,13 @@ hipError_t launch_compose_bwd(const void* dy, const void* base, const void* lora
                               void* d_base, void* d_lora, float* d_m, void* workspace,
                               hipStream_t stream);
 
+// -------------------------------------------------------------------- merge
+
+size_t merge_workspace_bytes(int64_t d_in, int64_t r, int dtype);
+
+// W = diag(g) (W0 + s B A); W may alias W0.
+hipError_t launch_merge(const void* W0, const void* A, const void* B, const float* g, float s,
+                        int64_t d_out, int64_t d_in, int64_t r, int dtype, void* W, void* workspace,
+                        hipStream_t stream);
+
 }  // namespace dora

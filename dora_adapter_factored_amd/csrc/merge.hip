@@ -1,0 +1,322 @@
+// DoRA merge for serving on gfx950: W_merged = diag(g) (W0 + s B A).
+//
+// "LoRA & DoRA: The Math, Memory, and Trade-offs" §6 gives the merged DoRA
+// weight m (W0 + sBA) / ||W0 + sBA||_row, an ordinary matrix with no adapter
+// left at inference; "Scaling DoRA" §4 computes g = m / max(wnorm, eps) once
+// from the factored norm, so the merge takes g as an input and never forms a
+// norm of its own.
+//
+// Mapping onto the chip.  B A is a dense contraction over K = r, so it runs on
+// MFMA; the rest (read W0, scale, write W) is a stream over d_out x d_in that
+// bounds the call.  Both MFMA operands must hold K contiguously per lane: B
+// does ([d_out][r] row-major), A does not ([r][d_in]), so transpose_a first
+// writes A^T into the workspace as [d_in][r_pad], zero-padded to whole 64-byte
+// k-tiles (the tail k-tile then needs no masking on that side).
+//
+// merge_tile: one workgroup per 128 x 128 output tile, 4 waves (2 x 2), each a
+// 64 x 64 block of 32 x 32 MFMA tiles with fp32 accumulators.  k-tiles of 64
+// bytes per row (32 bf16 or 16 fp32) of both operands are staged through LDS
+// (register-prefetched double buffer, swizzled rows).  The W0 tile is loaded
+// into registers at the start so its HBM latency hides under the MFMA loop;
+// the epilogue passes the accumulators through an fp32 LDS tile so that each
+// thread finishes whole 16-byte chunks: W = g_i * fmaf(s, acc, W0), rounded
+// once.  W may alias W0 exactly: every element is read and written by the
+// same thread of the same workgroup.
+#include "dora_device.h"
+#include "dora_launch.h"
+
+namespace dora {
+namespace {
+
+constexpr int kNumXCD = 8;
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------ transpose A
+constexpr int kTrTile = 64;
+
+template <typename E>
+__global__ __launch_bounds__(256) void transpose_a(const E* __restrict__ A, int64_t r, int64_t d_in,
+                                                   E* __restrict__ At, int64_t r_pad) {
+    __shared__ E tile[kTrTile][kTrTile + 2];
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const int64_t n0 = (int64_t)blockIdx.x * kTrTile, k0 = (int64_t)blockIdx.y * kTrTile;
+#pragma unroll
+    for (int i = 0; i < kTrTile / 4; ++i) {
+        const int64_t k = k0 + ty + 4 * i, n = n0 + tx;
+        tile[ty + 4 * i][tx] = (k < r && n < d_in) ? A[k * d_in + n] : Cvt<E>::from_f(0.0f);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kTrTile / 4; ++i) {
+        const int64_t n = n0 + ty + 4 * i, k = k0 + tx;
+        if (n < d_in && k < r_pad) At[n * r_pad + k] = tile[tx][ty + 4 * i];
+    }
+}
+
+// ------------------------------------------------------------- MFMA traits
+// A k-tile holds 64 bytes of K per row.  In each of its two MFMA k-steps a
+// lane supplies the 16-byte chunk 2*step + lane/32 of its row, for both
+// operands, so every product pairs matching K.
+template <typename E> struct MergeMma;
+
+template <> struct MergeMma<bf16_t> {
+    static constexpr int KT = 32;
+    __device__ __forceinline__ static void mma(f32x16_t& c, u32x4_t a, u32x4_t b) {
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+};
+
+template <> struct MergeMma<float> {
+    static constexpr int KT = 16;
+    // four K=2 products: element i of the chunk, lanes < 32 and >= 32 hold
+    // two different chunks, so each K value enters exactly once
+    __device__ __forceinline__ static void mma(f32x16_t& c, u32x4_t a, u32x4_t b) {
+        const f32x4_t av = __builtin_bit_cast(f32x4_t, a), bv = __builtin_bit_cast(f32x4_t, b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[i], c, 0, 0, 0);
+    }
+};
+
+// 64-byte LDS rows of 4 chunks: XOR swizzle of the chunk index that keeps the
+// MFMA fragment reads (32 rows, one chunk each per half-wave) and the
+// row-major tile writes free of bank conflicts.
+__device__ __forceinline__ int swz64(int row) { return ((row >> 2) & 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 1); }
+
+constexpr int kBM = 128, kBN = 128, kNTh = 256;
+constexpr int kRowB = 64;                                // bytes per LDS row per k-tile
+constexpr int kStageB = (kBM + kBN) * kRowB;             // 16 KB
+constexpr int kEpiPitch = kBN + 8;                       // floats per LDS row of the epilogue tile
+constexpr int kEpiB = kBM * kEpiPitch * 4;               // 69,632 B
+constexpr int kLdsB = kEpiB > 2 * kStageB ? kEpiB : 2 * kStageB;
+
+struct MergeArgs {
+    const void* W0;
+    const void* At;
+    const void* B;
+    const float* g;
+    void* W;
+    float s;
+    int64_t d_out, d_in, r, r_pad;
+    int n_mt, n_nt;   // output tiles along d_out and d_in
+    int per_xcd;      // tiles per XCD slice (grid = 8 * per_xcd)
+};
+
+// workgroup -> output tile: consecutive workgroups go to consecutive XCDs;
+// each XCD takes one contiguous slice of the tile list, which runs through
+// panels of 8 row-tiles column by column, so the workgroups resident on one
+// XCD share a few row-tiles of B and column-tiles of A^T in its L2.
+__device__ __forceinline__ bool merge_tile_of(const MergeArgs& a, int& mt, int& nt) {
+    const int id = blockIdx.x;
+    const int t = (id % kNumXCD) * a.per_xcd + id / kNumXCD;
+    if (t >= a.n_mt * a.n_nt) return false;
+    constexpr int PM = 8;
+    const int panel = t / (PM * a.n_nt);
+    const int u = t - panel * PM * a.n_nt;
+    const int pm = min(PM, a.n_mt - panel * PM);
+    mt = panel * PM + u % pm;
+    nt = u / pm;
+    return true;
+}
+
+template <typename E, bool ALIGNED>
+__device__ __forceinline__ u32x4_t load_b_chunk(const E* B, int64_t row, int64_t k, const MergeArgs& a) {
+    constexpr int VEC = 16 / sizeof(E);
+    if (ALIGNED) {
+        if (row < a.d_out && k < a.r) return *reinterpret_cast<const u32x4_t*>(B + row * a.r + k);
+        return u32x4_t{0u, 0u, 0u, 0u};
+    } else {
+        Pack<E> v;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            v.e[e] = (row < a.d_out && k + e < a.r) ? B[row * a.r + k + e] : Cvt<E>::from_f(0.0f);
+        return v.u;
+    }
+}
+
+template <typename E, bool ALIGNED>
+__global__ __launch_bounds__(kNTh, 2) void merge_tile(MergeArgs a) {
+    int mt, nt;
+    if (!merge_tile_of(a, mt, nt)) return;
+    constexpr int VEC = 16 / sizeof(E);
+    constexpr int KT = MergeMma<E>::KT;
+    constexpr int CPR = kBN / VEC;                       // 16-byte chunks per output row
+    constexpr int NOUT = kBM * CPR / kNTh;               // output chunks per thread
+    __shared__ __attribute__((aligned(16))) char lds[kLdsB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)mt * kBM, n0 = (int64_t)nt * kBN;
+    const E* W0 = static_cast<const E*>(a.W0);
+    const E* B = static_cast<const E*>(a.B);
+    const E* At = static_cast<const E*>(a.At);
+
+    // W0 tile into registers now; consumed by the epilogue
+    u32x4_t w0v[NOUT];
+#pragma unroll
+    for (int i = 0; i < NOUT; ++i) {
+        const int c = tid + kNTh * i, row = c / CPR, cc = c % CPR;
+        const int64_t gm = m0 + row, gn = n0 + (int64_t)cc * VEC;
+        if (ALIGNED) {
+            w0v[i] = (gm < a.d_out && gn < a.d_in)
+                         ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(W0 + gm * a.d_in + gn))
+                         : u32x4_t{0u, 0u, 0u, 0u};
+        } else {
+            Pack<E> v;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                v.e[e] = (gm < a.d_out && gn + e < a.d_in) ? W0[gm * a.d_in + gn + e] : Cvt<E>::from_f(0.0f);
+            w0v[i] = v.u;
+        }
+    }
+
+    // k-tile staging: 2 chunks of B rows and 2 of A^T rows per thread
+    const int nk = (int)(a.r_pad / KT);
+    u32x4_t lreg[2], rreg[2];
+    auto load_tile = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = tid + kNTh * i, row = c >> 2, q = c & 3;
+            const int64_t k = (int64_t)kt * KT + q * VEC;
+            lreg[i] = load_b_chunk<E, ALIGNED>(B, m0 + row, k, a);
+            const int64_t gn = n0 + row;
+            rreg[i] = gn < a.d_in ? *reinterpret_cast<const u32x4_t*>(At + gn * a.r_pad + k)
+                                  : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store_tile = [&](int buf) {
+        char* st = lds + buf * kStageB;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = tid + kNTh * i, row = c >> 2, q = c & 3;
+            *reinterpret_cast<u32x4_t*>(st + row * kRowB + ((q ^ swz64(row)) << 4)) = lreg[i];
+            *reinterpret_cast<u32x4_t*>(st + (kBM + row) * kRowB + ((q ^ swz64(row)) << 4)) = rreg[i];
+        }
+    };
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    load_tile(0);
+    store_tile(0);
+    if (nk > 1) load_tile(1);
+    __syncthreads();
+    const int fr = lane & 31, fh = lane >> 5;
+    for (int kt = 0; kt < nk; ++kt) {
+        const char* st = lds + (kt & 1) * kStageB;
+#pragma unroll
+        for (int step = 0; step < 2; ++step) {
+            const int q = 2 * step + fh;
+            u32x4_t av[2], bv[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = wm * 64 + i * 32 + fr;
+                av[i] = *reinterpret_cast<const u32x4_t*>(st + row * kRowB + ((q ^ swz64(row)) << 4));
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int row = wn * 64 + j * 32 + fr;
+                bv[j] = *reinterpret_cast<const u32x4_t*>(st + (kBM + row) * kRowB + ((q ^ swz64(row)) << 4));
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) MergeMma<E>::mma(acc[i][j], av[i], bv[j]);
+        }
+        if (kt + 1 < nk) store_tile((kt + 1) & 1);
+        if (kt + 2 < nk) load_tile(kt + 2);
+        __syncthreads();
+    }
+
+    // epilogue: accumulators -> fp32 LDS tile -> whole 16-byte output chunks
+    float* epi = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = wm * 64 + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+                const int col = wn * 64 + j * 32 + fr;
+                epi[row * kEpiPitch + col] = acc[i][j][e];
+            }
+    __syncthreads();
+    E* W = static_cast<E*>(a.W);
+    const float s = a.s;
+#pragma unroll
+    for (int i = 0; i < NOUT; ++i) {
+        const int c = tid + kNTh * i, row = c / CPR, cc = c % CPR;
+        const int64_t gm = m0 + row, gn = n0 + (int64_t)cc * VEC;
+        if (gm >= a.d_out || gn >= a.d_in) continue;
+        const float gi = a.g[gm];
+        const float* src = epi + row * kEpiPitch + cc * VEC;
+        Pack<E> w, o;
+        w.u = w0v[i];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o.e[e] = Cvt<E>::from_f(gi * fmaf(s, src[e], Cvt<E>::to_f(w.e[e])));
+        if (ALIGNED) {
+            __builtin_nontemporal_store(o.u, reinterpret_cast<u32x4_t*>(W + gm * a.d_in + gn));
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                if (gn + e < a.d_in) W[gm * a.d_in + gn + e] = o.e[e];
+        }
+    }
+}
+
+template <typename E>
+hipError_t merge_typed(const void* W0, const void* A, const void* B, const float* g, float s, int64_t d_out,
+                       int64_t d_in, int64_t r, void* W, void* workspace, hipStream_t st) {
+    constexpr int KT = MergeMma<E>::KT;
+    const int64_t r_pad = (r + KT - 1) / KT * KT;
+    E* At = static_cast<E*>(workspace);
+    const dim3 tgrid((unsigned)((d_in + kTrTile - 1) / kTrTile), (unsigned)((r_pad + kTrTile - 1) / kTrTile));
+    transpose_a<E><<<tgrid, 256, 0, st>>>(static_cast<const E*>(A), r, d_in, At, r_pad);
+
+    MergeArgs a;
+    a.W0 = W0;
+    a.At = At;
+    a.B = B;
+    a.g = g;
+    a.W = W;
+    a.s = s;
+    a.d_out = d_out;
+    a.d_in = d_in;
+    a.r = r;
+    a.r_pad = r_pad;
+    a.n_mt = (int)((d_out + kBM - 1) / kBM);
+    a.n_nt = (int)((d_in + kBN - 1) / kBN);
+    const int64_t tiles = (int64_t)a.n_mt * a.n_nt;
+    a.per_xcd = (int)((tiles + kNumXCD - 1) / kNumXCD);
+    const unsigned grid = (unsigned)(a.per_xcd * kNumXCD);
+    constexpr int VEC = 16 / sizeof(E);
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    const bool aligned = d_in % VEC == 0 && r % VEC == 0 && al16(W0) && al16(B) && al16(W);
+    if (aligned)
+        merge_tile<E, true><<<grid, kNTh, 0, st>>>(a);
+    else
+        merge_tile<E, false><<<grid, kNTh, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t merge_workspace_bytes(int64_t d_in, int64_t r, int dtype) {
+    const int64_t kt = dtype == kF32 ? MergeMma<float>::KT : MergeMma<bf16_t>::KT;
+    const int64_t r_pad = (r + kt - 1) / kt * kt;
+    return align_up((size_t)d_in * (size_t)r_pad * dtype_size(dtype), 256);
+}
+
+hipError_t launch_merge(const void* W0, const void* A, const void* B, const float* g, float s, int64_t d_out,
+                        int64_t d_in, int64_t r, int dtype, void* W, void* workspace, hipStream_t stream) {
+    if (dtype == kF32) return merge_typed<float>(W0, A, B, g, s, d_out, d_in, r, W, workspace, stream);
+    return merge_typed<bf16_t>(W0, A, B, g, s, d_out, d_in, r, W, workspace, stream);
+}
+
+}  // namespace dora

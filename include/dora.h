@@ -201,6 +201,37 @@ int dora_compose_backward_inner(const void* dy, const void* inner, const float* 
                                 int dtype, int delta_only, void* d_base, void* d_lora, float* d_m,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Workspace bytes needed by dora_merge (host call, launches nothing).
+ */
+int dora_merge_workspace_size(int64_t d_in, int64_t r, int dtype, size_t* bytes);
+
+/*
+ * DoRA merge for serving: one weight with the adapter folded in.
+ *
+ * [LoRA&DoRA] §6 (merged DoRA weight m (W0 + sBA) / ||W0 + sBA||_row, an
+ * ordinary matrix at inference) with the scale g = m / max(wnorm, eps) that
+ * dora_factored_norm returns ([ScalingDoRA] §4):
+ *   W_ij = g_i * (W0_ij + s * sum_k B_ik A_kj)
+ * The product B A is accumulated in fp32 (MFMA), W0 + s*(BA) is one fused
+ * multiply-add in fp32, the product with g is fp32, and the result is
+ * rounded once (round-to-nearest-even) to dtype.
+ *
+ *   W0, A, B  device, dtype DORA_BF16 or DORA_F32 (DORA_F16 returns
+ *             DORA_ERR_UNSUPPORTED), layouts above.
+ *   g         device fp32 [d_out] (the g output of dora_factored_norm).
+ *   s         LoRA scale (alpha / r).
+ *   r         at most 4,194,176.
+ *   W         device [d_out, d_in], dtype, output; may alias W0 exactly (an
+ *             in-place merge), must not overlap A, B, g or the workspace.
+ *   workspace device scratch of at least dora_merge_workspace_size() bytes,
+ *             256-byte aligned; it receives A transposed, no initialisation
+ *             needed.
+ */
+int dora_merge(const void* W0, const void* A, const void* B, const float* g, float s, int64_t d_out,
+               int64_t d_in, int64_t r, int dtype, void* W, void* workspace, size_t workspace_bytes,
+               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

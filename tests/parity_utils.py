@@ -53,3 +53,32 @@ def sample_rows(n, k, seed=0):
     fixed |= {min(n - 1, b) for b in range(127, n, 128 * 7)}
     extra = rng.choice(n, size=min(n, k), replace=False)
     return np.array(sorted(fixed | set(extra.tolist())), dtype=np.int64)
+
+
+def check_merge(got, W0, A, B, g, s, dtype, rows=None, what="W"):
+    """Merged weight against the oracle with an error bound derived from the
+    kernel's arithmetic.  With u = 2^-24:
+      - B A accumulated in fp32 over r products (in any order, rounding to
+        nearest or toward zero): |err| <= 2 gamma_r sum_k |B_ik||A_kj|,
+        gamma_r = r u / (1 - r u), times |g s|;
+      - fmaf(s, acc, W0) and the product with g: |ref| 4u;
+      - the final rounding to dtype: |ref| 2^-8 (bf16: 8-bit significand) or
+        u (fp32).
+    """
+    if rows is not None:
+        idx = torch.as_tensor(np.asarray(rows, dtype=np.int64))
+        W0, B, g = W0[idx], B[idx], g[idx]
+    W0, A, B, g = (oracle.as_f64(x) for x in (W0, A, B, g))
+    got = np.asarray(got, np.float64)
+    ref = oracle.merge_with_scale(W0, A, B, g, s)
+    r = A.shape[0]
+    u = 2.0 ** -24
+    gamma = r * u / (1 - r * u)
+    u_out = 2.0 ** -8 if dtype == torch.bfloat16 else u
+    bound = (u_out + 4 * u) * np.abs(ref) + 2 * gamma * np.abs(g * s)[:, None] * (np.abs(B) @ np.abs(A))
+    err = np.abs(got - ref)
+    bad = ~(err <= bound)
+    if bad.any():
+        i = int(np.argmax(err - bound))
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} out of bound; worst at {i}: "
+                             f"got {got.flat[i]!r} ref {ref.flat[i]!r} bound {bound.flat[i]!r}")

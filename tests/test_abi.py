@@ -198,6 +198,49 @@ def test_compose_backward_inner_validation(lib):
     assert _bwd_inner(lib, ws=ctypes.c_void_p(0x100008)) == E.DORA_ERR_WORKSPACE
 
 
+def test_merge_workspace_size(lib):
+    n = ctypes.c_size_t()
+    # A transposed, r padded to whole 64-byte k-tiles
+    assert lib.dora_merge_workspace_size(8192, 384, 1, ctypes.byref(n)) == 0 and n.value == 8192 * 384 * 2
+    assert lib.dora_merge_workspace_size(1000, 40, 1, ctypes.byref(n)) == 0 and n.value == 1000 * 64 * 2
+    assert lib.dora_merge_workspace_size(3, 5, 1, ctypes.byref(n)) == 0 and n.value == 256   # 192 B, rounded up
+    assert lib.dora_merge_workspace_size(100, 40, 0, ctypes.byref(n)) == 0 and n.value == 100 * 48 * 4
+    assert lib.dora_merge_workspace_size(100, 40, 2, ctypes.byref(n)) == Bn.DORA_ERR_UNSUPPORTED
+    assert lib.dora_merge_workspace_size(0, 40, 1, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
+    assert lib.dora_merge_workspace_size(10, 1 << 23, 1, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
+    assert lib.dora_merge_workspace_size(10, 4, 1, None) == Bn.DORA_ERR_INVALID_ARG
+
+
+def _merge(lib, **kw):
+    a = dict(W0=FAKE, A=ctypes.c_void_p(0x20000), B=ctypes.c_void_p(0x30000), g=ctypes.c_void_p(0x40000), s=1.0,
+             d_out=64, d_in=48, r=8, dtype=1, W=ctypes.c_void_p(0x50000), ws=FAKE_WS, nbytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.dora_merge(a["W0"], a["A"], a["B"], a["g"], a["s"], a["d_out"], a["d_in"], a["r"], a["dtype"],
+                          a["W"], a["ws"], a["nbytes"], a["stream"])
+
+
+def test_merge_validation(lib):
+    E = Bn
+    for k in ("W0", "A", "B", "g", "W"):
+        assert _merge(lib, **{k: None}) == E.DORA_ERR_INVALID_ARG, k
+    assert _merge(lib, d_out=0) == E.DORA_ERR_INVALID_ARG
+    assert _merge(lib, d_in=-1) == E.DORA_ERR_INVALID_ARG
+    assert _merge(lib, r=0) == E.DORA_ERR_INVALID_ARG
+    assert _merge(lib, r=1 << 23) == E.DORA_ERR_INVALID_ARG
+    assert _merge(lib, d_out=1 << 30, d_in=1 << 30) == E.DORA_ERR_INVALID_ARG   # tile count
+    assert _merge(lib, dtype=4) == E.DORA_ERR_INVALID_ARG
+    assert _merge(lib, dtype=2) == E.DORA_ERR_UNSUPPORTED
+    assert _merge(lib, s=float("nan")) == E.DORA_ERR_INVALID_ARG
+    assert _merge(lib, W=ctypes.c_void_p(0x20000)) == E.DORA_ERR_INVALID_ARG    # W aliases A
+    assert _merge(lib, W=ctypes.c_void_p(0x30000)) == E.DORA_ERR_INVALID_ARG    # W aliases B
+    assert _merge(lib, W=ctypes.c_void_p(0x40000)) == E.DORA_ERR_INVALID_ARG    # W aliases g
+    assert _merge(lib, W=FAKE_WS) == E.DORA_ERR_INVALID_ARG                     # W is the workspace
+    assert _merge(lib, ws=None) == E.DORA_ERR_WORKSPACE
+    assert _merge(lib, nbytes=100) == E.DORA_ERR_WORKSPACE
+    assert _merge(lib, ws=ctypes.c_void_p(0x100040)) == E.DORA_ERR_WORKSPACE
+    assert b"256-byte" in lib.dora_last_error_detail()
+
+
 def test_binding_rejects_bad_tensors_before_the_library():
     # host tensors are refused by the shape/device checks of the binding
     cpu = torch.zeros(4, 8, dtype=torch.bfloat16)
