@@ -68,6 +68,11 @@ def compose_bwd_inner_bytes(T, d_out, esz):
     return 4 * T * d_out * esz + 3 * d_out * 4
 
 
+def merge_bytes(d_out, d_in, r, esz):
+    # W0 read and W written once; A, B read once; g read
+    return (2 * d_out * d_in + r * (d_in + d_out)) * esz + d_out * 4
+
+
 COPY_CALIB_BYTES = 256 << 20
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 NORM_SOURCES = ("dora_adapter_factored_amd/csrc/norm.hip", "dora_adapter_factored_amd/csrc/dora_launch.h",
@@ -218,6 +223,8 @@ def main():
                          db=torch.empty_like(layer.base_out),
                          dl=torch.empty_like(layer.base_out), dm=torch.empty(d_out, device=dev)))
     ws_norm = torch.empty(D.norm_workspace_size(d_out, d_in, r, dt), dtype=torch.uint8, device=dev)
+    ws_merge = torch.empty(D.merge_workspace_size(d_in, r, dt), dtype=torch.uint8, device=dev)
+    w_merged = [torch.empty_like(layer.W0) for _ in range(min(nsets, 2))]
     ws_bwd = torch.empty(max(1, D.compose_backward_workspace_size(T, d_out)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -237,6 +244,12 @@ def main():
     def run_bwd_inner(st):
         D.compose_backward_inner(st["dy"], st["inner"], st["g"], st["wn"], s, eps,
                                  d_base=st["db"], d_lora=st["dl"], d_m=st["dm"], ws=ws_bwd)
+
+    merge_i = [0]
+
+    def run_merge(st):
+        merge_i[0] += 1
+        D.merge(st["W0"], st["A"], st["B"], st["g"], s, out=w_merged[merge_i[0] % len(w_merged)], ws=ws_merge)
 
     def step(st):
         run_norm(st)
@@ -293,6 +306,9 @@ def main():
     # the training tier (one saved activation): measured beside the step
     t_dual = per_call(run_dual)
     t_bwdi = per_call(run_bwd_inner)
+    # the merge for serving: measured beside the step
+    t_merge = per_call(run_merge)
+    mb = merge_bytes(d_out, d_in, r, esz)
     db_, bib = compose_dual_bytes(T, d_out, esz), compose_bwd_inner_bytes(T, d_out, esz)
     F = norm_flops(d_out, d_in, r)
     nb = norm_bytes(d_out, d_in, r, esz)
@@ -332,6 +348,9 @@ def main():
         "compose_bwd_inner": {"ms": round(t_bwdi * 1e3, 4), "GBps": round(bib / t_bwdi / 1e9, 1),
                               "frac_hbm_peak": round(bib / t_bwdi / 1e9 / PEAK_HBM_GBS, 4),
                               "algorithmic_bytes": bib},
+        "merge": {"ms": round(t_merge * 1e3, 4), "GBps": round(mb / t_merge / 1e9, 1),
+                  "frac_hbm_peak": round(mb / t_merge / 1e9 / PEAK_HBM_GBS, 4), "algorithmic_bytes": mb,
+                  "TFLOPs": round(2 * d_out * d_in * r / t_merge / 1e12, 1)},
         "copy_calibration": calib,
         "roofline": {"kernel": "dora_factored_norm (Gram partials, Gram finalize, W0 pass, norm finalize)",
                      "bound": "mfma", "achieved": round(norm_tflops, 2), "peak": peak_mm, "unit": "TFLOP/s",

@@ -23,14 +23,13 @@
 // once.  W may alias W0 exactly: every element is read and written by the
 // same thread of the same workgroup.
 #include "dora_device.h"
+#include "dora_gfx950.h"
 #include "dora_launch.h"
 
 namespace dora {
 namespace {
 
 constexpr int kNumXCD = 8;
-
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // ------------------------------------------------------------ transpose A
 constexpr int kTrTile = 64;
@@ -51,6 +50,37 @@ __global__ __launch_bounds__(256) void transpose_a(const E* __restrict__ A, int6
     for (int i = 0; i < kTrTile / 4; ++i) {
         const int64_t n = n0 + ty + 4 * i, k = k0 + tx;
         if (n < d_in && k < r_pad) At[n * r_pad + k] = tile[tx][ty + 4 * i];
+    }
+}
+
+// 16-byte form (d_in a multiple of the vector width, A 16-byte aligned): each
+// thread loads whole 16-byte runs of a row of A, scatters them into an LDS
+// tile held n-major, and stores whole 16-byte runs of a row of A^T.
+template <typename E>
+__global__ __launch_bounds__(256) void transpose_a_vec(const E* __restrict__ A, int64_t r, int64_t d_in,
+                                                       E* __restrict__ At, int64_t r_pad) {
+    constexpr int VEC = 16 / sizeof(E);
+    constexpr int CPR = kTrTile / VEC;          // 16-byte runs per tile row
+    constexpr int PITCH = kTrTile + VEC;        // elements per LDS row (16-byte aligned rows)
+    __shared__ __attribute__((aligned(16))) E tile[kTrTile][PITCH];   // [n][k]
+    const int tid = threadIdx.x;
+    const int64_t n0 = (int64_t)blockIdx.x * kTrTile, k0 = (int64_t)blockIdx.y * kTrTile;
+#pragma unroll
+    for (int i = 0; i < kTrTile * CPR / 256; ++i) {
+        const int c = tid + 256 * i, kr = c / CPR, cc = c % CPR;
+        const int64_t k = k0 + kr, n = n0 + (int64_t)cc * VEC;
+        Pack<E> v;
+        v.u = (k < r && n < d_in) ? *reinterpret_cast<const u32x4_t*>(A + k * d_in + n) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) tile[cc * VEC + e][kr] = v.e[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kTrTile * CPR / 256; ++i) {
+        const int c = tid + 256 * i, nr = c / CPR, kc = c % CPR;
+        const int64_t n = n0 + nr, k = k0 + (int64_t)kc * VEC;
+        if (n < d_in && k < r_pad)
+            *reinterpret_cast<u32x4_t*>(At + n * r_pad + k) = *reinterpret_cast<const u32x4_t*>(&tile[nr][kc * VEC]);
     }
 }
 
@@ -78,11 +108,6 @@ template <> struct MergeMma<float> {
         for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[i], c, 0, 0, 0);
     }
 };
-
-// 64-byte LDS rows of 4 chunks: XOR swizzle of the chunk index that keeps the
-// MFMA fragment reads (32 rows, one chunk each per half-wave) and the
-// row-major tile writes free of bank conflicts.
-__device__ __forceinline__ int swz64(int row) { return ((row >> 2) & 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 1); }
 
 constexpr int kBM = 128, kBN = 128, kNTh = 256;
 constexpr int kRowB = 64;                                // bytes per LDS row per k-tile
@@ -270,14 +295,232 @@ __global__ __launch_bounds__(kNTh, 2) void merge_tile(MergeArgs a) {
     }
 }
 
+// ------------------------------------------------- LDS-DMA form (aligned)
+// The k-tiles of both operands move global -> LDS by DMA through a ring of
+// kRing stages; lane l of a DMA instruction moves slot l % 4 of row l / 4 of
+// a 16-row group (1 KiB).  Each wave issues kDmaPerWave instructions per
+// stage.  The W0 tile is loaded into registers right after the last real
+// stage is issued: vector-memory loads retire in issue order, so earlier
+// waits would otherwise also wait for W0; issued last, its HBM latency hides
+// under the remaining k-tiles, and the waits below let it stay in flight.
+constexpr int kRing = 3;
+constexpr int kDmaPerWave = (kBM + kBN) / 16 / (kNTh / 64);
+constexpr int kEpiRows = 64;                              // epilogue in two 64-row halves
+static_assert(kRing * kStageB >= kEpiRows * kEpiPitch * 4, "epilogue half fits in the ring");
+
+struct DmaOp {
+    uint32_t base_lo, base_hi;   // first row of the workgroup's tile
+    int bytes;                   // from there to the operand's end (clamped to 31 bits)
+    int ld_bytes, kmax_bytes;
+};
+
+__device__ __forceinline__ DmaOp make_dma_op(const void* p, int64_t ld_bytes, int64_t rows, int64_t row0,
+                                             int64_t kmax_bytes) {
+    DmaOp d;
+    const uint64_t base = reinterpret_cast<uint64_t>(static_cast<const char*>(p) + row0 * ld_bytes);
+    int64_t bytes = (rows - row0) * ld_bytes;
+    if (bytes < 0) bytes = 0;
+    if (bytes > 0x7ffffff0) bytes = 0x7ffffff0;
+    d.base_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    d.base_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
+    d.bytes = __builtin_amdgcn_readfirstlane((int)bytes);
+    d.ld_bytes = __builtin_amdgcn_readfirstlane((int)ld_bytes);
+    d.kmax_bytes = __builtin_amdgcn_readfirstlane((int)kmax_bytes);
+    return d;
+}
+
+// DMA of 16-row group `grp` of k-tile kt into LDS at dst.  lane_off is the
+// lane's byte offset inside the group ((l / 4) rows and the chunk its slot
+// holds, chunk_b); the group and k-tile offsets move the scalar base, and the
+// record count shrinks with it, so rows past the operand read zeros.  Chunks
+// past K (kmax) read zeros.  Offsets fit 31 bits: a tile spans 128 rows.
+__device__ __forceinline__ void dma_group(const DmaOp& d, int grp, int kt, int lane_off, int chunk_b, char* dst) {
+    const int k0b = kt * kRowB;
+    const int voff = chunk_b < d.kmax_bytes - k0b ? lane_off : kOutOfRange;
+    const int off = grp * 16 * d.ld_bytes + k0b;
+    const int left = d.bytes > off ? d.bytes - off : 0;
+    const uint64_t addr = (((uint64_t)d.base_hi << 32) | d.base_lo) + (uint32_t)off;
+    i32x4_t rs;
+    rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+    rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32));
+    rs[2] = __builtin_amdgcn_readfirstlane(left);
+    rs[3] = kRsrcWord3;
+    raw_buffer_load_lds(rs, (lds_void_t*)(dst + grp * 1024), 16, voff, 0, 0, 0);
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are
+// complete, then s_barrier.  Unlike __syncthreads it does not wait for
+// outstanding global loads and stores.  The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Wait until a stage has landed while `after` later stages (and, if w0, the
+// NW0 W0 loads) may stay in flight.  Both are wave-uniform run-time values;
+// each combination gets its own immediate.
+template <int NW0, int A>
+__device__ __forceinline__ void wait_stage(int after, bool w0) {
+    if constexpr (A < 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (after == A) {
+            if (w0)
+                wait_vmcnt<A * kDmaPerWave + NW0>();
+            else
+                wait_vmcnt<A * kDmaPerWave>();
+            return;
+        }
+        wait_stage<NW0, A - 1>(after, w0);
+    }
+}
+
+template <typename E>
+__global__ __launch_bounds__(kNTh, sizeof(E) == 2 ? 3 : 2) void merge_tile_dma(MergeArgs a) {
+    int mt, nt;
+    if (!merge_tile_of(a, mt, nt)) return;
+    constexpr int VEC = 16 / sizeof(E);
+    constexpr int CPR = kBN / VEC;
+    constexpr int NH = kEpiRows * CPR / kNTh;           // output chunks per thread per half
+    constexpr int NW0 = 2 * NH;                         // W0 chunks per thread
+    constexpr int NLD = 2 * NW0;                        // loads issued with them: W0 chunk and g of its row
+    __shared__ __attribute__((aligned(1024))) char lds[kRing * kStageB];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)mt * kBM, n0 = (int64_t)nt * kBN;
+    const int esz = (int)sizeof(E);
+    const DmaOp lop = make_dma_op(a.B, a.r * esz, a.d_out, m0, a.r * esz);
+    const DmaOp rop = make_dma_op(a.At, a.r_pad * esz, a.d_in, n0, a.r_pad * esz);
+    const int grow = lane >> 2, slot = lane & 3;
+    const int chunk_b = (slot ^ swz64(grow)) * 16;
+    const int loff = grow * lop.ld_bytes + chunk_b, roff = grow * rop.ld_bytes + chunk_b;
+    const int nk = (int)(a.r_pad / MergeMma<E>::KT);
+
+    auto issue = [&](int kt) {
+        char* st = lds + (kt % kRing) * kStageB;
+#pragma unroll
+        for (int q = 0; q < kDmaPerWave / 2; ++q) {
+            const int grp = wave + q * (kNTh / 64);
+            dma_group(lop, grp, kt, loff, chunk_b, st);
+            dma_group(rop, grp, kt, roff, chunk_b, st + kBM * kRowB);
+        }
+    };
+    const E* W0 = static_cast<const E*>(a.W0);
+    // W0 chunks and the g of their rows, loaded unconditionally (addresses
+    // clamped into the tensors) so that every wave issues the same count
+    u32x4_t w0v[NW0];
+    float gv[NW0];
+    auto issue_w0 = [&]() {
+#pragma unroll
+        for (int i = 0; i < NW0; ++i) {
+            const int h = i / NH, c = tid + kNTh * (i % NH);
+            const int64_t gm = min(m0 + h * kEpiRows + c / CPR, a.d_out - 1);
+            const int64_t gn = min(n0 + (int64_t)(c % CPR) * VEC, a.d_in - VEC);
+            w0v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(W0 + gm * a.d_in + gn));
+            gv[i] = a.g[gm];
+        }
+    };
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    for (int t = 0; t < kRing - 1; ++t)
+        if (t < nk) issue(t);
+    // W0 goes out in iteration kt_w0, right after the last real stage
+    const int kt_w0 = max(0, nk - kRing);
+    const int fr = lane & 31, fh = lane >> 5;
+    for (int kt = 0; kt < nk; ++kt) {
+        // stage kt has landed once only the stages issued after it (and the
+        // W0 loads, if issued) are outstanding
+        const int after = min(nk, kt + kRing - 1) - kt - 1;
+        wait_stage<NLD, kRing - 2>(after, kt > kt_w0);
+        lds_barrier();
+        if (kt + kRing - 1 < nk) issue(kt + kRing - 1);
+        if (kt == kt_w0) issue_w0();
+        const char* st = lds + (kt % kRing) * kStageB;
+#pragma unroll
+        for (int step = 0; step < 2; ++step) {
+            const int q = 2 * step + fh;
+            u32x4_t av[2], bv[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = wm * 64 + i * 32 + fr;
+                av[i] = *reinterpret_cast<const u32x4_t*>(st + row * kRowB + ((q ^ swz64(row)) << 4));
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int row = wn * 64 + j * 32 + fr;
+                bv[j] = *reinterpret_cast<const u32x4_t*>(st + (kBM + row) * kRowB + ((q ^ swz64(row)) << 4));
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) MergeMma<E>::mma(acc[i][j], av[i], bv[j]);
+        }
+    }
+    lds_barrier();   // every wave is done with the ring
+
+    // epilogue, one 64-row half at a time: accumulators -> fp32 LDS tile ->
+    // whole 16-byte chunks of W
+    float* epi = reinterpret_cast<float*>(lds);
+    E* W = static_cast<E*>(a.W);
+    const float s = a.s;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (wm == h) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int row = i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+                        const int col = wn * 64 + j * 32 + fr;
+                        epi[row * kEpiPitch + col] = acc[i][j][e];
+                    }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+            const int c = tid + kNTh * i, row = c / CPR, cc = c % CPR;
+            const int64_t gm = m0 + h * kEpiRows + row, gn = n0 + (int64_t)cc * VEC;
+            if (gm < a.d_out && gn < a.d_in) {
+                const float gi = gv[h * NH + i];
+                const float* src = epi + row * kEpiPitch + cc * VEC;
+                Pack<E> w, o;
+                w.u = w0v[h * NH + i];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) o.e[e] = Cvt<E>::from_f(gi * fmaf(s, src[e], Cvt<E>::to_f(w.e[e])));
+                __builtin_nontemporal_store(o.u, reinterpret_cast<u32x4_t*>(W + gm * a.d_in + gn));
+            }
+        }
+        lds_barrier();
+    }
+}
+
 template <typename E>
 hipError_t merge_typed(const void* W0, const void* A, const void* B, const float* g, float s, int64_t d_out,
                        int64_t d_in, int64_t r, void* W, void* workspace, hipStream_t st) {
     constexpr int KT = MergeMma<E>::KT;
     const int64_t r_pad = (r + KT - 1) / KT * KT;
     E* At = static_cast<E*>(workspace);
+    constexpr int VEC = 16 / sizeof(E);
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
     const dim3 tgrid((unsigned)((d_in + kTrTile - 1) / kTrTile), (unsigned)((r_pad + kTrTile - 1) / kTrTile));
-    transpose_a<E><<<tgrid, 256, 0, st>>>(static_cast<const E*>(A), r, d_in, At, r_pad);
+    if (d_in % VEC == 0 && al16(A))
+        transpose_a_vec<E><<<tgrid, 256, 0, st>>>(static_cast<const E*>(A), r, d_in, At, r_pad);
+    else
+        transpose_a<E><<<tgrid, 256, 0, st>>>(static_cast<const E*>(A), r, d_in, At, r_pad);
 
     MergeArgs a;
     a.W0 = W0;
@@ -295,11 +538,9 @@ hipError_t merge_typed(const void* W0, const void* A, const void* B, const float
     const int64_t tiles = (int64_t)a.n_mt * a.n_nt;
     a.per_xcd = (int)((tiles + kNumXCD - 1) / kNumXCD);
     const unsigned grid = (unsigned)(a.per_xcd * kNumXCD);
-    constexpr int VEC = 16 / sizeof(E);
-    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
     const bool aligned = d_in % VEC == 0 && r % VEC == 0 && al16(W0) && al16(B) && al16(W);
     if (aligned)
-        merge_tile<E, true><<<grid, kNTh, 0, st>>>(a);
+        merge_tile_dma<E><<<grid, kNTh, 0, st>>>(a);
     else
         merge_tile<E, false><<<grid, kNTh, 0, st>>>(a);
     return hipGetLastError();

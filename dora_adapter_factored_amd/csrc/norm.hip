@@ -22,6 +22,7 @@
 //      takes the square root and divides m.
 // Every reduction has a fixed order, so results are bitwise reproducible.
 #include "dora_device.h"
+#include "dora_gfx950.h"
 #include "dora_launch.h"
 
 namespace dora {
@@ -289,16 +290,6 @@ __device__ __forceinline__ void mainloop_staged(const Contraction& c, int64_t m0
     }
 }
 
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Buffer load of 4 dwords per lane straight into LDS (M0-based destination,
-// lane l writes 16 bytes at dst + 16 l).  An offset at or beyond the buffer's
-// size reads zeros.
-__device__ void raw_buffer_load_lds(i32x4_t rsrc, lds_void_t* lds, int size, int voffset, int soffset,
-                                    int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
-
-constexpr int kOutOfRange = (int)0x80000000;
 
 // Chunk swizzle of the DMA layout: logical chunk c of tile row i sits in
 // physical slot c ^ swz(i).  Any 8 consecutive rows, and the even (odd) rows
@@ -307,13 +298,6 @@ constexpr int kOutOfRange = (int)0x80000000;
 // a DMA group of 8 rows the swizzle depends only on the group's parity.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-// s_waitcnt on vector-memory operations only (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 // One operand of one phase as the DMA sees it: a buffer starting at the
 // workgroup's first tile row, sized to the rows that exist, so rows past the
@@ -999,7 +983,6 @@ __global__ __launch_bounds__(WM * WN * 64) void w0_pass(W0PassArgs a) {
 // every SIMD and cover each other's LDS and memory waits.  Tiles are 32
 // elements of K (64-byte rows): W0 (then B) runs in an LDS ring of LS = 4
 // stages, A (then Gs) in RS = 3 stages, all moved by LDS DMA.
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 template <int V>
 struct IntC {
@@ -1030,13 +1013,6 @@ struct Big {
     static_assert(MT == WN, "each wave sums the base term of one 32-row block");
 };
 
-// Chunk swizzle of 64-byte rows: logical chunk c of row i sits in slot
-// c ^ swz64(i).  For a fixed chunk, the 16 rows of any aligned 16-row block
-// map to 16 distinct (row mod 4, slot) pairs and the even (odd) rows of any
-// aligned 8 rows to 4 distinct slots, so 16-lane (64-bank) and 8-lane
-// (32-bank) phases of a fragment read are conflict-free.  It depends only on
-// the row modulo 16, the height of one DMA group.
-__device__ __forceinline__ int swz64(int row) { return ((row >> 2) & 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 1); }
 
 // One operand as the 64-byte-row DMA sees it; lane l moves slot l % 4 of row
 // l / 4 of a 16-row group (1 KiB per instruction).  The row and K offsets of
