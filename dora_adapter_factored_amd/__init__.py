@@ -17,9 +17,11 @@ from .binding import (  # noqa: F401
     compose_backward_workspace_size,
     default_eps,
     factored_norm,
+    factored_norm_group,
     library_path,
     load,
     merge,
     merge_workspace_size,
+    norm_group_workspace_size,
     norm_workspace_size,
 )

@@ -24,6 +24,14 @@ _lib_lock = threading.Lock()
 
 # C entry points and their signatures, as declared in include/dora.h.
 _i64, _f32, _vp, _sz = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+class NormMember(ctypes.Structure):
+    """DoraNormMember of include/dora.h."""
+    _fields_ = [("W0", ctypes.c_void_p), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("m", ctypes.c_void_p),
+                ("wnorm", ctypes.c_void_p), ("g", ctypes.c_void_p), ("d_out", ctypes.c_int64), ("s", ctypes.c_float)]
+
+
+MAX_NORM_GROUP = 8
+
 _SIGNATURES = {
     "dora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "dora_last_error_detail": (ctypes.c_char_p, []),
@@ -35,6 +43,10 @@ _SIGNATURES = {
     "dora_compose_backward_workspace_size": (ctypes.c_int, [_i64, _i64, ctypes.POINTER(_sz)]),
     "dora_compose_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _f32, _i64, _i64, ctypes.c_int,
                                              ctypes.c_int, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "dora_factored_norm_group_workspace_size": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(_i64), _i64, _i64,
+                                                               ctypes.c_int, ctypes.POINTER(_sz)]),
+    "dora_factored_norm_group": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(NormMember), _i64, _i64, ctypes.c_int,
+                                                _f32, _vp, _sz, _vp]),
     "dora_merge_workspace_size": (ctypes.c_int, [_i64, _i64, ctypes.c_int, ctypes.POINTER(_sz)]),
     "dora_merge": (ctypes.c_int, [_vp, _vp, _vp, _vp, _f32, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _sz, _vp]),
     "dora_compose_dual": (ctypes.c_int, [_vp, _vp, _vp, _f32, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp,
@@ -139,6 +151,15 @@ def compose_backward_workspace_size(T: int, d_out: int) -> int:
     return n.value
 
 
+def norm_group_workspace_size(d_outs, d_in: int, r: int, dtype: torch.dtype) -> int:
+    n = ctypes.c_size_t(0)
+    arr = (_i64 * len(d_outs))(*[int(d) for d in d_outs])
+    _check(load().dora_factored_norm_group_workspace_size(len(d_outs), arr, d_in, r, _DTYPE_CODE[dtype],
+                                                           ctypes.byref(n)),
+           "dora_factored_norm_group_workspace_size")
+    return n.value
+
+
 def merge_workspace_size(d_in: int, r: int, dtype: torch.dtype) -> int:
     n = ctypes.c_size_t(0)
     _check(load().dora_merge_workspace_size(d_in, r, _DTYPE_CODE[dtype], ctypes.byref(n)),
@@ -179,6 +200,51 @@ def factored_norm(W0, A, B, s: float, m=None, eps: float | None = None, *, wnorm
                                   float(s), eps, _ptr(wnorm), _ptr(g), _ptr(ws), nbytes, _stream(dev)),
            "dora_factored_norm")
     return wnorm, (g if m is not None else None)
+
+
+def factored_norm_group(members, eps: float | None = None, *, outs=None, ws=None):
+    """Factored norms of several projections sharing d_in and r in one call.
+
+    members: sequence of (W0, A, B, s, m) with m fp32 [d_out] or None.
+    Returns a list of (wnorm, g) per member, g None where m is None; each
+    equals factored_norm's result for that member bitwise.
+    """
+    lib = load()
+    n = len(members)
+    if not 1 <= n <= MAX_NORM_GROUP:
+        raise ValueError(f"a group holds 1..{MAX_NORM_GROUP} members (got {n})")
+    W0_0, A_0 = members[0][0], members[0][1]
+    dev, dt = W0_0.device, W0_0.dtype
+    d_in, r = W0_0.shape[1], A_0.shape[0]
+    if dt not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {dt}")
+    eps = default_eps(dt) if eps is None else float(eps)
+    arr = (NormMember * n)()
+    results = []
+    for j, (W0, A, B, s, m) in enumerate(members):
+        d_out = W0.shape[0]
+        _need(W0, f"W0[{j}]", dev, dt, (d_out, d_in))
+        _need(A, f"A[{j}]", dev, dt, (r, d_in))
+        _need(B, f"B[{j}]", dev, dt, (d_out, r))
+        if m is not None:
+            _need(m, f"m[{j}]", dev, torch.float32, (d_out,))
+        if outs is not None:
+            wnorm, g = outs[j]
+        else:
+            wnorm = torch.empty(d_out, dtype=torch.float32, device=dev)
+            g = torch.empty(d_out, dtype=torch.float32, device=dev) if m is not None else None
+        _need(wnorm, f"wnorm[{j}]", dev, torch.float32, (d_out,))
+        if m is not None:
+            _need(g, f"g[{j}]", dev, torch.float32, (d_out,))
+        arr[j] = NormMember(_ptr(W0), _ptr(A), _ptr(B), _ptr(m), _ptr(wnorm), _ptr(g) if m is not None else None,
+                            d_out, float(s))
+        results.append((wnorm, g if m is not None else None))
+    if ws is None:
+        ws = workspace(norm_group_workspace_size([mb[0].shape[0] for mb in members], d_in, r, dt), dev)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.dora_factored_norm_group(n, arr, d_in, r, _DTYPE_CODE[dt], eps, _ptr(ws), nbytes, _stream(dev)),
+           "dora_factored_norm_group")
+    return results
 
 
 def merge(W0, A, B, g, s: float, *, out=None, ws=None):

@@ -41,6 +41,25 @@ struct NormPlan {
 
 NormPlan plan_norm(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool base_only);
 
+// Members of one grouped norm call (sizes validated by the caller).
+constexpr int kMaxNormGroup = 8;
+struct NormMember {
+    const void* W0;
+    const void* A;
+    const void* B;
+    const float* m;
+    float* wnorm;
+    float* g;
+    int64_t d_out;
+    float s;
+};
+
+// Workspace of a group: each member's own region, 256-byte aligned, in order.
+size_t norm_group_workspace_bytes(int n, const int64_t* d_out, int64_t d_in, int64_t r, int dtype);
+
+hipError_t launch_norm_group(int n, const NormMember* mem, int64_t d_in, int64_t r, int dtype, float eps,
+                             void* workspace, hipStream_t stream);
+
 hipError_t launch_norm(const NormPlan& p, const void* W0, const void* A, const void* B,
                        const float* m, float s, float eps, float* wnorm, float* g,
                        void* workspace, hipStream_t stream);

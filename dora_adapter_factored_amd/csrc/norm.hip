@@ -1072,16 +1072,14 @@ __device__ __forceinline__ void dma64_tile(const Dma64& d, int lane_off, int chu
     }
 }
 
-__global__ __launch_bounds__(Big::NTH) void w0_pass_big(W0PassArgs a) {
+__device__ __forceinline__ void w0_pass_big_body(const W0PassArgs& a, const int id, char* smem) {
     typedef Big G;
-    __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / G::WN, wn = wave % G::WN;
 
     // workgroup -> (m-tile, n-tile, k-chunk), K-chunks mapped to XCDs
     const int Q = a.n_ntiles * a.ksplit;
-    const int id = blockIdx.x;
     int q, mtile;
     if (a.xcd_map) {
         const int xcd = id % kNumXCD, slot = id / kNumXCD;
@@ -1435,15 +1433,16 @@ __global__ __launch_bounds__(256) void gram_partial(GramArgs a) {
 // stages (left and right 64-row tiles), kGramStages - 1 tiles ahead.
 constexpr int kGramStages = 8;
 
-__global__ __launch_bounds__(256) void gram_split_bf16(GramArgs a) {
+constexpr int kGramSplitLds = kGramStages * (Tile<bf16_t, 2, 2, 2, 2>::LBYTES + Tile<bf16_t, 2, 2, 2, 2>::RBYTES);
+
+__device__ __forceinline__ void gram_split_bf16_body(const GramArgs& a, const int id, char* smem) {
     typedef Tile<bf16_t, 2, 2, 2, 2> TL;
     typedef Mma<bf16_t> M;
     constexpr int NS = kGramStages;
     constexpr int STAGE = TL::LBYTES + TL::RBYTES;   // 8 KB + 8 KB
     constexpr int LPW = 2 * (TL::BM / 8 / TL::NW);   // DMA instructions per wave per tile (left + right)
     static_assert(LPW * (NS - 2) < 64, "vmcnt range");
-    __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
-    const int id = blockIdx.x;
+    static_assert(NS * STAGE == kGramSplitLds, "LDS size");
     const int xcd = id % kNumXCD, slot = id / kNumXCD;
     const int split = xcd + kNumXCD * (slot / a.nupper);
     if (split >= a.nsplit) return;
@@ -1572,9 +1571,9 @@ __global__ __launch_bounds__(256) void gram_split_bf16(GramArgs a) {
 // Gs[i][j] = (s/2) * sum_split G[i][j] for i < r, j < r; zero for r <= j < ldg.
 // The split partials are summed in split order.
 template <typename E>
-__global__ __launch_bounds__(256) void gram_finalize(const float* __restrict__ part, int nsplit, int64_t rnp,
-                                                     int64_t r, int64_t ldg, float half_s, E* __restrict__ gs) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void gram_finalize_body(const float* __restrict__ part, int nsplit, int64_t rnp,
+                                                   int64_t r, int64_t ldg, float half_s, E* __restrict__ gs,
+                                                   const int64_t idx) {
     if (idx >= r * ldg) return;
     const int64_t i = idx / ldg, j = idx % ldg;
     float v = 0.0f;
@@ -1621,11 +1620,10 @@ __global__ __launch_bounds__(256) void row_sumsq(const E* __restrict__ W0, int64
 }
 
 // ------------------------------------------------------------- finalize
-__global__ __launch_bounds__(256) void norm_finalize(const float* __restrict__ pbase, int nbase,
-                                                     const float* __restrict__ pcross, int ncross, int64_t d_out,
-                                                     float two_s, const float* __restrict__ m, float eps,
-                                                     float* __restrict__ wnorm, float* __restrict__ g) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void norm_finalize_body(const float* __restrict__ pbase, int nbase,
+                                                  const float* __restrict__ pcross, int ncross, int64_t d_out,
+                                                  float two_s, const float* __restrict__ m, float eps,
+                                                  float* __restrict__ wnorm, float* __restrict__ g, const int64_t i) {
     if (i >= d_out) return;
     // partials are loaded in batches of 16 (both kinds together) before they
     // are summed, each kind in partial order
@@ -1652,6 +1650,95 @@ __global__ __launch_bounds__(256) void norm_finalize(const float* __restrict__ p
     const float wn = sqrtf(n2);
     wnorm[i] = wn;
     if (m) g[i] = m[i] / fmaxf(wn, eps);
+}
+
+// ------------------------------------------------------------- launches
+// Kernels of one norm, and of a group of norms in one launch per stage.  A
+// group runs each stage of every member in a single grid: member j owns
+// workgroups [start[j], start[j+1]), and its starts are multiples of the XCD
+// count, so member-local workgroup ids keep their XCD.
+__global__ __launch_bounds__(Big::NTH) void w0_pass_big(W0PassArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[Big::LDS_BYTES];
+    w0_pass_big_body(a, blockIdx.x, smem);
+}
+
+__global__ __launch_bounds__(256) void gram_split_bf16(GramArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[kGramSplitLds];
+    gram_split_bf16_body(a, blockIdx.x, smem);
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void gram_finalize(const float* __restrict__ part, int nsplit, int64_t rnp,
+                                                     int64_t r, int64_t ldg, float half_s, E* __restrict__ gs) {
+    gram_finalize_body<E>(part, nsplit, rnp, r, ldg, half_s, gs, (int64_t)blockIdx.x * 256 + threadIdx.x);
+}
+
+__global__ __launch_bounds__(256) void norm_finalize(const float* __restrict__ pbase, int nbase,
+                                                     const float* __restrict__ pcross, int ncross, int64_t d_out,
+                                                     float two_s, const float* __restrict__ m, float eps,
+                                                     float* __restrict__ wnorm, float* __restrict__ g) {
+    norm_finalize_body(pbase, nbase, pcross, ncross, d_out, two_s, m, eps, wnorm, g,
+                       (int64_t)blockIdx.x * 256 + threadIdx.x);
+}
+
+struct GramFinArgs {
+    const float* part;
+    int nsplit;
+    int64_t rnp, r, ldg;
+    float half_s;
+    void* gs;
+};
+
+struct NormFinArgs {
+    const float* pbase;
+    const float* pcross;
+    int nbase, ncross;
+    int64_t d_out;
+    float two_s, eps;
+    const float* m;
+    float* wnorm;
+    float* g;
+};
+
+template <typename A>
+struct Group {
+    A a[kMaxNormGroup];
+    int start[kMaxNormGroup + 1];
+    int n;
+};
+
+// member owning workgroup id (wave-uniform; at most kMaxNormGroup compares)
+template <typename A>
+__device__ __forceinline__ int group_member(const Group<A>& g, int id) {
+    int j = 0;
+    while (j + 1 < g.n && id >= g.start[j + 1]) ++j;
+    return j;
+}
+
+__global__ __launch_bounds__(Big::NTH) void w0_pass_big_group(Group<W0PassArgs> g) {
+    __shared__ __attribute__((aligned(1024))) char smem[Big::LDS_BYTES];
+    const int j = group_member(g, blockIdx.x);
+    w0_pass_big_body(g.a[j], blockIdx.x - g.start[j], smem);
+}
+
+__global__ __launch_bounds__(256) void gram_split_bf16_group(Group<GramArgs> g) {
+    __shared__ __attribute__((aligned(1024))) char smem[kGramSplitLds];
+    const int j = group_member(g, blockIdx.x);
+    gram_split_bf16_body(g.a[j], blockIdx.x - g.start[j], smem);
+}
+
+__global__ __launch_bounds__(256) void gram_finalize_group(Group<GramFinArgs> g) {
+    const int j = group_member(g, blockIdx.x);
+    const GramFinArgs& a = g.a[j];
+    gram_finalize_body<bf16_t>(a.part, a.nsplit, a.rnp, a.r, a.ldg, a.half_s, static_cast<bf16_t*>(a.gs),
+                               (int64_t)(blockIdx.x - g.start[j]) * 256 + threadIdx.x);
+}
+
+__global__ __launch_bounds__(256) void norm_finalize_group(Group<NormFinArgs> g) {
+    const int j = group_member(g, blockIdx.x);
+    const NormFinArgs& a = g.a[j];
+    norm_finalize_body(a.pbase, a.nbase, a.pcross, a.ncross, a.d_out, a.two_s, a.m, a.eps, a.wnorm, a.g,
+                       (int64_t)(blockIdx.x - g.start[j]) * 256 + threadIdx.x);
 }
 
 // ------------------------------------------------------------- configs
@@ -1706,6 +1793,71 @@ bool operands_aligned(const NormPlan& p, const void* W0, const void* A, const vo
     return p.d_in % VEC == 0 && p.r % VEC == 0 && al16(W0) && al16(A) && al16(B) && span < (1LL << 30);
 }
 
+// Arguments and grids of the three stages of one norm (not base-only).
+struct NormLaunch {
+    GramArgs ga;
+    unsigned ggrid;
+    GramFinArgs gf;
+    unsigned gfgrid;
+    W0PassArgs wa;
+    int wgrid;
+    NormFinArgs nf;
+    unsigned nfgrid;
+};
+
+template <typename E>
+NormLaunch make_norm_launch(const NormPlan& p, bool aligned, const void* W0, const void* A, const void* B,
+                            const float* m, float s, float eps, float* wnorm, float* g, void* ws) {
+    char* w = static_cast<char*>(ws);
+    const int64_t d_out = p.d_out, d_in = p.d_in, r = p.r;
+    NormLaunch L;
+    float* gpart = reinterpret_cast<float*>(w + p.off_gpart);
+    GramArgs& ga = L.ga;
+    ga.c.left0 = Operand{A, d_in, r, d_in};
+    ga.c.right0 = ga.c.left0;
+    ga.c.left1 = ga.c.right1 = Operand{nullptr, 0, 0, 0};
+    ga.c.nkt0 = (int)((d_in + Mma<E>::BK - 1) / Mma<E>::BK);
+    ga.c.nkt1 = 0;
+    ga.ntiles = p.gram_tiles;
+    ga.nsplit = p.gram_split;
+    ga.nupper = p.gram_tiles * (p.gram_tiles + 1) / 2;
+    ga.rnp = (int64_t)p.gram_tiles * kGramTile;
+    ga.part = gpart;
+    if (sizeof(E) == 2 && aligned && p.gram_xcd)   // gram_split_bf16
+        L.ggrid = (unsigned)(kNumXCD * ((ga.nsplit + kNumXCD - 1) / kNumXCD) * ga.nupper);
+    else
+        L.ggrid = (unsigned)(ga.nupper * ga.nsplit);
+    L.gf = GramFinArgs{gpart, ga.nsplit, ga.rnp, r, p.ldg, 0.5f * s, w + p.off_gs};
+    L.gfgrid = (unsigned)((r * p.ldg + 255) / 256);
+
+    W0PassArgs& wa = L.wa;
+    wa.c.left0 = Operand{W0, d_in, d_out, d_in};
+    wa.c.right0 = Operand{A, d_in, r, d_in};
+    wa.c.left1 = Operand{B, r, d_out, r};
+    wa.c.right1 = Operand{w + p.off_gs, p.ldg, r, r};
+    wa.c.nkt0 = p.nkt_w0;
+    wa.c.nkt1 = p.nkt_g;
+    wa.B = B;
+    wa.d_out = d_out;
+    wa.r = r;
+    wa.ksplit = p.ksplit;
+    wa.n_mtiles = p.n_mtiles;
+    wa.n_ntiles = p.n_ntiles;
+    const int Q = p.n_ntiles * p.ksplit;
+    wa.xcd_map = (Q <= kNumXCD && kNumXCD % Q == 0) ? 1 : 0;
+    wa.part_base = reinterpret_cast<float*>(w + p.off_pbase);
+    wa.part_cross = reinterpret_cast<float*>(w + p.off_pcross);
+    if (wa.xcd_map) {
+        const int per = kNumXCD / Q;   // m-tiles per XCD slot
+        L.wgrid = kNumXCD * ((p.n_mtiles + per - 1) / per);
+    } else {
+        L.wgrid = Q * p.n_mtiles;
+    }
+    L.nf = NormFinArgs{wa.part_base, wa.part_cross, p.ksplit, Q, d_out, 2.0f * s, eps, m, wnorm, g};
+    L.nfgrid = (unsigned)((d_out + 255) / 256);
+    return L;
+}
+
 template <typename E>
 hipError_t norm_typed(const NormPlan& p, const void* W0, const void* A, const void* B, const float* m, float s,
                       float eps, float* wnorm, float* g, void* ws, hipStream_t st) {
@@ -1726,79 +1878,40 @@ hipError_t norm_typed(const NormPlan& p, const void* W0, const void* A, const vo
                                                                         wnorm, g);
         return hipGetLastError();
     }
-    E* gs = reinterpret_cast<E*>(w + p.off_gs);
-    float* gpart = reinterpret_cast<float*>(w + p.off_gpart);
-    float* pcross = reinterpret_cast<float*>(w + p.off_pcross);
     const bool al = operands_aligned<E>(p, W0, A, B);
     if (p.big && !al) return hipErrorInvalidValue;   // the caller runs the fallback plan
+    const NormLaunch L = make_norm_launch<E>(p, al, W0, A, B, m, s, eps, wnorm, g, ws);
 
     // 1. Gs = (s/2) A A^T
-    GramArgs ga;
-    ga.c.left0 = Operand{A, d_in, r, d_in};
-    ga.c.right0 = ga.c.left0;
-    ga.c.left1 = ga.c.right1 = Operand{nullptr, 0, 0, 0};
-    ga.c.nkt0 = (int)((d_in + Mma<E>::BK - 1) / Mma<E>::BK);
-    ga.c.nkt1 = 0;
-    ga.ntiles = p.gram_tiles;
-    ga.nsplit = p.gram_split;
-    ga.nupper = p.gram_tiles * (p.gram_tiles + 1) / 2;
-    ga.rnp = (int64_t)p.gram_tiles * kGramTile;
-    ga.part = gpart;
     if (sizeof(E) == 2 && al && p.gram_xcd) {
-        const unsigned ggrid = (unsigned)(kNumXCD * ((ga.nsplit + kNumXCD - 1) / kNumXCD) * ga.nupper);
-        gram_split_bf16<<<ggrid, 256, 0, st>>>(ga);
+        gram_split_bf16<<<L.ggrid, 256, 0, st>>>(L.ga);
     } else {
-        const unsigned ggrid = (unsigned)(ga.nupper * ga.nsplit);
         if (al)
-            gram_partial<E, true><<<ggrid, 256, 0, st>>>(ga);
+            gram_partial<E, true><<<L.ggrid, 256, 0, st>>>(L.ga);
         else
-            gram_partial<E, false><<<ggrid, 256, 0, st>>>(ga);
+            gram_partial<E, false><<<L.ggrid, 256, 0, st>>>(L.ga);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    gram_finalize<E><<<(unsigned)((r * p.ldg + 255) / 256), 256, 0, st>>>(gpart, ga.nsplit, ga.rnp, r, p.ldg,
-                                                                          0.5f * s, gs);
+    gram_finalize<E><<<L.gfgrid, 256, 0, st>>>(L.gf.part, L.gf.nsplit, L.gf.rnp, L.gf.r, L.gf.ldg, L.gf.half_s,
+                                               static_cast<E*>(L.gf.gs));
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     // 2. streaming pass over [W0 | B] x [A | Gs]^T with the row-dot epilogue
-    W0PassArgs wa;
-    wa.c.left0 = Operand{W0, d_in, d_out, d_in};
-    wa.c.right0 = Operand{A, d_in, r, d_in};
-    wa.c.left1 = Operand{B, r, d_out, r};
-    wa.c.right1 = Operand{gs, p.ldg, r, r};
-    wa.c.nkt0 = p.nkt_w0;
-    wa.c.nkt1 = p.nkt_g;
-    wa.B = B;
-    wa.d_out = d_out;
-    wa.r = r;
-    wa.ksplit = p.ksplit;
-    wa.n_mtiles = p.n_mtiles;
-    wa.n_ntiles = p.n_ntiles;
-    const int Q = p.n_ntiles * p.ksplit;
-    wa.xcd_map = (Q <= kNumXCD && kNumXCD % Q == 0) ? 1 : 0;
-    wa.part_base = pbase;
-    wa.part_cross = pcross;
-    int grid;
-    if (wa.xcd_map) {
-        const int per = kNumXCD / Q;   // m-tiles per XCD slot
-        grid = kNumXCD * ((p.n_mtiles + per - 1) / per);
-    } else {
-        grid = Q * p.n_mtiles;
-    }
     if constexpr (sizeof(E) == 2) {
         if (p.big) {
-            w0_pass_big<<<grid, Big::NTH, 0, st>>>(wa);
+            w0_pass_big<<<L.wgrid, Big::NTH, 0, st>>>(L.wa);
             e = hipGetLastError();
         } else {
-            e = al ? launch_w0<E, true>(p.cfg, wa, grid, st) : launch_w0<E, false>(p.cfg, wa, grid, st);
+            e = al ? launch_w0<E, true>(p.cfg, L.wa, L.wgrid, st) : launch_w0<E, false>(p.cfg, L.wa, L.wgrid, st);
         }
     } else {
-        e = al ? launch_w0<E, true>(p.cfg, wa, grid, st) : launch_w0<E, false>(p.cfg, wa, grid, st);
+        e = al ? launch_w0<E, true>(p.cfg, L.wa, L.wgrid, st) : launch_w0<E, false>(p.cfg, L.wa, L.wgrid, st);
     }
     if (e != hipSuccess) return e;
 
     // 3. assemble
-    norm_finalize<<<(unsigned)((d_out + 255) / 256), 256, 0, st>>>(pbase, p.ksplit, pcross, Q, d_out, 2.0f * s, m,
-                                                                    eps, wnorm, g);
+    norm_finalize<<<L.nfgrid, 256, 0, st>>>(L.nf.pbase, L.nf.nbase, L.nf.pcross, L.nf.ncross, L.nf.d_out,
+                                            L.nf.two_s, L.nf.m, L.nf.eps, L.nf.wnorm, L.nf.g);
     return hipGetLastError();
 }
 
@@ -1931,6 +2044,72 @@ hipError_t launch_norm(const NormPlan& p, const void* W0, const void* A, const v
         return norm_typed<bf16_t>(f, W0, A, B, m, s, eps, wnorm, g, workspace, stream);
     }
     return norm_typed<bf16_t>(p, W0, A, B, m, s, eps, wnorm, g, workspace, stream);
+}
+
+size_t norm_group_workspace_bytes(int n, const int64_t* d_out, int64_t d_in, int64_t r, int dtype) {
+    size_t total = 0;
+    for (int j = 0; j < n; ++j) total += align_up(plan_norm(d_out[j], d_in, r, dtype, false).bytes_needed, 256);
+    return total;
+}
+
+// One call for several norms that share d_in and r (the projections of one
+// layer that read the same input).  When every member takes the aligned bf16
+// large-tile path, each stage runs once for the whole group (four launches in
+// all); otherwise the members run one after another.  Either way a member's
+// kernels, tiling and summation order are those of its own single call, so
+// the results are bitwise the same.
+hipError_t launch_norm_group(int n, const NormMember* mem, int64_t d_in, int64_t r, int dtype, float eps,
+                             void* workspace, hipStream_t st) {
+    static_assert(sizeof(Group<W0PassArgs>) <= 4096 && sizeof(Group<GramArgs>) <= 4096, "kernel argument size");
+    NormPlan plans[kMaxNormGroup];
+    char* wsj[kMaxNormGroup];
+    size_t off = 0;
+    bool grouped = dtype == kBF16;
+    for (int j = 0; j < n; ++j) {
+        const NormMember& M = mem[j];
+        plans[j] = plan_norm(M.d_out, d_in, r, dtype, M.s == 0.0f);
+        wsj[j] = static_cast<char*>(workspace) + off;
+        off += align_up(plan_norm(M.d_out, d_in, r, dtype, false).bytes_needed, 256);
+        grouped = grouped && plans[j].big && plans[j].gram_xcd && !plans[j].base_only &&
+                  operands_aligned<bf16_t>(plans[j], M.W0, M.A, M.B);
+    }
+    if (!grouped) {
+        for (int j = 0; j < n; ++j) {
+            const NormMember& M = mem[j];
+            const hipError_t e = launch_norm(plans[j], M.W0, M.A, M.B, M.m, M.s, eps, M.wnorm, M.g, wsj[j], st);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    Group<GramArgs> gg;
+    Group<GramFinArgs> gf;
+    Group<W0PassArgs> gw;
+    Group<NormFinArgs> gn;
+    gg.n = gf.n = gw.n = gn.n = n;
+    gg.start[0] = gf.start[0] = gw.start[0] = gn.start[0] = 0;
+    auto pad8 = [](int x) { return (x + kNumXCD - 1) / kNumXCD * kNumXCD; };
+    for (int j = 0; j < n; ++j) {
+        const NormMember& M = mem[j];
+        const NormLaunch L = make_norm_launch<bf16_t>(plans[j], true, M.W0, M.A, M.B, M.m, M.s, eps, M.wnorm, M.g,
+                                                      wsj[j]);
+        gg.a[j] = L.ga;
+        gg.start[j + 1] = gg.start[j] + pad8((int)L.ggrid);
+        gf.a[j] = L.gf;
+        gf.start[j + 1] = gf.start[j] + (int)L.gfgrid;
+        gw.a[j] = L.wa;
+        gw.start[j + 1] = gw.start[j] + pad8(L.wgrid);
+        gn.a[j] = L.nf;
+        gn.start[j + 1] = gn.start[j] + (int)L.nfgrid;
+    }
+    hipError_t e;
+    gram_split_bf16_group<<<gg.start[n], 256, 0, st>>>(gg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    gram_finalize_group<<<gf.start[n], 256, 0, st>>>(gf);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    w0_pass_big_group<<<gw.start[n], Big::NTH, 0, st>>>(gw);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    norm_finalize_group<<<gn.start[n], 256, 0, st>>>(gn);
+    return hipGetLastError();
 }
 
 }  // namespace dora

@@ -96,6 +96,54 @@ int dora_factored_norm(const void* W0, const void* A, const void* B, const float
                        void* stream);
 
 /*
+ * One member of a grouped norm call: the operands and outputs of one
+ * dora_factored_norm call (same meanings and layouts).  W0 is [d_out, d_in],
+ * A [r, d_in], B [d_out, r]; m may be NULL (then g is not written).
+ */
+typedef struct DoraNormMember {
+    const void* W0;
+    const void* A;
+    const void* B;
+    const float* m;
+    float* wnorm;
+    float* g;
+    int64_t d_out;
+    float s;
+} DoraNormMember;
+
+/* Maximum members of one grouped norm call. */
+#define DORA_MAX_NORM_GROUP 8
+
+/*
+ * Workspace bytes needed by dora_factored_norm_group for members of these
+ * row counts (host call, launches nothing).
+ */
+int dora_factored_norm_group_workspace_size(int n, const int64_t* d_out, int64_t d_in, int64_t r, int dtype,
+                                            size_t* bytes);
+
+/*
+ * Factored row norms of up to DORA_MAX_NORM_GROUP adapted projections that
+ * share d_in and r (the projections of one layer reading the same input),
+ * in one call.  Each member computes exactly what dora_factored_norm
+ * computes for it, with bitwise the same result; when every member is bf16
+ * with 16-byte aligned operands and r > 192, each stage of the method
+ * ([ScalingDoRA] §2: Gram, the W0 pass with its row epilogue, assembly)
+ * runs as one launch for the whole group, so small projections (k/v rows)
+ * share the chip instead of paying launch and tail costs one by one.
+ *
+ *   n         1 .. DORA_MAX_NORM_GROUP.
+ *   members   host array of n members; every member's pointers are device
+ *             pointers, validated as in dora_factored_norm.  Outputs of
+ *             different members must not overlap.
+ *   d_in, r, dtype, eps   shared by all members.
+ *   workspace device scratch of at least
+ *             dora_factored_norm_group_workspace_size() bytes, 256-byte
+ *             aligned.
+ */
+int dora_factored_norm_group(int n, const DoraNormMember* members, int64_t d_in, int64_t r, int dtype, float eps,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Fused compose forward, one pass: 2 reads + 1 write per element.
  *
  * [ScalingDoRA] §3 (compose kernel, numerically stable form with fp32

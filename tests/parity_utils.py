@@ -49,7 +49,7 @@ def sample_rows(n, k, seed=0):
     """Deterministic sample of k row indices of n, always including both ends
     and the first rows of each 128-row tile boundary region."""
     rng = np.random.default_rng(seed)
-    fixed = {0, 1, n - 1, n // 2}
+    fixed = {i for i in (0, 1, n - 1, n // 2) if i < n}
     fixed |= {min(n - 1, b) for b in range(127, n, 128 * 7)}
     extra = rng.choice(n, size=min(n, k), replace=False)
     return np.array(sorted(fixed | set(extra.tolist())), dtype=np.int64)

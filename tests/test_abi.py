@@ -241,6 +241,58 @@ def test_merge_validation(lib):
     assert b"256-byte" in lib.dora_last_error_detail()
 
 
+def test_norm_group_workspace_size(lib):
+    n = ctypes.c_size_t()
+    d = (ctypes.c_int64 * 3)(5120, 1024, 1024)
+    assert lib.dora_factored_norm_group_workspace_size(3, d, 5120, 384, 1, ctypes.byref(n)) == 0
+    total = 0
+    for d_out in (5120, 1024, 1024):   # each member's own region, 256-byte aligned
+        one = ctypes.c_size_t()
+        assert lib.dora_factored_norm_workspace_size(d_out, 5120, 384, 1, ctypes.byref(one)) == 0
+        total += (one.value + 255) // 256 * 256
+    assert n.value == total
+    assert lib.dora_factored_norm_group_workspace_size(0, d, 5120, 384, 1, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
+    assert lib.dora_factored_norm_group_workspace_size(9, d, 5120, 384, 1, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
+    assert lib.dora_factored_norm_group_workspace_size(3, None, 5120, 384, 1, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
+    assert lib.dora_factored_norm_group_workspace_size(3, d, 5120, 384, 2, ctypes.byref(n)) == Bn.DORA_ERR_UNSUPPORTED
+    bad = (ctypes.c_int64 * 2)(64, 0)
+    assert lib.dora_factored_norm_group_workspace_size(2, bad, 48, 8, 1, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
+
+
+def _group(lib, members=None, **kw):
+    if members is None:
+        members = [dict()]
+    arr = (Bn.NormMember * max(1, len(members)))()
+    for j, over in enumerate(members):
+        mb = dict(W0=0x10000, A=0x20000, B=0x30000, m=0x40000, wnorm=0x50000 + 0x1000 * j, g=0x60000 + 0x1000 * j,
+                  d_out=64, s=1.0)
+        mb.update(over)
+        arr[j] = Bn.NormMember(mb["W0"], mb["A"], mb["B"], mb["m"], mb["wnorm"], mb["g"], mb["d_out"], mb["s"])
+    a = dict(n=len(members), arr=arr, d_in=48, r=8, dtype=1, eps=1e-6, ws=FAKE_WS, nbytes=1 << 30)
+    a.update(kw)
+    return lib.dora_factored_norm_group(a["n"], a["arr"], a["d_in"], a["r"], a["dtype"], a["eps"], a["ws"],
+                                        a["nbytes"], None)
+
+
+def test_norm_group_validation(lib):
+    E = Bn
+    assert _group(lib, arr=None) == E.DORA_ERR_INVALID_ARG
+    assert _group(lib, n=0) == E.DORA_ERR_INVALID_ARG
+    assert _group(lib, [dict()] * 9) == E.DORA_ERR_INVALID_ARG
+    for k in ("W0", "A", "B", "wnorm"):
+        assert _group(lib, [dict(), {k: None}]) == E.DORA_ERR_INVALID_ARG, k
+    assert _group(lib, [dict(g=None)]) == E.DORA_ERR_INVALID_ARG            # m given without g
+    assert _group(lib, [dict(), dict(d_out=0)]) == E.DORA_ERR_INVALID_ARG
+    assert _group(lib, [dict(s=float("nan"))]) == E.DORA_ERR_INVALID_ARG
+    assert _group(lib, d_in=0) == E.DORA_ERR_INVALID_ARG
+    assert _group(lib, dtype=2) == E.DORA_ERR_UNSUPPORTED
+    assert _group(lib, dtype=7) == E.DORA_ERR_INVALID_ARG
+    assert _group(lib, eps=-1.0) == E.DORA_ERR_INVALID_ARG
+    assert _group(lib, ws=None) == E.DORA_ERR_WORKSPACE
+    assert _group(lib, nbytes=8) == E.DORA_ERR_WORKSPACE
+    assert _group(lib, ws=ctypes.c_void_p(0x100080)) == E.DORA_ERR_WORKSPACE
+
+
 def test_binding_rejects_bad_tensors_before_the_library():
     # host tensors are refused by the shape/device checks of the binding
     cpu = torch.zeros(4, 8, dtype=torch.bfloat16)

@@ -1,0 +1,128 @@
+"""GPU parity of the grouped norm (several projections sharing d_in and r in
+one call): every member's result is bitwise that of its own single call, and
+agrees with the fp64 oracle on sampled rows."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import dora_adapter_factored_amd as D
+import dora_inputs as DI
+import oracle
+from parity_utils import check_rel, host64, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _members(layers, with_m=True):
+    return [(L.W0, L.A, L.B, L.spec.s, L.m if with_m else None) for L in layers]
+
+
+def _check_against_single_calls(layers, results, with_m=True):
+    torch.cuda.synchronize()
+    for L, (wn, g) in zip(layers, results):
+        wn1, g1 = D.factored_norm(L.W0, L.A, L.B, L.spec.s, L.m if with_m else None)
+        torch.cuda.synchronize()
+        assert torch.equal(wn, wn1), L.spec.name
+        if with_m:
+            assert torch.equal(g, g1), L.spec.name
+        else:
+            assert g is None
+
+
+def _check_oracle(L, wn, g, nrows, seed, rtol):
+    rows = sample_rows(L.spec.d_out, nrows, seed=seed)
+    ref = oracle.dense_row_norm(L.W0.cpu(), L.A.cpu(), L.B.cpu(), L.spec.s, rows=rows)
+    check_rel(host64(wn)[rows], ref, rtol, f"{L.spec.name} wnorm")
+    if g is not None:
+        eps = D.default_eps(L.W0.dtype)
+        check_rel(host64(g)[rows], oracle.magnitude_scale(host64(L.m)[rows], ref, eps), rtol, f"{L.spec.name} g")
+
+
+def test_group_of_one_layer_of_the_sweep():
+    # the six projections of one layer that read the 5120-wide input
+    layers = []
+    for proj in range(6):
+        spec = DI.sweep_spec(proj)
+        say(f"[group] generating {spec.name}")
+        layers.append(DI.make_layer(spec, DI.sweep_seed(3, proj), device=DEV, activations=False,
+                                    gen_device="cuda"))
+    say("[group] sweep layer, 6 members")
+    res = D.factored_norm_group(_members(layers))
+    _check_against_single_calls(layers, res)
+    for j, (L, (wn, g)) in enumerate(zip(layers, res)):
+        _check_oracle(L, wn, g, 64, 90 + j, 2e-3)
+
+
+GROUP_CASES = [
+    # (d_outs, d_in, r, dtype): grouped kernels when bf16, aligned, r > 192
+    ((300, 1000, 520), 4096, 256, "bf16"),
+    ((64, 8, 1), 1024, 384, "bf16"),
+    ((257, 129), 2048, 200, "bf16"),
+    ((64, 48), 48, 8, "f32"),          # member by member
+    ((500, 33), 640, 16, "bf16"),      # r <= 192: member by member
+]
+
+
+@pytest.mark.parametrize("d_outs,d_in,r,dt", GROUP_CASES)
+def test_group_shapes(d_outs, d_in, r, dt):
+    say(f"[group] d_outs={d_outs} d_in={d_in} r={r} {dt}")
+    layers = [DI.make_layer(DI.custom_spec(d, d_in, r, 1, dtype=dt, s=1.5, b_std=0.05), 700 + j, device=DEV,
+                            activations=False) for j, d in enumerate(d_outs)]
+    res = D.factored_norm_group(_members(layers))
+    _check_against_single_calls(layers, res)
+    rtol = 2e-3 if dt == "bf16" else 1e-4
+    for j, (L, (wn, g)) in enumerate(zip(layers, res)):
+        _check_oracle(L, wn, g, 128, j, rtol)
+
+
+def test_group_mixed_members_and_no_magnitude():
+    say("[group] s = 0 member, m = None members, unaligned member")
+    layers = [DI.make_layer(DI.custom_spec(d, 1024, 256, 1, s=1.0, b_std=0.05), 800 + j, device=DEV,
+                            activations=False) for j, d in enumerate((256, 512, 384))]
+    # wnorm only (m = None) for every member: the grouped kernels
+    res = D.factored_norm_group(_members(layers, with_m=False))
+    _check_against_single_calls(layers, res, with_m=False)
+    # one member with s = 0 (base norm only): member by member
+    members = _members(layers)
+    members[1] = (layers[1].W0, layers[1].A, layers[1].B, 0.0, layers[1].m)
+    res = D.factored_norm_group(members)
+    torch.cuda.synchronize()
+    wn1, _ = D.factored_norm(layers[1].W0, layers[1].A, layers[1].B, 0.0, layers[1].m)
+    torch.cuda.synchronize()
+    assert torch.equal(res[1][0], wn1)
+    ref = torch.linalg.vector_norm(layers[1].W0.double(), dim=1).cpu().numpy()
+    check_rel(host64(res[1][0]), ref, 2e-3, "s = 0 member")
+    for j in (0, 2):
+        wn, g = D.factored_norm(layers[j].W0, layers[j].A, layers[j].B, 1.0, layers[j].m)
+        torch.cuda.synchronize()
+        assert torch.equal(res[j][0], wn) and torch.equal(res[j][1], g)
+    # one member whose W0 is not 16-byte aligned: member by member, same results
+    buf = torch.empty(layers[2].W0.numel() + 1, dtype=torch.bfloat16, device=DEV)
+    W0u = buf[1:].view(layers[2].W0.shape)
+    W0u.copy_(layers[2].W0)
+    members = _members(layers)
+    members[2] = (W0u, layers[2].A, layers[2].B, 1.0, layers[2].m)
+    res = D.factored_norm_group(members)
+    torch.cuda.synchronize()
+    for j, (W0, A, B, s, m) in enumerate(members):
+        wn, g = D.factored_norm(W0, A, B, s, m)
+        torch.cuda.synchronize()
+        assert torch.equal(res[j][0], wn) and torch.equal(res[j][1], g), j
+    _check_oracle(layers[2], res[2][0], res[2][1], 128, 7, 2e-3)
+
+
+def test_group_of_one_and_repeated_calls():
+    say("[group] one member; repeated calls")
+    L = DI.make_layer(DI.custom_spec(1024, 2048, 384, 1, b_std=0.05), 901, device=DEV, activations=False)
+    a = D.factored_norm_group(_members([L]))
+    a = [(w.clone(), g.clone()) for w, g in a]
+    b = D.factored_norm_group(_members([L]))
+    _check_against_single_calls([L], b)
+    assert torch.equal(a[0][0], b[0][0]) and torch.equal(a[0][1], b[0][1])
