@@ -187,10 +187,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4])
+    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args()
+    args.steps_given = any(a.startswith("--steps") for a in sys.argv[1:])
+    args.warmup_given = any(a.startswith("--warmup") for a in sys.argv[1:])
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the DoRA norm and compose are "
               "per-layer kernels; multi-GPU sharding is not part of this build.", file=sys.stderr)
@@ -200,6 +202,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.config == 5:
+        return sweep_main(args, D, dev)
     spec = DI.CONFIGS[args.config]
     calib = copy_calibration(dev)
     print(f"[bench] copy calibration {calib}", file=sys.stderr, flush=True)
@@ -360,6 +364,172 @@ def main():
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(layer, args.cpu_budget)
     print(json.dumps(out), flush=True)
+
+
+SWEEP_METRIC = "many-module sweep: norm + compose fwd/bwd ms per step (64 layers x 7 projections, r=384 bf16)"
+
+
+def sweep_main(args, D, dev):
+    """The many-module sweep: 64 layers x 7 adapted projections, every
+    module's weights resident; a step is every layer's norms (the six
+    projections reading the 5120-wide input in one grouped call, down on its
+    own) and compose forward and backward of every module, in model order.
+    Activations are pooled per shape, two rotating copies."""
+    nl, npj = DI.SWEEP_LAYERS, len(DI.SWEEP_PROJECTIONS)
+    T, r = DI.SWEEP_T, DI.SWEEP_R
+    print(f"[bench] generating {nl} x {npj} modules on the device", file=sys.stderr, flush=True)
+    layers = []
+    for li in range(nl):
+        mods = []
+        for pj in range(npj):
+            L = DI.make_layer(DI.sweep_spec(pj), DI.sweep_seed(li, pj), device=dev, activations=False,
+                              gen_device="cuda")
+            L.wn = torch.empty(L.spec.d_out, device=dev)
+            L.g = torch.empty(L.spec.d_out, device=dev)
+            mods.append(L)
+        layers.append(mods)
+    torch.cuda.synchronize()
+    weight_bytes = sum(L.W0.numel() * 2 + L.A.numel() * 2 + L.B.numel() * 2 for mods in layers for L in mods)
+    gen = torch.Generator(device=dev).manual_seed(77)
+    pool = {}
+    for _, d_out, _ in DI.SWEEP_PROJECTIONS:
+        if d_out in pool:
+            continue
+        sets = []
+        for _ in range(2):
+            mk = lambda: torch.randn(T, d_out, device=dev, generator=gen).to(torch.bfloat16)  # noqa: E731
+            sets.append(dict(base=mk(), lora=mk(), dy=mk(), y=torch.empty(T, d_out, dtype=torch.bfloat16, device=dev),
+                             db=torch.empty(T, d_out, dtype=torch.bfloat16, device=dev),
+                             dl=torch.empty(T, d_out, dtype=torch.bfloat16, device=dev),
+                             dm=torch.empty(d_out, device=dev)))
+        pool[d_out] = sets
+    grp = list(range(6))        # q, k, v, o, gate, up: d_in 5120
+    d_in_g = DI.SWEEP_PROJECTIONS[0][2]
+    ws_group = torch.empty(D.norm_group_workspace_size([DI.SWEEP_PROJECTIONS[j][1] for j in grp], d_in_g, r,
+                                                       torch.bfloat16), dtype=torch.uint8, device=dev)
+    ws_single = torch.empty(max(D.norm_workspace_size(d_out, d_in, r, torch.bfloat16)
+                                for _, d_out, d_in in DI.SWEEP_PROJECTIONS), dtype=torch.uint8, device=dev)
+    ws_bwd = torch.empty(max(D.compose_backward_workspace_size(T, d_out) for _, d_out, _ in DI.SWEEP_PROJECTIONS),
+                         dtype=torch.uint8, device=dev)
+    eps = D.default_eps(torch.bfloat16)
+    stream = torch.cuda.current_stream(dev)
+
+    def norms(mods, grouped):
+        if grouped:
+            D.factored_norm_group([(mods[j].W0, mods[j].A, mods[j].B, mods[j].spec.s, mods[j].m) for j in grp],
+                                  eps, outs=[(mods[j].wn, mods[j].g) for j in grp], ws=ws_group)
+            rest = [j for j in range(npj) if j not in grp]
+        else:
+            rest = range(npj)
+        for j in rest:
+            L = mods[j]
+            D.factored_norm(L.W0, L.A, L.B, L.spec.s, L.m, eps, wnorm=L.wn, g=L.g, ws=ws_single)
+
+    def composes(mods, it):
+        for L in mods:
+            st = pool[L.spec.d_out][it % 2]
+            D.compose(st["base"], st["lora"], L.g, L.spec.s, out=st["y"])
+            D.compose_backward(st["dy"], st["base"], st["lora"], L.g, L.wn, L.spec.s, eps, d_base=st["db"],
+                               d_lora=st["dl"], d_m=st["dm"], ws=ws_bwd)
+
+    def step(it, grouped=True, do_norm=True, do_compose=True):
+        for mods in layers:
+            if do_norm:
+                norms(mods, grouped)
+            if do_compose:
+                composes(mods, it)
+
+    def timed(k, **kw):
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        for i in range(k):
+            step(i, **kw)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / k, ev[0].elapsed_time(ev[1]) * 1e-3 / k
+
+    steps = args.steps if args.steps_given else 10
+    warm = args.warmup if args.warmup_given else 2
+    print(f"[bench] sweep warmup {warm}, timing {steps} steps", file=sys.stderr, flush=True)
+    for i in range(warm):
+        step(i)
+    wall, gpu = timed(steps)
+    k2 = max(2, min(steps, 5))
+    _, t_norm_g = timed(k2, do_compose=False)
+    _, t_norm_s = timed(k2, grouped=False, do_compose=False)
+    _, t_comp = timed(k2, do_norm=False)
+    F = nl * sum(norm_flops(d_out, d_in, r) for _, d_out, d_in in DI.SWEEP_PROJECTIONS)
+    cbytes = nl * sum(compose_fwd_bytes(T, d_out, 2) + compose_bwd_bytes(T, d_out, 2)
+                      for _, d_out, _ in DI.SWEEP_PROJECTIONS)
+    per_module_ws = {f"{n}-{d_out}x{d_in}": D.norm_workspace_size(d_out, d_in, r, torch.bfloat16)
+                     for n, d_out, d_in in DI.SWEEP_PROJECTIONS}
+    out = {
+        "metric": SWEEP_METRIC,
+        "value": round(gpu * 1e3, 3),
+        "unit": "ms/step",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(wall * 1e3, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
+        "config": {"workload": "sweep-64x7-r384-bf16", "layers": nl, "projections": [p[0] for p in
+                   DI.SWEEP_PROJECTIONS], "tokens": T, "r": r, "weights_resident_bytes": weight_bytes},
+        "sweep": {
+            "norm_ms_per_step_grouped": round(t_norm_g * 1e3, 3),
+            "norm_ms_per_step_one_by_one": round(t_norm_s * 1e3, 3),
+            "norm_TFLOPs_grouped": round(F / t_norm_g / 1e12, 1),
+            "compose_ms_per_step": round(t_comp * 1e3, 3),
+            "compose_GBps": round(cbytes / t_comp / 1e9, 1),
+            "norm_workspace_bytes_per_module": per_module_ws,
+            "norm_workspace_bytes_group_of_6": int(ws_group.numel()),
+            "compose_bwd_workspace_bytes_max": int(ws_bwd.numel()),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a row sample of one layer", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = sweep_cpu_baseline(layers[0], args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+def sweep_cpu_baseline(mods, budget_s=12.0):
+    """The oracle on a row and token sample of one layer of the sweep,
+    extrapolated to a whole step (64 layers)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    per = budget_s / len(mods)
+    total, parts = 0.0, []
+    for L in mods:
+        spec = L.spec
+        W0, A, B = L.W0.cpu(), L.A.cpu(), L.B.cpu()
+        rows_done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 0.8 * per and rows_done < spec.d_out:
+            rows = np.arange(rows_done, min(spec.d_out, rows_done + 128))
+            oracle.dense_row_norm(W0, A, B, spec.s, rows=rows)
+            rows_done += rows.size
+        t_norm = (time.perf_counter() - t0) * spec.d_out / rows_done
+        tok = 64
+        x = np.random.default_rng(0).standard_normal((tok, spec.d_out))
+        g = np.ones(spec.d_out)
+        t1 = time.perf_counter()
+        oracle.compose_forward(x, x, g, spec.s)
+        oracle.compose_backward(x, x, x, g, g, spec.s, 1e-7)
+        t_comp = (time.perf_counter() - t1) * DI.SWEEP_T / tok
+        total += t_norm + t_comp
+        parts.append(f"{spec.name}: {rows_done} rows, {tok} tokens")
+    return {"value": round(total * DI.SWEEP_LAYERS * 1e3, 1), "unit": "ms/step (extrapolated)",
+            "cores": int(threads), "kind": "oracle",
+            "sample": "one layer, row and token samples, scaled to 64 layers: " + "; ".join(parts),
+            "cpu": _cpu_model()}
 
 
 if __name__ == "__main__":
