@@ -21,6 +21,7 @@
 // the whole strip and walks rows, with several rows' loads in flight before
 // the first store.
 #include "dora_device.h"
+#include "dora_gfx950.h"
 #include "dora_launch.h"
 
 namespace dora {
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void compose_bwd_vec(const T* dy, const T
 #pragma unroll
             for (int e = 0; e < N; ++e) red[tr - 1][tc * N + e] = acc[e];
         }
-        __syncthreads();
+        lds_barrier();   // the d_base / d_lora stores stay in flight
         if (tr == 0 && active) {
 #pragma unroll
             for (int e = 0; e < N; ++e) {

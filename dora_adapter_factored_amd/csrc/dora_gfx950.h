@@ -37,6 +37,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 // s_waitcnt on LDS / scalar-memory operations only (lgkmcnt = 0).
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are
+// complete, then s_barrier.  Unlike __syncthreads it does not wait for
+// outstanding global loads and stores (on gfx9 one counter covers both), so
+// stores issued before it stay in flight.  The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Chunk swizzle of 64-byte rows: logical chunk c of row i sits in slot
 // c ^ swz64(i).  For a fixed chunk, the 16 rows of any aligned 16-row block
 // map to 16 distinct (row mod 4, slot) pairs and the even (odd) rows of any

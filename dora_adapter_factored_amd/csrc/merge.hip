@@ -348,17 +348,6 @@ __device__ __forceinline__ void dma_group(const DmaOp& d, int grp, int kt, int l
     raw_buffer_load_lds(rs, (lds_void_t*)(dst + grp * 1024), 16, voff, 0, 0, 0);
 }
 
-// Workgroup barrier for LDS traffic only: this wave's LDS operations are
-// complete, then s_barrier.  Unlike __syncthreads it does not wait for
-// outstanding global loads and stores.  The empty asm statements keep the
-// compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // Wait until a stage has landed while `after` later stages (and, if w0, the
 // NW0 W0 loads) may stay in flight.  Both are wave-uniform run-time values;
 // each combination gets its own immediate.
