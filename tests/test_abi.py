@@ -64,6 +64,21 @@ def test_workspace_queries(lib):
     assert lib.dora_compose_backward_workspace_size(-1, 8192, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
 
 
+def test_norm_transient_against_the_dense_product(lib):
+    # The pages' accounting: the factored norm needs O(d r + r^2) scratch where
+    # the dense route materialises d x d; at d = 8192, r = 512 the ratio of the
+    # element counts is d^2 / (d r + r^2) = 15.06.
+    d, r = 8192, 512
+    assert round(d * d / (d * r + r * r), 2) == 15.06
+    # this library's scratch (fp32 split partials included) stays an order of
+    # magnitude below the bf16 dense product: 24x at r = 384, 13.8x at r = 512
+    n = ctypes.c_size_t()
+    for rr in (384, 512):
+        assert lib.dora_factored_norm_workspace_size(d, d, rr, 1, ctypes.byref(n)) == 0
+        dense_bytes = d * d * 2
+        assert n.value * 10 < dense_bytes, (rr, n.value)
+
+
 def _norm(lib, **kw):
     a = dict(W0=FAKE, A=FAKE, B=FAKE, m=FAKE, d_out=64, d_in=48, r=8, dtype=1, s=1.0, eps=1e-6,
              wnorm=FAKE, g=FAKE, ws=FAKE_WS, nbytes=1 << 30, stream=None)
