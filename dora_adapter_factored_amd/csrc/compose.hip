@@ -212,24 +212,39 @@ __global__ __launch_bounds__(kThreads) void compose_bwd_scalar(const T* dy, cons
 // A workgroup owns 64 columns; its 4 waves sum interleaved partial rows
 // (p = w, w + 4, ...) with independent loads in flight, then wave 0 adds the
 // four sums in wave order.  The order is fixed, so d_m is reproducible.
-constexpr int kFinCols = 64;
+constexpr int kFinCols = 32;                       // d_m columns per workgroup
+constexpr int kFinLanes = kThreads / kFinCols;      // partial rows per column, summed side by side
+constexpr int kFinBatch = 16;                       // loads a lane issues before summing
+
+// d_m_j = (sum over partial rows p of part[p][j]) / max(wnorm_j, eps).  Lane
+// w of column j sums rows w, w + kFinLanes, ... in order, loading a batch of
+// them at once; the kFinLanes sums are then added in lane order.  The order
+// is fixed, so the result is bitwise reproducible.
 __global__ __launch_bounds__(kThreads) void dm_finalize(const float* __restrict__ part, int nparts,
                                                         const float* __restrict__ wnorm, float eps,
                                                         int64_t d_out, float* __restrict__ d_m) {
-    __shared__ float red[kThreads / kFinCols][kFinCols];
+    __shared__ float red[kFinLanes][kFinCols];
     const int c = threadIdx.x % kFinCols, w = threadIdx.x / kFinCols;
     const int64_t j = (int64_t)blockIdx.x * kFinCols + c;
     float acc = 0.0f;
     if (j < d_out) {
-#pragma unroll 8
-        for (int p = w; p < nparts; p += kThreads / kFinCols) acc += part[(int64_t)p * d_out + j];
+        for (int p0 = w; p0 < nparts; p0 += kFinLanes * kFinBatch) {
+            float x[kFinBatch];
+#pragma unroll
+            for (int t = 0; t < kFinBatch; ++t) {
+                const int p = p0 + t * kFinLanes;
+                x[t] = p < nparts ? part[(int64_t)p * d_out + j] : 0.0f;
+            }
+#pragma unroll
+            for (int t = 0; t < kFinBatch; ++t) acc += x[t];
+        }
     }
     red[w][c] = acc;
     __syncthreads();
     if (w == 0 && j < d_out) {
         float v = red[0][c];
 #pragma unroll
-        for (int q = 1; q < kThreads / kFinCols; ++q) v += red[q][c];
+        for (int q = 1; q < kFinLanes; ++q) v += red[q][c];
         d_m[j] = nparts > 0 ? v / fmaxf(wnorm[j], eps) : 0.0f;
     }
 }
