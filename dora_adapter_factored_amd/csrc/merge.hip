@@ -84,6 +84,46 @@ __global__ __launch_bounds__(256) void transpose_a_vec(const E* __restrict__ A, 
     }
 }
 
+// bf16 form: a thread loads 16 bytes from each of two adjacent k-rows of A,
+// packs each column's (k, k + 1) pair into one 32-bit word and writes it to
+// an LDS tile held n-major with a 33-word pitch (a wave's writes then fall
+// in 64 distinct banks); it then reads 4 words (8 k-values) of one n and
+// stores them as one 16-byte run of A^T.
+constexpr int kTrPitchW = kTrTile / 2 + 1;          // words per LDS row of the bf16 tile
+
+__global__ __launch_bounds__(256) void transpose_a_bf16(const bf16_t* __restrict__ A, int64_t r, int64_t d_in,
+                                                        bf16_t* __restrict__ At, int64_t r_pad) {
+    __shared__ uint32_t tile[kTrTile][kTrPitchW];   // [n][k / 2]
+    const int tid = threadIdx.x;
+    const int64_t n0 = (int64_t)blockIdx.x * kTrTile, k0 = (int64_t)blockIdx.y * kTrTile;
+    {
+        const int cc = tid & 7, kp = tid >> 3;       // 8 column chunks x 32 k-pairs
+        const int64_t n = n0 + (int64_t)cc * 8, k = k0 + 2 * kp;
+        Pack<bf16_t> lo, hi;
+        lo.u = (k < r && n < d_in) ? *reinterpret_cast<const u32x4_t*>(A + k * d_in + n) : u32x4_t{0u, 0u, 0u, 0u};
+        hi.u = (k + 1 < r && n < d_in) ? *reinterpret_cast<const u32x4_t*>(A + (k + 1) * d_in + n)
+                                       : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t w = (uint32_t)__builtin_bit_cast(uint16_t, lo.e[e]) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, hi.e[e]) << 16);
+            tile[cc * 8 + e][kp] = w;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = tid + 256 * i, nr = c >> 3, kc = c & 7;
+        const int64_t n = n0 + nr, k = k0 + (int64_t)kc * 8;
+        if (n < d_in && k < r_pad) {
+            u32x4_t v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = tile[nr][kc * 4 + j];
+            *reinterpret_cast<u32x4_t*>(At + n * r_pad + k) = v;
+        }
+    }
+}
+
 // ------------------------------------------------------------- MFMA traits
 // A k-tile holds 64 bytes of K per row.  In each of its two MFMA k-steps a
 // lane supplies the 16-byte chunk 2*step + lane/32 of its row, for both
@@ -497,6 +537,8 @@ __global__ __launch_bounds__(kNTh, sizeof(E) == 2 ? 3 : 2) void merge_tile_dma(M
     }
 }
 
+inline const bf16_t* A_bf16(const void* p) { return static_cast<const bf16_t*>(p); }
+
 template <typename E>
 hipError_t merge_typed(const void* W0, const void* A, const void* B, const float* g, float s, int64_t d_out,
                        int64_t d_in, int64_t r, void* W, void* workspace, hipStream_t st) {
@@ -506,8 +548,12 @@ hipError_t merge_typed(const void* W0, const void* A, const void* B, const float
     constexpr int VEC = 16 / sizeof(E);
     auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
     const dim3 tgrid((unsigned)((d_in + kTrTile - 1) / kTrTile), (unsigned)((r_pad + kTrTile - 1) / kTrTile));
-    if (d_in % VEC == 0 && al16(A))
-        transpose_a_vec<E><<<tgrid, 256, 0, st>>>(static_cast<const E*>(A), r, d_in, At, r_pad);
+    if (d_in % VEC == 0 && al16(A)) {
+        if constexpr (sizeof(E) == 2)
+            transpose_a_bf16<<<tgrid, 256, 0, st>>>(A_bf16(A), r, d_in, reinterpret_cast<bf16_t*>(At), r_pad);
+        else
+            transpose_a_vec<E><<<tgrid, 256, 0, st>>>(static_cast<const E*>(A), r, d_in, At, r_pad);
+    }
     else
         transpose_a<E><<<tgrid, 256, 0, st>>>(static_cast<const E*>(A), r, d_in, At, r_pad);
 
