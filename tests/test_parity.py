@@ -150,6 +150,46 @@ def test_norm_scale_zero(dt):
     check_rel(host64(wn), ref, NORM_RTOL[L.W0.dtype], "wnorm s=0")
 
 
+CANCEL_CASES = [(256, 512, 256, "bf16"), (256, 512, 32, "bf16"), (128, 256, 16, "f32")]
+
+
+@pytest.mark.parametrize("d_out,d_in,r,dt", CANCEL_CASES)
+def test_norm_near_cancellation(d_out, d_in, r, dt):
+    # Rows with W0_i close to -s (BA)_i: n^2 is a small difference of large
+    # terms, so relative error means nothing there.  Checked: wnorm finite and
+    # >= 0 everywhere, and wnorm^2 within an absolute bound built from the
+    # magnitudes the kernel sums (base, 2|s| sum_j |B_ij| (|W0||A|^T)_ij,
+    # s^2 (|B||G||B|^T)_ii): 2^-8 of it for bf16 (the bf16 rounding of
+    # (s/2) A A^T is 2^-9 relative), 2^-16 for fp32.
+    say(f"[parity] near cancellation {d_out}x{d_in} r={r} {dt}")
+    dtype = DI.DTYPES[dt]
+    g = torch.Generator().manual_seed(d_out + r)
+    s = 1.25
+    A = ((torch.rand(r, d_in, generator=g) * 2 - 1) / d_in ** 0.5).to(dtype)
+    B = (torch.randn(d_out, r, generator=g) * 0.3).to(dtype)
+    BA = B.double() @ A.double()
+    W0 = torch.randn(d_out, d_in, generator=g, dtype=torch.float64) / d_in ** 0.5
+    near = torch.arange(d_out) % 2 == 0
+    W0[near] = -s * BA[near] + 1e-3 * W0[near]
+    W0 = W0.to(dtype)
+    wn, _ = D.factored_norm(W0.to(DEV), A.to(DEV), B.to(DEV), s)
+    torch.cuda.synchronize()
+    got = host64(wn)
+    assert np.all(np.isfinite(got)) and np.all(got >= 0)
+    W0d, Ad, Bd = (oracle.as_f64(t) for t in (W0, A, B))
+    ref = oracle.dense_row_norm(W0, A, B, s)
+    base = np.sum(W0d * W0d, axis=1)
+    cross_abs = np.sum(np.abs(Bd) * (np.abs(W0d) @ np.abs(Ad).T), axis=1)
+    G = Ad @ Ad.T
+    gram_abs = np.sum((np.abs(Bd) @ np.abs(G)) * np.abs(Bd), axis=1)
+    scale = base + 2 * abs(s) * cross_abs + s * s * gram_abs
+    u = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -16
+    err = np.abs(got ** 2 - ref ** 2)
+    assert np.all(err <= u * scale), (float(np.max(err / scale)), u)
+    # the cancelling rows really are small against their terms
+    assert np.max(ref[near.numpy()] ** 2 / scale[near.numpy()]) < 1e-2
+
+
 def test_norm_deterministic():
     L = config_layer(3)
     say("[parity] norm determinism")
