@@ -654,145 +654,6 @@ __device__ __forceinline__ void mainloop_w0_narrow(const Contraction& c, int64_t
     }
 }
 
-// W0 pass main loop, wide form with the right operand in registers.  The
-// left operand (W0, then B) is shared by the WN waves of the workgroup and
-// goes global -> LDS by DMA into a ring of LS = P + 2 stages; each wave loads
-// the right-operand fragments it alone uses (its NT blocks of A, then Gs)
-// straight into registers in MFMA operand layout, P tiles ahead.  Only the
-// left tile crosses LDS, which halves LDS traffic per k-tile compared with
-// staging both operands.  Per step a wave issues right(j + P), then
-// left(j + P + 1): vector-memory loads complete in issue order, so waiting for
-// right(j) also covers left(j) (issued one step earlier) while left(j + 1)
-// and the later steps stay in flight.  Per k-tile j:
-//   wait for this wave's loads of tile j, barrier (every wave's DMA share of
-//   left(j) landed, and the stage of tile j-1 is free), enqueue right(j + P)
-//   and left(j + P + 1), MFMA over tile j.
-// The K walk is rotated as in mainloop_dma; the base term is summed from the
-// left fragments.
-template <typename E, int WN, int MT, int NT, int P>
-__device__ __forceinline__ void mainloop_adirect(const Contraction& c, int64_t m0, int64_t n0, int kt_begin,
-                                                 int kt_end, int rot, float* base_dst, int64_t d_out,
-                                                 f32x4_t (&acc)[MT][NT], char* smem) {
-    typedef Tile<E, 1, WN, MT, NT> TL;
-    typedef Mma<E> M;
-    constexpr int LS = P + 2;
-    constexpr int FR = M::BK / 32, FL = M::FL;
-    constexpr int NRW = FR * NT * FL;   // right loads per wave per tile
-    constexpr int LPW = TL::LPW;        // left DMA instructions per wave per tile
-    constexpr int TKB = TL::BK * (int)sizeof(E);
-    static_assert(TL::NW % 2 == 0, "DMA lane offsets assume an even wave count");
-    static_assert(LPW + (P - 1) * (NRW + LPW) < 64, "vmcnt range");
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wn = wave;
-    const int q = lane >> 4;
-    const int n = kt_end - kt_begin;
-    if (n <= 0) {
-        // an empty K-chunk still owns its base partials
-        if (base_dst)
-            for (int mt = wn; mt < MT; mt += WN) {
-                const int64_t m = m0 + mt * 16 + lane;
-                if (lane < 16 && m < d_out) base_dst[m] = 0.0f;
-            }
-        return;
-    }
-
-    const DmaSrc L0 = make_dma_src<E>(c.left0, m0, lane);
-    const DmaSrc L1 = make_dma_src<E>(c.left1, m0, lane);
-    const FragSrc R0 = make_frag_src<E>(c.right0, n0 + wn * NT * 16, lane);
-    const FragSrc R1 = make_frag_src<E>(c.right1, n0 + wn * NT * 16, lane);
-
-    int lrow[MT], lsw[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        lrow[mt] = mt * 16 + (lane & 15);
-        lsw[mt] = swz(lrow[mt]);
-    }
-    float bs[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) bs[mt] = 0.0f;
-
-    auto tile = [&](int i) __attribute__((always_inline)) {
-        int t = i + rot;
-        if (t >= n) t -= n;
-        return kt_begin + t;
-    };
-    auto issue_left = [&](int i) __attribute__((always_inline)) {
-        const int kt = tile(i);
-        char* dst = smem + (i % LS) * TL::LBYTES;
-        if (kt < c.nkt0)
-            dma_tile<TL::BM, 0, TL::NW>(L0, kt * TKB, dst, wave, TKB);
-        else
-            dma_tile<TL::BM, 0, TL::NW>(L1, (kt - c.nkt0) * TKB, dst, wave, TKB);
-    };
-    auto issue_right = [&](int i, u32x4_t* regs) __attribute__((always_inline)) {
-        const int kt = tile(i);
-        if (kt < c.nkt0)
-            load_frags<E, NT>(R0, (int64_t)kt * M::BK, regs);
-        else
-            load_frags<E, NT>(R1, (int64_t)(kt - c.nkt0) * M::BK, regs);
-    };
-    auto compute = [&](int i, const u32x4_t* regs) __attribute__((always_inline)) {
-        const char* Lt = smem + (i % LS) * TL::LBYTES;
-        const bool base = base_dst != nullptr && tile(i) < c.nkt0;
-#pragma unroll
-        for (int ks = 0; ks < FR; ++ks) {
-            typename M::frag_t a[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) a[mt] = M::load_frag_swz(Lt + lrow[mt] * 128, ks, q, lsw[mt]);
-            if (base) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    if (mt % WN == wn) bs[mt] += M::frag_sumsq(a[mt]);
-            }
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const typename M::frag_t b = M::frag_from_regs(regs + (ks * NT + nt) * FL);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) M::mma(acc[mt][nt], a[mt], b);
-            }
-        }
-    };
-    // one step; cur holds right(i), nxt receives right(i + P)
-    auto step = [&](int i, const u32x4_t* cur, u32x4_t* nxt) __attribute__((always_inline)) {
-        if (i + P < n)
-            wait_vmcnt<LPW + (P - 1) * (NRW + LPW)>();
-        else
-            wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        if (i + P < n) issue_right(i + P, nxt);
-        if (i + P + 1 < n) issue_left(i + P + 1);
-        compute(i, cur);
-    };
-
-    static_assert(P == 2, "register sets are rotated three ways");
-    u32x4_t s0[NRW], s1[NRW], s2[NRW];
-    issue_left(0);
-    issue_right(0, s0);
-    if (n > 1) issue_left(1);
-    if (n > 1) issue_right(1, s1);
-    if (n > 2) issue_left(2);
-    for (int i = 0; i < n; i += 3) {
-        step(i, s0, s2);
-        if (i + 1 >= n) break;
-        step(i + 1, s1, s0);
-        if (i + 2 >= n) break;
-        step(i + 2, s2, s1);
-    }
-    __builtin_amdgcn_s_barrier();   // LDS is free for the caller's epilogue
-    if (base_dst) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            if (mt % WN != wn) continue;
-            float v = bs[mt];
-            v += __shfl_xor(v, 16);
-            v += __shfl_xor(v, 32);
-            const int64_t m = m0 + mt * 16 + lane;
-            if (lane < 16 && m < d_out) base_dst[m] = v;
-        }
-    }
-}
-
 template <typename E, int WM, int WN, int MT, int NT, bool ALIGNED>
 __device__ __forceinline__ void mainloop(const Contraction& c, int64_t m0, int64_t n0, int kt_begin, int kt_end,
                                          int rot, float* base_dst, int64_t d_out, f32x4_t (&acc)[MT][NT],
@@ -832,11 +693,7 @@ __global__ __launch_bounds__(WM * WN * 64) void w0_pass(W0PassArgs a) {
     constexpr int B_PITCH = B_SLOTS * 16;
     constexpr int B_BYTES = ALIGNED ? TL::BM * B_PITCH : 0;
     constexpr int EPI = B_BYTES + RED_BYTES;
-#ifdef DORA_W0_ADIRECT
-    constexpr int WIDE_BYTES = 4 * TL::LBYTES;
-#else
     constexpr int WIDE_BYTES = TL::DMA_BYTES;
-#endif
     constexpr int MAIN = F::WIDE ? WIDE_BYTES : (F::NARROW ? 0 : TL::STAGED_BYTES);
     __shared__ __attribute__((aligned(1024))) char smem[MAIN > EPI ? MAIN : EPI];
 
@@ -874,11 +731,7 @@ __global__ __launch_bounds__(WM * WN * 64) void w0_pass(W0PassArgs a) {
     const int nk = kt_end - kt_begin;
     const int rot = nk > 0 ? (int)(((unsigned)id * 7u + ((unsigned)id >> 3) * 3u) % (unsigned)nk) : 0;
     if constexpr (F::WIDE)
-#ifdef DORA_W0_ADIRECT
-        mainloop_adirect<E, WN, MT, NT, 2>(a.c, m0, n0, kt_begin, kt_end, rot, base_dst, a.d_out, acc, smem);
-#else
         mainloop_dma<E, WM, WN, MT, NT, false>(a.c, m0, n0, kt_begin, kt_end, rot, base_dst, a.d_out, acc, smem);
-#endif
     else if constexpr (F::NARROW)
         mainloop_w0_narrow<E, MT, NT>(a.c, m0, n0, kt_begin, kt_end, rot, base_dst, a.d_out, acc);
     else
@@ -1752,11 +1605,7 @@ constexpr TileCfg kCfgs[] = {
     {4, 1, 2, 4},    // narrow, BM 128, BN 64
     {1, 4, 8, 2},    // wide,   BM 128, BN 128
     {1, 4, 8, 3},    // wide,   BM 128, BN 192
-#ifdef DORA_W0_WN8
-    {1, 8, 8, 3},    // wide,   BM 128, BN 384, 8 waves
-#else
     {1, 4, 8, 6},    // wide,   BM 128, BN 384
-#endif
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
