@@ -1021,7 +1021,12 @@ __device__ __forceinline__ void w0_pass_big_body(const W0PassArgs& a, const int 
 #pragma unroll
             for (int nt = 0; nt < G::NT; ++nt) bv[nt] = *reinterpret_cast<const bf16x8_t*>(Rt + nt * 32 * G::ROWB);
         };
-        // MFMAs over blocks (mt, nt) with lo <= mt * NT + nt < hi
+        // MFMAs over blocks (mt, nt) with lo <= mt * NT + nt < hi.  The right
+        // fragments go in the A slot and the left ones in the B slot, so each
+        // accumulator block holds U^T: lane l carries row l % 32 of the left
+        // block and register e column 8 (e / 4) + 4 (l / 32) + e % 4 of the
+        // right block (runs of 4 consecutive columns, read as one 8-byte load
+        // of B in the epilogue).
         auto mma = [&](const bf16x8_t (&av)[G::MT], const bf16x8_t (&bv)[G::NT], int lo, int hi)
             __attribute__((always_inline)) {
 #pragma unroll
@@ -1030,7 +1035,7 @@ __device__ __forceinline__ void w0_pass_big_body(const W0PassArgs& a, const int 
                 for (int nt = 0; nt < G::NT; ++nt) {
                     const int k = mt * G::NT + nt;
                     if (k < lo || k >= hi) continue;
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[nt], av[mt], acc[mt][nt], 0, 0, 0);
                 }
             }
         };
@@ -1115,13 +1120,14 @@ __device__ __forceinline__ void w0_pass_big_body(const W0PassArgs& a, const int 
     // block wn of this wave's 128 rows
     const float base_part = bs + __shfl_xor(bs, 32);   // row l % 32 of block wn, lanes < 32
 
-    // cross partial: sum_n B[m][n] acc[m][n] over this workgroup's columns.
-    // acc[mt][nt][e] is row mt*32 + 8 (e/4) + 4 (l/32) + e%4 of the wave's
-    // 128 rows and column nt*32 + l%32 of its 96.  Round mt handles row block
-    // mt of both row halves (64 rows): its B rows are staged in LDS (double
-    // buffered, the next round's DMA overlaps this round's dots), every wave
-    // dots its accumulators with them, sums each row over its 32 lanes, and
-    // the four column waves' partials are added in order.
+    // cross partial: sum_n B[m][n] U[m][n] over this workgroup's columns.
+    // acc[mt][nt][e] is U at row mt*32 + l%32 of the wave's 128 rows and
+    // column nt*32 + 8 (e/4) + 4 (l/32) + e%4 of its 96.  Round mt handles row
+    // block mt of both row halves (64 rows): its B rows are staged in LDS
+    // (double buffered, the next round's DMA overlaps this round's dots);
+    // every lane dots its row with 4-column runs of B (one 8-byte read each),
+    // adds the other half-wave's columns of the same row, and the four column
+    // waves' partials are added in order.
     {
         const int64_t rb = a.r * 2;
         const int colb0 = (int)(n0 * 2);
@@ -1155,53 +1161,28 @@ __device__ __forceinline__ void w0_pass_big_body(const W0PassArgs& a, const int 
             }
         };
         stage_b(0, smem);
+        const int srow = wm * 32 + (lane & 31);               // this lane's staged row
+        const int colh = 4 * (lane >> 5);                      // its column offset in a run of 8
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt) {
             wait_vmcnt<0>();
             __syncthreads();   // round mt's B landed; round mt - 1's readers are done
             if (mt + 1 < G::MT) stage_b(mt + 1, smem + ((mt + 1) & 1) * EBUF);
-            const char* buf = smem + (mt & 1) * EBUF;
-            float v[16];
+            const bf16_t* brow =
+                reinterpret_cast<const bf16_t*>(smem + (mt & 1) * EBUF + srow * G::EB_PITCH) + wn * 96 + colh;
+            float x = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                const bf16_t* brow = reinterpret_cast<const bf16_t*>(buf + row * G::EB_PITCH) + wn * 96 + (lane & 31);
-                float x = 0.0f;
+            for (int nt = 0; nt < G::NT; ++nt) {
 #pragma unroll
-                for (int nt = 0; nt < G::NT; ++nt) x = fmaf(static_cast<float>(brow[nt * 32]), acc[mt][nt][e], x);
-                v[e] = x;
-            }
-            // sum each row over the 32 lanes that share l / 32, halving the
-            // number of rows a lane carries at every exchange
-            const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+                for (int q = 0; q < 4; ++q) {
+                    typedef bf16_t bf16x4_t __attribute__((ext_vector_type(4)));
+                    const bf16x4_t bq = *reinterpret_cast<const bf16x4_t*>(brow + nt * 32 + 8 * q);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const float send = b4 ? v[q] : v[q + 8];
-                const float keep = b4 ? v[q + 8] : v[q];
-                v[q] = keep + __shfl_xor(send, 16);
+                    for (int c = 0; c < 4; ++c) x = fmaf(static_cast<float>(bq[c]), acc[mt][nt][4 * q + c], x);
+                }
             }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float send = b3 ? v[q] : v[q + 4];
-                const float keep = b3 ? v[q + 4] : v[q];
-                v[q] = keep + __shfl_xor(send, 8);
-            }
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const float send = b2 ? v[q] : v[q + 2];
-                const float keep = b2 ? v[q + 2] : v[q];
-                v[q] = keep + __shfl_xor(send, 4);
-            }
-            {
-                const float send = b1 ? v[0] : v[1];
-                const float keep = b1 ? v[1] : v[0];
-                v[0] = keep + __shfl_xor(send, 2);
-            }
-            v[0] += __shfl_xor(v[0], 1);
-            // lane l now holds the row with e = (l >> 1) & 15
-            const int e = (lane >> 1) & 15;
-            const int row = wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            if ((lane & 1) == 0) red[mt * G::WN * ER + wn * ER + row] = v[0];
+            x += __shfl_xor(x, 32);   // the other half-wave holds the row's other columns
+            if (lane < 32) red[mt * G::WN * ER + wn * ER + srow] = x;
         }
         __syncthreads();
     }
