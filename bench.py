@@ -90,6 +90,20 @@ def norm_source_digest():
     return h.hexdigest()
 
 
+def norm_roofline(flop, nbytes, t, peak_mm, traffic):
+    """The norm call against the roof its arithmetic intensity puts it under:
+    MFMA when FLOP per algorithmic byte is above the ridge (peak FLOP/s over
+    peak HBM bytes/s), HBM otherwise (low rank)."""
+    kernel = "dora_factored_norm (Gram partials, Gram finalize, W0 pass, norm finalize)"
+    if flop / nbytes >= peak_mm * 1e12 / (PEAK_HBM_GBS * 1e9):
+        ach = flop / t / 1e12
+        return {"kernel": kernel, "bound": "mfma", "achieved": round(ach, 2), "peak": peak_mm, "unit": "TFLOP/s",
+                "frac": round(ach / peak_mm, 4), "traffic": traffic}
+    ach = nbytes / t / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic}
+
+
 def stored_traffic(workload):
     """Per-call HBM bytes of the norm, from the committed counter summary for
     this workload, or None when absent or counted on other kernel sources."""
@@ -340,6 +354,7 @@ def main():
         "norm": {"ms": round(t_norm * 1e3, 4), "TFLOPs": round(norm_tflops, 2),
                  "frac_mfma_peak": round(norm_tflops / peak_mm, 4), "algorithmic_flop": F,
                  "algorithmic_bytes": nb, "GBps": round(nb / t_norm / 1e9, 1),
+                 "frac_hbm_peak": round(nb / t_norm / 1e9 / PEAK_HBM_GBS, 4),
                  "workspace_bytes": int(ws_norm.numel())},
         "compose_fwd": {"ms": round(t_fwd * 1e3, 4), "GBps": round(fwd_gbs, 1),
                         "frac_hbm_peak": round(fwd_gbs / PEAK_HBM_GBS, 4),
@@ -356,9 +371,7 @@ def main():
                   "frac_hbm_peak": round(mb / t_merge / 1e9 / PEAK_HBM_GBS, 4), "algorithmic_bytes": mb,
                   "TFLOPs": round(2 * d_out * d_in * r / t_merge / 1e12, 1)},
         "copy_calibration": calib,
-        "roofline": {"kernel": "dora_factored_norm (Gram partials, Gram finalize, W0 pass, norm finalize)",
-                     "bound": "mfma", "achieved": round(norm_tflops, 2), "peak": peak_mm, "unit": "TFLOP/s",
-                     "frac": round(norm_tflops / peak_mm, 4), "traffic": stored_traffic(spec.name)},
+        "roofline": norm_roofline(F, nb, t_norm, peak_mm, stored_traffic(spec.name)),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)

@@ -557,10 +557,12 @@ __device__ __forceinline__ void load_frags(const FragSrc& f, int64_t k0, u32x4_t
 // waves, so both operands are loaded straight into registers, four register
 // sets deep (three tiles in flight), with no LDS and no barrier.  K-walk
 // rotated as in the wide form.
-template <typename E, int MT, int NT>
+// With GIP, the right fragments (rows of A) also feed this K-chunk's Gram
+// blocks G_c = A_c A_c^T: gacc holds the upper blocks (b1 <= b2) in order.
+template <typename E, int MT, int NT, bool GIP, int NG>
 __device__ __forceinline__ void mainloop_w0_narrow(const Contraction& c, int64_t m0, int64_t n0, int kt_begin,
                                                    int kt_end, int rot, float* base_dst, int64_t d_out,
-                                                   f32x4_t (&acc)[MT][NT]) {
+                                                   f32x4_t (&acc)[MT][NT], f32x4_t (&gacc)[NG]) {
     typedef Mma<E> M;
     constexpr int FR = M::BK / 32, FL = M::FL;
     constexpr int NLW = FR * MT * FL, NRW = FR * NT * FL;   // loads per wave per tile
@@ -601,10 +603,10 @@ __device__ __forceinline__ void mainloop_w0_narrow(const Contraction& c, int64_t
             load_frags<E, NT>(R1, (int64_t)(kt - c.nkt0) * M::BK, regs + NLW);
         }
     };
-    auto compute = [&](const u32x4_t* regs, bool base) __attribute__((always_inline)) {
+    auto compute = [&](const u32x4_t* regs, bool base, bool gram) __attribute__((always_inline)) {
 #pragma unroll
         for (int ks = 0; ks < FR; ++ks) {
-            typename M::frag_t a[MT];
+            typename M::frag_t a[MT], b[NT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 a[mt] = M::frag_from_regs(regs + (ks * MT + mt) * FL);
@@ -612,9 +614,18 @@ __device__ __forceinline__ void mainloop_w0_narrow(const Contraction& c, int64_t
             }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const typename M::frag_t b = M::frag_from_regs(regs + NLW + (ks * NT + nt) * FL);
+                b[nt] = M::frag_from_regs(regs + NLW + (ks * NT + nt) * FL);
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) M::mma(acc[mt][nt], a[mt], b);
+                for (int mt = 0; mt < MT; ++mt) M::mma(acc[mt][nt], a[mt], b[nt]);
+            }
+            if constexpr (GIP) {
+                if (gram) {
+                    int q = 0;
+#pragma unroll
+                    for (int b1 = 0; b1 < NT; ++b1)
+#pragma unroll
+                        for (int b2 = b1; b2 < NT; ++b2) M::mma(gacc[q++], b[b1], b[b2]);
+                }
             }
         }
     };
@@ -626,7 +637,8 @@ __device__ __forceinline__ void mainloop_w0_narrow(const Contraction& c, int64_t
         else
             wait_vmcnt<0>();
         if (i + 3 < n) load(i + 3, nxt3);   // set of tile i - 1, already consumed
-        compute(cur, base_dst != nullptr && tile(i) < c.nkt0);
+        const bool ph0 = tile(i) < c.nkt0;
+        compute(cur, base_dst != nullptr && ph0, ph0);
     };
 
     u32x4_t s0[PER], s1[PER], s2[PER], s3[PER];
@@ -673,6 +685,7 @@ struct W0PassArgs {
     int xcd_map;            // workgroups on one XCD share (n-tile, k-chunk)
     float* part_base;       // [ksplit][d_out]
     float* part_cross;      // [n_ntiles * ksplit][d_out]
+    float half_s;           // s / 2, for the Gram term formed inside the pass
 };
 
 template <int WM, int WN, int MT, int NT, bool ALIGNED>
@@ -681,8 +694,27 @@ struct W0Form {
     static constexpr bool NARROW = ALIGNED && WN == 1;
 };
 
+// Narrow bf16 tiles with r <= 32 form the Gram term inside the W0 pass.  The
+// norm's Gram term is a sum over K of per-chunk terms,
+//   B_i G B_i^T = sum_c B_i (A_c A_c^T) B_i^T,
+// so each K-chunk workgroup builds G_c from the A fragments it already
+// holds and adds (s/2) B G_c to its U accumulators before the row dot with
+// B, exactly as the extended contraction adds B Gs with the whole Gram.  No
+// Gram kernels run and the contraction has no Gs k-tiles.
+template <typename E, int WN, int NT, bool ALIGNED>
+struct GramInPass {
+    static constexpr bool value = ALIGNED && WN == 1 && NT <= 2 && sizeof(E) == 2;
+    static constexpr int NG = value ? NT * (NT + 1) / 2 : 1;   // upper 16 x 16 blocks of G_c
+    static constexpr int RP = 32;                               // K of the B Gs product, zero-padded
+    static constexpr int PITCH = RP * 2 + 16;                   // Gs tile row bytes in LDS
+    static constexpr int BYTES = value ? RP * PITCH : 0;
+};
+
+// The narrowest register-fed form (r <= 16) is held to three workgroups per
+// CU (168 VGPRs, no spills): tall projections run several rounds of its
+// workgroups, and with the Gram blocks it would otherwise drop to two.
 template <typename E, int WM, int WN, int MT, int NT, bool ALIGNED>
-__global__ __launch_bounds__(WM * WN * 64) void w0_pass(W0PassArgs a) {
+__global__ __launch_bounds__(WM * WN * 64, (ALIGNED && WN == 1 && NT == 1) ? 3 : 1) void w0_pass(W0PassArgs a) {
     typedef Tile<E, WM, WN, MT, NT> TL;
     typedef W0Form<WM, WN, MT, NT, ALIGNED> F;
     static_assert(!ALIGNED || F::WIDE || F::NARROW, "aligned W0 pass needs the wide or narrow form");
@@ -693,9 +725,11 @@ __global__ __launch_bounds__(WM * WN * 64) void w0_pass(W0PassArgs a) {
     constexpr int B_PITCH = B_SLOTS * 16;
     constexpr int B_BYTES = ALIGNED ? TL::BM * B_PITCH : 0;
     constexpr int EPI = B_BYTES + RED_BYTES;
+    typedef GramInPass<E, WN, NT, ALIGNED> GIP;
+    constexpr int EPI_ALL = EPI + GIP::BYTES;
     constexpr int WIDE_BYTES = TL::DMA_BYTES;
     constexpr int MAIN = F::WIDE ? WIDE_BYTES : (F::NARROW ? 0 : TL::STAGED_BYTES);
-    __shared__ __attribute__((aligned(1024))) char smem[MAIN > EPI ? MAIN : EPI];
+    __shared__ __attribute__((aligned(1024))) char smem[MAIN > EPI_ALL ? MAIN : EPI_ALL];
 
     // Workgroup -> (m-tile, n-tile, k-chunk).  Workgroups are handed to the 8
     // XCDs round-robin; when possible all workgroups of one XCD share the same
@@ -725,6 +759,9 @@ __global__ __launch_bounds__(WM * WN * 64) void w0_pass(W0PassArgs a) {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t gacc[GIP::NG];
+#pragma unroll
+    for (int q = 0; q < GIP::NG; ++q) gacc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     float* base_dst = base_rows ? a.part_base + (int64_t)kc * a.d_out : nullptr;
     // rotated start of the K walk (see mainloop_dma)
@@ -733,7 +770,8 @@ __global__ __launch_bounds__(WM * WN * 64) void w0_pass(W0PassArgs a) {
     if constexpr (F::WIDE)
         mainloop_dma<E, WM, WN, MT, NT, false>(a.c, m0, n0, kt_begin, kt_end, rot, base_dst, a.d_out, acc, smem);
     else if constexpr (F::NARROW)
-        mainloop_w0_narrow<E, MT, NT>(a.c, m0, n0, kt_begin, kt_end, rot, base_dst, a.d_out, acc);
+        mainloop_w0_narrow<E, MT, NT, GIP::value, GIP::NG>(a.c, m0, n0, kt_begin, kt_end, rot, base_dst, a.d_out,
+                                                           acc, gacc);
     else
         mainloop_staged<E, WM, WN, MT, NT>(a.c, m0, n0, kt_begin, kt_end, base_dst, a.d_out, acc, smem);
 
@@ -771,8 +809,48 @@ __global__ __launch_bounds__(WM * WN * 64) void w0_pass(W0PassArgs a) {
                 raw_buffer_load_lds(rs, (lds_void_t*)(smem + ins * 1024), 16, voff, 0, 0, 0);
             }
         }
+        if constexpr (GIP::value) {
+            // wave 0 stores Gs_c = (s/2) G_c as bf16 [RP][RP] (zero past BN)
+            // from its accumulators (every wave holds the same G_c)
+            char* gs = smem + B_BYTES + RED_BYTES;
+            if (wave == 0) {
+                for (int o = lane * 16; o < GIP::BYTES; o += 64 * 16)
+                    *reinterpret_cast<u32x4_t*>(gs + o) = u32x4_t{0u, 0u, 0u, 0u};
+                int q = 0;
+#pragma unroll
+                for (int b1 = 0; b1 < NT; ++b1)
+#pragma unroll
+                    for (int b2 = b1; b2 < NT; ++b2, ++q)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int i = b1 * 16 + 4 * (lane >> 4) + j, k = b2 * 16 + (lane & 15);
+                            const E v = Cvt<E>::from_f(a.half_s * gacc[q][j]);
+                            *reinterpret_cast<E*>(gs + i * GIP::PITCH + k * 2) = v;
+                            if (b1 != b2) *reinterpret_cast<E*>(gs + k * GIP::PITCH + i * 2) = v;
+                        }
+            }
+        }
         wait_vmcnt<0>();
         __syncthreads();
+        if constexpr (GIP::value) {
+            // U += B Gs_c: left fragments are this wave's rows of the staged B
+            // (K = columns of r, zero at and past BN), right fragments rows of Gs_c
+            const char* gs = smem + B_BYTES + RED_BYTES;
+            typedef Mma<E> M;
+            const int kk = 8 * (lane >> 4);
+            typename M::frag_t gf[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                gf[nt] = *reinterpret_cast<const typename M::frag_t*>(gs + (nt * 16 + (lane & 15)) * GIP::PITCH + kk * 2);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int row = wm * MT * 16 + mt * 16 + (lane & 15);
+                typename M::frag_t bf{};
+                if (kk < TL::BN) bf = *reinterpret_cast<const typename M::frag_t*>(smem + row * B_PITCH + kk * 2);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) M::mma(acc[mt][nt], bf, gf[nt]);
+            }
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -1623,6 +1701,15 @@ bool operands_aligned(const NormPlan& p, const void* W0, const void* A, const vo
     return p.d_in % VEC == 0 && p.r % VEC == 0 && al16(W0) && al16(A) && al16(B) && span < (1LL << 30);
 }
 
+// Whether this plan's W0 pass forms the Gram term itself (the kernel-side
+// condition is GramInPass for the same tile configuration).
+template <typename E>
+bool gram_in_pass(const NormPlan& p, bool aligned) {
+    if (p.big || p.cfg < 0) return false;
+    const TileCfg t = kCfgs[p.cfg];
+    return GramInPass<E, 1, 1, true>::value && aligned && t.wn == 1 && t.nt <= 2;
+}
+
 // Arguments and grids of the three stages of one norm (not base-only).
 struct NormLaunch {
     GramArgs ga;
@@ -1677,6 +1764,8 @@ NormLaunch make_norm_launch(const NormPlan& p, bool aligned, const void* W0, con
     wa.xcd_map = (Q <= kNumXCD && kNumXCD % Q == 0) ? 1 : 0;
     wa.part_base = reinterpret_cast<float*>(w + p.off_pbase);
     wa.part_cross = reinterpret_cast<float*>(w + p.off_pcross);
+    wa.half_s = 0.5f * s;
+    if (gram_in_pass<E>(p, aligned)) wa.c.nkt1 = 0;   // no Gs k-tiles: the pass forms the Gram term
     if (wa.xcd_map) {
         const int per = kNumXCD / Q;   // m-tiles per XCD slot
         L.wgrid = kNumXCD * ((p.n_mtiles + per - 1) / per);
@@ -1712,19 +1801,21 @@ hipError_t norm_typed(const NormPlan& p, const void* W0, const void* A, const vo
     if (p.big && !al) return hipErrorInvalidValue;   // the caller runs the fallback plan
     const NormLaunch L = make_norm_launch<E>(p, al, W0, A, B, m, s, eps, wnorm, g, ws);
 
-    // 1. Gs = (s/2) A A^T
-    if (sizeof(E) == 2 && al && p.gram_xcd) {
-        gram_split_bf16<<<L.ggrid, 256, 0, st>>>(L.ga);
-    } else {
-        if (al)
-            gram_partial<E, true><<<L.ggrid, 256, 0, st>>>(L.ga);
-        else
-            gram_partial<E, false><<<L.ggrid, 256, 0, st>>>(L.ga);
+    // 1. Gs = (s/2) A A^T, unless the W0 pass forms the Gram term
+    if (!gram_in_pass<E>(p, al)) {
+        if (sizeof(E) == 2 && al && p.gram_xcd) {
+            gram_split_bf16<<<L.ggrid, 256, 0, st>>>(L.ga);
+        } else {
+            if (al)
+                gram_partial<E, true><<<L.ggrid, 256, 0, st>>>(L.ga);
+            else
+                gram_partial<E, false><<<L.ggrid, 256, 0, st>>>(L.ga);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        gram_finalize<E><<<L.gfgrid, 256, 0, st>>>(L.gf.part, L.gf.nsplit, L.gf.rnp, L.gf.r, L.gf.ldg, L.gf.half_s,
+                                                   static_cast<E*>(L.gf.gs));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    gram_finalize<E><<<L.gfgrid, 256, 0, st>>>(L.gf.part, L.gf.nsplit, L.gf.rnp, L.gf.r, L.gf.ldg, L.gf.half_s,
-                                               static_cast<E*>(L.gf.gs));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
 
     // 2. streaming pass over [W0 | B] x [A | Gs]^T with the row-dot epilogue
     if constexpr (sizeof(E) == 2) {

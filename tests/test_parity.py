@@ -84,6 +84,9 @@ EDGE_SHAPES = [
     (64, 48, 8, "f32"), (64, 48, 8, "bf16"),
     (300, 1000, 384, "bf16"),    # 256-row tiles: ragged rows, K tail inside a 32-wide tile
     (520, 8200, 200, "bf16"),    # 256-row tiles with r < 384 (ragged slice of r)
+    # r <= 32 bf16: the W0 pass forms each K-chunk's Gram term itself
+    (520, 8200, 24, "bf16"),     # eight ragged K-chunks, r below the 32-wide tile
+    (300, 4104, 8, "bf16"),      # rank 8 in a 16-wide tile, ragged rows
 ]
 
 
@@ -115,11 +118,12 @@ def test_norm_unaligned_operands_take_the_fallback_plan():
     check_rel(host64(g), ref_g, NORM_RTOL[L.W0.dtype], "g")
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_norm_dominated_by_low_rank_term(dt):
-    # W0 = 0: the whole norm comes from the cross-free s^2 B G B^T term
-    say(f"[parity] norm W0=0 {dt}")
-    spec = DI.custom_spec(300, 520, 48, 1, dtype=dt, s=2.0, b_std=0.3)
+@pytest.mark.parametrize("dt,r,d_in", [("bf16", 48, 520), ("f32", 48, 520), ("bf16", 16, 4096), ("bf16", 32, 2056)])
+def test_norm_dominated_by_low_rank_term(dt, r, d_in):
+    # W0 = 0: the whole norm comes from the cross-free s^2 B G B^T term (for
+    # bf16 r <= 32 formed per K-chunk inside the W0 pass)
+    say(f"[parity] norm W0=0 {dt} r={r} d_in={d_in}")
+    spec = DI.custom_spec(300, d_in, r, 1, dtype=dt, s=2.0, b_std=0.3)
     L = DI.make_layer(spec, 5, device=DEV, activations=False, w_scale=0.0)
     wn, _ = gpu_norm(L, m=False)
     ref, _ = oracle_norm(L)
