@@ -557,29 +557,24 @@ __device__ __forceinline__ void load_frags(const FragSrc& f, int64_t k0, u32x4_t
 // waves, so both operands are loaded straight into registers, four register
 // sets deep (three tiles in flight), with no LDS and no barrier.  K-walk
 // rotated as in the wide form.
-// With GIP, the right fragments (rows of A) also feed this K-chunk's Gram
+// One wave's rows [mrow0, mrow0 + 16 MT) over k-tiles [kt_begin, kt_end).
+// With GIP, the right fragments (rows of A) also feed this K range's Gram
 // blocks G_c = A_c A_c^T: gacc holds the upper blocks (b1 <= b2) in order.
+// bsum[mt] receives the base partial of row mrow0 + mt * 16 + lane % 16 in
+// every lane (zero without want_base or for an empty range).
 template <typename E, int MT, int NT, bool GIP, int NG>
-__device__ __forceinline__ void mainloop_w0_narrow(const Contraction& c, int64_t m0, int64_t n0, int kt_begin,
-                                                   int kt_end, int rot, float* base_dst, int64_t d_out,
-                                                   f32x4_t (&acc)[MT][NT], f32x4_t (&gacc)[NG]) {
+__device__ __forceinline__ void mainloop_w0_narrow(const Contraction& c, int64_t mrow0, int64_t n0, int kt_begin,
+                                                   int kt_end, int rot, bool want_base, f32x4_t (&acc)[MT][NT],
+                                                   f32x4_t (&gacc)[NG], float (&bsum)[MT]) {
     typedef Mma<E> M;
     constexpr int FR = M::BK / 32, FL = M::FL;
     constexpr int NLW = FR * MT * FL, NRW = FR * NT * FL;   // loads per wave per tile
     constexpr int PER = NLW + NRW;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = kt_end - kt_begin;
-    const int64_t mrow0 = m0 + wave * MT * 16;
-    if (n <= 0) {
-        // an empty K-chunk still owns its base partials
-        if (base_dst)
-            for (int mt = 0; mt < MT; ++mt) {
-                const int64_t m = mrow0 + mt * 16 + lane;
-                if (lane < 16 && m < d_out) base_dst[m] = 0.0f;
-            }
-        return;
-    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) bsum[mt] = 0.0f;
+    if (n <= 0) return;
     const FragSrc L0 = make_frag_src<E>(c.left0, mrow0, lane);
     const FragSrc L1 = make_frag_src<E>(c.left1, mrow0, lane);
     const FragSrc R0 = make_frag_src<E>(c.right0, n0, lane);
@@ -638,7 +633,7 @@ __device__ __forceinline__ void mainloop_w0_narrow(const Contraction& c, int64_t
             wait_vmcnt<0>();
         if (i + 3 < n) load(i + 3, nxt3);   // set of tile i - 1, already consumed
         const bool ph0 = tile(i) < c.nkt0;
-        compute(cur, base_dst != nullptr && ph0, ph0);
+        compute(cur, want_base && ph0, ph0);
     };
 
     u32x4_t s0[PER], s1[PER], s2[PER], s3[PER];
@@ -654,14 +649,13 @@ __device__ __forceinline__ void mainloop_w0_narrow(const Contraction& c, int64_t
         if (i + 3 >= n) break;
         step(i + 3, s3, s2);
     }
-    if (base_dst) {
+    if (want_base) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             float v = bs[mt];
             v += __shfl_xor(v, 16);
             v += __shfl_xor(v, 32);
-            const int64_t m = mrow0 + mt * 16 + lane;
-            if (lane < 16 && m < d_out) base_dst[m] = v;
+            bsum[mt] = v;
         }
     }
 }
@@ -769,9 +763,20 @@ __global__ __launch_bounds__(WM * WN * 64, (ALIGNED && WN == 1 && NT == 1) ? 3 :
     const int rot = nk > 0 ? (int)(((unsigned)id * 7u + ((unsigned)id >> 3) * 3u) % (unsigned)nk) : 0;
     if constexpr (F::WIDE)
         mainloop_dma<E, WM, WN, MT, NT, false>(a.c, m0, n0, kt_begin, kt_end, rot, base_dst, a.d_out, acc, smem);
-    else if constexpr (F::NARROW)
-        mainloop_w0_narrow<E, MT, NT, GIP::value, GIP::NG>(a.c, m0, n0, kt_begin, kt_end, rot, base_dst, a.d_out,
-                                                           acc, gacc);
+    else if constexpr (F::NARROW) {
+        const int64_t mrow0 = m0 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * MT * 16;
+        float bsum[MT];
+        mainloop_w0_narrow<E, MT, NT, GIP::value, GIP::NG>(a.c, mrow0, n0, kt_begin, kt_end, rot,
+                                                           base_dst != nullptr, acc, gacc, bsum);
+        if (base_dst) {
+            const int lane = threadIdx.x & 63;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int64_t m = mrow0 + mt * 16 + lane;
+                if (lane < 16 && m < a.d_out) base_dst[m] = bsum[mt];
+            }
+        }
+    }
     else
         mainloop_staged<E, WM, WN, MT, NT>(a.c, m0, n0, kt_begin, kt_end, base_dst, a.d_out, acc, smem);
 
@@ -899,6 +904,147 @@ __global__ __launch_bounds__(WM * WN * 64, (ALIGNED && WN == 1 && NT == 1) ? 3 :
 #pragma unroll
             for (int w = 1; w < WN; ++w) v += red[w * TL::BM + row];
             a.part_cross[((int64_t)ntile * a.ksplit + kc) * a.d_out + m] = v;
+        }
+    }
+}
+
+// ------------------------------------------------------------- W0 pass, whole rows (low rank)
+// bf16, 16-byte aligned operands, r <= 32.  A workgroup owns 16 whole rows
+// of W0 and its four waves split K four ways: each runs the narrow
+// register-fed loop over its K range (U, base and Gram blocks of that range,
+// whose Gram term is a sum over K ranges like any other K split), adds
+// (s/2) B G_w to its U accumulators and takes the row dots with B.  The
+// workgroup then adds the waves' base and cross partials in wave order in
+// LDS and writes wnorm and g itself: no partials leave the workgroup and no
+// assembly kernel runs.
+struct W0RowsArgs {
+    Contraction c;        // left0 = W0, right0 = A; no second phase
+    const void* B;        // [d_out, r]
+    const float* m;       // [d_out] or null
+    int64_t d_out, r;
+    float half_s, two_s, eps;
+    float* wnorm;
+    float* g;
+};
+
+constexpr int kRowsWaves = 4;
+constexpr int kRowsPerWg = 16;
+
+template <int NT>
+__global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) {
+    typedef bf16_t E;
+    typedef Mma<E> M;
+    typedef GramInPass<E, 1, NT, true> GIP;
+    static_assert(GIP::value, "the whole-row form forms the Gram term in the pass");
+    constexpr int BN = NT * 16;
+    constexpr int B_SLOTS = BN * 2 / 16 + 1;                      // 16-byte slots per staged B row (+1 zero pad)
+    constexpr int B_PITCH = B_SLOTS * 16;
+    constexpr int B_NINS = (kRowsPerWg * B_SLOTS + 63) / 64;      // DMA instructions staging B
+    constexpr int GS_OFF = B_NINS * 1024;                         // the DMA fills whole 1 KiB blocks
+    constexpr int RED_OFF = GS_OFF + kRowsWaves * GIP::BYTES;
+    constexpr int LDS = RED_OFF + 2 * kRowsWaves * kRowsPerWg * 4;
+    __shared__ __attribute__((aligned(1024))) char smem[LDS];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t m0 = (int64_t)blockIdx.x * kRowsPerWg;
+    const int nkt = a.c.nkt0;
+    const int kt_begin = (int)((int64_t)wave * nkt / kRowsWaves);
+    const int kt_end = (int)((int64_t)(wave + 1) * nkt / kRowsWaves);
+
+    f32x4_t acc[1][NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[0][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t gacc[GIP::NG];
+#pragma unroll
+    for (int q = 0; q < GIP::NG; ++q) gacc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float bsum[1];
+    mainloop_w0_narrow<E, 1, NT, true, GIP::NG>(a.c, m0, 0, kt_begin, kt_end, 0, true, acc, gacc, bsum);
+
+    // B rows [m0, m0 + 16), columns [0, BN) (zeros past r and past d_out)
+    if (wave == 0) {
+        const int64_t rb = a.r * 2;
+        const uint64_t addr = reinterpret_cast<uint64_t>(static_cast<const char*>(a.B) + m0 * rb);
+        int64_t bytes = (a.d_out - m0) * rb;
+        if (bytes > 0x7ffffff0) bytes = 0x7ffffff0;
+        i32x4_t rs;
+        rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+        rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32));
+        rs[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+        rs[3] = 0x00020000;
+#pragma unroll
+        for (int ins = 0; ins < B_NINS; ++ins) {
+            const int slot = ins * 64 + lane;
+            const int row = slot / B_SLOTS, ch = slot % B_SLOTS;
+            const int colb = ch * 16;
+            const bool ok = ch < B_SLOTS - 1 && row < kRowsPerWg && colb < (int)rb;
+            const int voff = ok ? row * (int)rb + colb : kOutOfRange;
+            raw_buffer_load_lds(rs, (lds_void_t*)(smem + ins * 1024), 16, voff, 0, 0, 0);
+        }
+    }
+    // this wave's Gs_w = (s/2) G_w as bf16 [RP][RP], zero past BN
+    {
+        char* gs = smem + GS_OFF + wave * GIP::BYTES;
+        for (int o = lane * 16; o < GIP::BYTES; o += 64 * 16)
+            *reinterpret_cast<u32x4_t*>(gs + o) = u32x4_t{0u, 0u, 0u, 0u};
+        int q = 0;
+#pragma unroll
+        for (int b1 = 0; b1 < NT; ++b1)
+#pragma unroll
+            for (int b2 = b1; b2 < NT; ++b2, ++q)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = b1 * 16 + 4 * (lane >> 4) + j, k = b2 * 16 + (lane & 15);
+                    const E v = Cvt<E>::from_f(a.half_s * gacc[q][j]);
+                    *reinterpret_cast<E*>(gs + i * GIP::PITCH + k * 2) = v;
+                    if (b1 != b2) *reinterpret_cast<E*>(gs + k * GIP::PITCH + i * 2) = v;
+                }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    // U_w += B Gs_w, then the row dots with B
+    {
+        const char* gs = smem + GS_OFF + wave * GIP::BYTES;
+        const int kk = 8 * (lane >> 4);
+        typename M::frag_t bf{};
+        if (kk < BN) bf = *reinterpret_cast<const typename M::frag_t*>(smem + (lane & 15) * B_PITCH + kk * 2);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const typename M::frag_t gf =
+                *reinterpret_cast<const typename M::frag_t*>(gs + (nt * 16 + (lane & 15)) * GIP::PITCH + kk * 2);
+            M::mma(acc[0][nt], bf, gf);
+        }
+    }
+    float* red = reinterpret_cast<float*>(smem + RED_OFF);   // [2][waves][16]: base, cross
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = 4 * (lane >> 4) + j;
+        const E* brow = reinterpret_cast<const E*>(smem + row * B_PITCH) + (lane & 15);
+        float v = 0.0f;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) v = fmaf(Cvt<E>::to_f(brow[nt * 16]), acc[0][nt][j], v);
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 8);
+        if ((lane & 15) == 0) red[(kRowsWaves + wave) * kRowsPerWg + row] = v;
+    }
+    if (lane < kRowsPerWg) red[wave * kRowsPerWg + lane] = bsum[0];
+    __syncthreads();
+    if (threadIdx.x < kRowsPerWg) {
+        const int row = threadIdx.x;
+        const int64_t i = m0 + row;
+        if (i < a.d_out) {
+            float base = red[row], cd = red[kRowsWaves * kRowsPerWg + row];
+#pragma unroll
+            for (int w = 1; w < kRowsWaves; ++w) {
+                base += red[w * kRowsPerWg + row];
+                cd += red[(kRowsWaves + w) * kRowsPerWg + row];
+            }
+            const float n2 = fmaxf(fmaf(a.two_s, cd, base), 0.0f);
+            const float wn = sqrtf(n2);
+            a.wnorm[i] = wn;
+            if (a.m) a.g[i] = a.m[i] / fmaxf(wn, a.eps);
         }
     }
 }
@@ -1710,6 +1856,21 @@ bool gram_in_pass(const NormPlan& p, bool aligned) {
     return GramInPass<E, 1, 1, true>::value && aligned && t.wn == 1 && t.nt <= 2;
 }
 
+// Whether the norm runs as the single whole-row kernel (w0_rows_narrow).
+// Measured on MI355X at r <= 32: up to 2^25 W0 elements (4096 x 8192,
+// 16384 x 2048, ...) it beats the K-split pass plus assembly by 10-25%; at
+// 6144^2 they tie, and from 8192^2 up the K-split pass is faster (its
+// 128-row workgroups keep more bytes in flight than 16-row ones).
+constexpr int64_t kRowsFormMaxElems = int64_t(1) << 25;
+
+template <typename E>
+bool rows_form(const NormPlan& p, bool aligned) {
+#ifdef DORA_NO_ROWS_FORM
+    return false;   // tile sweeps only
+#endif
+    return gram_in_pass<E>(p, aligned) && p.d_out * p.d_in <= kRowsFormMaxElems;
+}
+
 // Arguments and grids of the three stages of one norm (not base-only).
 struct NormLaunch {
     GramArgs ga;
@@ -1799,6 +1960,31 @@ hipError_t norm_typed(const NormPlan& p, const void* W0, const void* A, const vo
     }
     const bool al = operands_aligned<E>(p, W0, A, B);
     if (p.big && !al) return hipErrorInvalidValue;   // the caller runs the fallback plan
+    if (rows_form<E>(p, al)) {
+        if constexpr (sizeof(E) == 2) {
+            W0RowsArgs ra;
+            ra.c.left0 = Operand{W0, d_in, d_out, d_in};
+            ra.c.right0 = Operand{A, d_in, r, d_in};
+            ra.c.left1 = ra.c.right1 = Operand{nullptr, 0, 0, 0};
+            ra.c.nkt0 = p.nkt_w0;
+            ra.c.nkt1 = 0;
+            ra.B = B;
+            ra.m = m;
+            ra.d_out = d_out;
+            ra.r = r;
+            ra.half_s = 0.5f * s;
+            ra.two_s = 2.0f * s;
+            ra.eps = eps;
+            ra.wnorm = wnorm;
+            ra.g = g;
+            const unsigned grid = (unsigned)((d_out + kRowsPerWg - 1) / kRowsPerWg);
+            if (kCfgs[p.cfg].nt == 1)
+                w0_rows_narrow<1><<<grid, kRowsWaves * 64, 0, st>>>(ra);
+            else
+                w0_rows_narrow<2><<<grid, kRowsWaves * 64, 0, st>>>(ra);
+            return hipGetLastError();
+        }
+    }
     const NormLaunch L = make_norm_launch<E>(p, al, W0, A, B, m, s, eps, wnorm, g, ws);
 
     // 1. Gs = (s/2) A A^T, unless the W0 pass forms the Gram term

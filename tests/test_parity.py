@@ -101,6 +101,22 @@ def test_norm_edge_shapes(d_out, d_in, r, dt):
     check_rel(host64(g), ref_g, NORM_RTOL[L.W0.dtype], "g")
 
 
+@pytest.mark.parametrize("d_out,d_in,r", [(4096, 8192, 16), (4100, 8200, 16), (8192, 4104, 24)])
+def test_norm_low_rank_forms_at_scale(d_out, d_in, r):
+    # bf16 r <= 32: up to 2^25 W0 elements (4096 x 8192) one whole-row kernel
+    # assembles wnorm and g; above it the K-split W0 pass (each K-chunk's
+    # Gram term formed in the pass) and the assembly kernel run.  Sampled rows.
+    say(f"[parity] low-rank norm {d_out}x{d_in} r={r}")
+    spec = DI.custom_spec(d_out, d_in, r, 1, dtype="bf16", s=1.5, b_std=0.05)
+    L = DI.make_layer(spec, 60 + r + d_out % 7, device=DEV, activations=False, gen_device="cuda")
+    wn, g = gpu_norm(L)
+    rows = sample_rows(d_out, 256, seed=r)
+    ref_wn, ref_g = oracle_norm(L, rows)
+    assert np.all(np.isfinite(host64(wn))) and np.all(host64(wn) > 0)
+    check_rel(host64(wn)[rows], ref_wn, NORM_RTOL[L.W0.dtype], "wnorm")
+    check_rel(host64(g)[rows], ref_g, NORM_RTOL[L.W0.dtype], "g")
+
+
 def test_norm_unaligned_operands_take_the_fallback_plan():
     # a W0 that is not 16-byte aligned cannot use the LDS-DMA tiles; the call
     # runs the register-staged plan inside the same workspace size
