@@ -2196,18 +2196,37 @@ hipError_t launch_norm_group(int n, const NormMember* mem, int64_t d_in, int64_t
     gg.n = gf.n = gw.n = gn.n = n;
     gg.start[0] = gf.start[0] = gw.start[0] = gn.start[0] = 0;
     auto pad8 = [](int x) { return (x + kNumXCD - 1) / kNumXCD * kNumXCD; };
+    NormLaunch L[kMaxNormGroup];
     for (int j = 0; j < n; ++j) {
         const NormMember& M = mem[j];
-        const NormLaunch L = make_norm_launch<bf16_t>(plans[j], true, M.W0, M.A, M.B, M.m, M.s, eps, M.wnorm, M.g,
-                                                      wsj[j]);
-        gg.a[j] = L.ga;
-        gg.start[j + 1] = gg.start[j] + pad8((int)L.ggrid);
-        gf.a[j] = L.gf;
-        gf.start[j + 1] = gf.start[j] + (int)L.gfgrid;
-        gw.a[j] = L.wa;
-        gw.start[j + 1] = gw.start[j] + pad8(L.wgrid);
-        gn.a[j] = L.nf;
-        gn.start[j + 1] = gn.start[j] + (int)L.nfgrid;
+        L[j] = make_norm_launch<bf16_t>(plans[j], true, M.W0, M.A, M.B, M.m, M.s, eps, M.wnorm, M.g, wsj[j]);
+        gg.a[j] = L[j].ga;
+        gg.start[j + 1] = gg.start[j] + pad8((int)L[j].ggrid);
+        gf.a[j] = L[j].gf;
+        gf.start[j + 1] = gf.start[j] + (int)L[j].gfgrid;
+        gn.a[j] = L[j].nf;
+        gn.start[j + 1] = gn.start[j] + (int)L[j].nfgrid;
+    }
+    // W0 pass: members with the longest workgroups (most k-tiles per K-chunk)
+    // go first, so the short workgroups of the others fill the last round's
+    // idle CUs instead of the long ones running alone at the end.  Each
+    // member keeps its own plan, so its result is unchanged.
+    int ord[kMaxNormGroup];
+    auto kt_per_wg = [&](int j) {
+        const int nkt = plans[j].nkt_w0 + plans[j].nkt_g;
+        return (nkt + plans[j].ksplit - 1) / plans[j].ksplit;
+    };
+    for (int i = 0; i < n; ++i) {
+        int k = i;
+        while (k > 0 && kt_per_wg(ord[k - 1]) < kt_per_wg(i)) {
+            ord[k] = ord[k - 1];
+            --k;
+        }
+        ord[k] = i;
+    }
+    for (int i = 0; i < n; ++i) {
+        gw.a[i] = L[ord[i]].wa;
+        gw.start[i + 1] = gw.start[i] + pad8(L[ord[i]].wgrid);
     }
     hipError_t e;
     gram_split_bf16_group<<<gg.start[n], 256, 0, st>>>(gg);
