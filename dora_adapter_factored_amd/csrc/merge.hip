@@ -346,7 +346,11 @@ __global__ __launch_bounds__(kNTh, 2) void merge_tile(MergeArgs a) {
 constexpr int kRing = 3;
 constexpr int kDmaPerWave = (kBM + kBN) / 16 / (kNTh / 64);
 constexpr int kEpiRows = 64;                              // epilogue in two 64-row halves
-static_assert(kRing * kStageB >= kEpiRows * kEpiPitch * 4, "epilogue half fits in the ring");
+// The DMA kernel's accumulators hold transposed blocks (see merge_tile_dma),
+// so a lane writes four consecutive floats of one row; a pitch of 4 mod 64
+// banks keeps those 16-byte writes free of bank conflicts.
+constexpr int kEpiPitchT = kBN + 4;
+static_assert(kRing * kStageB >= kEpiRows * kEpiPitchT * 4, "epilogue half fits in the ring");
 
 struct DmaOp {
     uint32_t base_lo, base_hi;   // first row of the workgroup's tile
@@ -494,13 +498,16 @@ __global__ __launch_bounds__(kNTh, sizeof(E) == 2 ? 3 : 2) void merge_tile_dma(M
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) MergeMma<E>::mma(acc[i][j], av[i], bv[j]);
+                for (int j = 0; j < 2; ++j) MergeMma<E>::mma(acc[i][j], bv[j], av[i]);
         }
     }
     lds_barrier();   // every wave is done with the ring
 
     // epilogue, one 64-row half at a time: accumulators -> fp32 LDS tile ->
-    // whole 16-byte chunks of W
+    // whole 16-byte chunks of W.  The MFMAs above take A^T's fragment first,
+    // so acc[i][j] is the transposed block: lane l owns row l % 32 of row
+    // block i and, in registers 4g .. 4g + 3, columns 8g + 4 (l / 32) .. + 3
+    // of column block j, one 16-byte LDS write each.
     float* epi = reinterpret_cast<float*>(lds);
     E* W = static_cast<E*>(a.W);
     const float s = a.s;
@@ -512,10 +519,12 @@ __global__ __launch_bounds__(kNTh, sizeof(E) == 2 ? 3 : 2) void merge_tile_dma(M
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int row = i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
-                        const int col = wn * 64 + j * 32 + fr;
-                        epi[row * kEpiPitch + col] = acc[i][j][e];
+                    for (int g = 0; g < 4; ++g) {
+                        const int row = i * 32 + fr;
+                        const int col = wn * 64 + j * 32 + 8 * g + 4 * fh;
+                        *reinterpret_cast<f32x4_t*>(epi + row * kEpiPitchT + col) =
+                            f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                    acc[i][j][4 * g + 3]};
                     }
         }
         lds_barrier();
@@ -525,7 +534,7 @@ __global__ __launch_bounds__(kNTh, sizeof(E) == 2 ? 3 : 2) void merge_tile_dma(M
             const int64_t gm = m0 + h * kEpiRows + row, gn = n0 + (int64_t)cc * VEC;
             if (gm < a.d_out && gn < a.d_in) {
                 const float gi = gv[h * NH + i];
-                const float* src = epi + row * kEpiPitch + cc * VEC;
+                const float* src = epi + row * kEpiPitchT + cc * VEC;
                 Pack<E> w, o;
                 w.u = w0v[h * NH + i];
 #pragma unroll
