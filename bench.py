@@ -209,7 +209,7 @@ def main():
     args.warmup_given = any(a.startswith("--warmup") for a in sys.argv[1:])
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the DoRA norm and compose are "
-              "per-layer kernels; multi-GPU sharding is not part of this build.", file=sys.stderr)
+              "per-layer kernels; sharding them across GPUs is not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import dora_adapter_factored_amd as D

@@ -5,7 +5,7 @@ import torch
 
 import oracle
 
-# Tolerances: norms relative 1e-4 with fp32 inputs, 2e-3 with
+# Tolerances of the workloads' acceptance bar: norms relative 1e-4 with fp32 inputs, 2e-3 with
 # bf16 inputs; bf16 compose outputs and grads |err| <= 2^-7 |ref| + 1e-3;
 # fp32 compose max-abs 1e-4.
 NORM_RTOL = {torch.float32: 1e-4, torch.bfloat16: 2e-3}
