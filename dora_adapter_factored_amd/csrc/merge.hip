@@ -411,7 +411,7 @@ __device__ __forceinline__ void wait_stage(int after, bool w0) {
     }
 }
 
-template <typename E>
+template <typename E, bool DIRECT>
 __global__ __launch_bounds__(kNTh, sizeof(E) == 2 ? 3 : 2) void merge_tile_dma(MergeArgs a) {
     int mt, nt;
     if (!merge_tile_of(a, mt, nt)) return;
@@ -436,6 +436,32 @@ __global__ __launch_bounds__(kNTh, sizeof(E) == 2 ? 3 : 2) void merge_tile_dma(M
 
     auto issue = [&](int kt) {
         char* st = lds + (kt % kRing) * kStageB;
+        if constexpr (DIRECT) {
+            // low rank (r <= 32, one k-tile): the A^T tile is built from A in
+            // place of a transpose launch.  A thread loads a 16-byte run of one
+            // row k of A (8 consecutive columns n) and scatters it into the
+            // swizzled rows n of the stage; rows k >= r give the zero padding.
+#pragma unroll
+            for (int q = 0; q < kDmaPerWave / 2; ++q) dma_group(lop, wave + q * (kNTh / 64), kt, loff, chunk_b, st);
+            constexpr int KT = MergeMma<E>::KT, NCH = kBN / VEC;
+            char* rst = st + kBM * kRowB;
+            const E* A = static_cast<const E*>(a.At);
+#pragma unroll 1
+            for (int c0 = 0; c0 < KT * NCH; c0 += kNTh) {
+                const int c = c0 + tid, k = c / NCH, n8 = (c % NCH) * VEC;
+                const int64_t gn = n0 + n8;
+                Pack<E> v;
+                v.u = (k < a.r && gn < a.d_in) ? *reinterpret_cast<const u32x4_t*>(A + (int64_t)k * a.d_in + gn)
+                                               : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const int nn = n8 + e;
+                    *reinterpret_cast<E*>(rst + nn * kRowB + (((k / VEC) ^ swz64(nn)) << 4) + (k % VEC) * (int)sizeof(E)) =
+                        v.e[e];
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int q = 0; q < kDmaPerWave / 2; ++q) {
             const int grp = wave + q * (kNTh / 64);
@@ -557,7 +583,11 @@ hipError_t merge_typed(const void* W0, const void* A, const void* B, const float
     constexpr int VEC = 16 / sizeof(E);
     auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
     const dim3 tgrid((unsigned)((d_in + kTrTile - 1) / kTrTile), (unsigned)((r_pad + kTrTile - 1) / kTrTile));
-    if (d_in % VEC == 0 && al16(A)) {
+    const bool aligned = d_in % VEC == 0 && r % VEC == 0 && al16(W0) && al16(B) && al16(W);
+    // bf16 with one k-tile of r: the tile kernel stages A^T from A itself
+    const bool a_direct = sizeof(E) == 2 && aligned && al16(A) && r_pad == KT;
+    if (a_direct) {
+    } else if (d_in % VEC == 0 && al16(A)) {
         if constexpr (sizeof(E) == 2)
             transpose_a_bf16<<<tgrid, 256, 0, st>>>(A_bf16(A), r, d_in, reinterpret_cast<bf16_t*>(At), r_pad);
         else
@@ -568,7 +598,7 @@ hipError_t merge_typed(const void* W0, const void* A, const void* B, const float
 
     MergeArgs a;
     a.W0 = W0;
-    a.At = At;
+    a.At = a_direct ? static_cast<const E*>(A) : At;   // merge_tile_dma<E, true> reads A [r][d_in]
     a.B = B;
     a.g = g;
     a.W = W;
@@ -582,11 +612,14 @@ hipError_t merge_typed(const void* W0, const void* A, const void* B, const float
     const int64_t tiles = (int64_t)a.n_mt * a.n_nt;
     a.per_xcd = (int)((tiles + kNumXCD - 1) / kNumXCD);
     const unsigned grid = (unsigned)(a.per_xcd * kNumXCD);
-    const bool aligned = d_in % VEC == 0 && r % VEC == 0 && al16(W0) && al16(B) && al16(W);
-    if (aligned)
-        merge_tile_dma<E><<<grid, kNTh, 0, st>>>(a);
-    else
+    if (a_direct) {
+        if constexpr (sizeof(E) == 2) merge_tile_dma<E, true><<<grid, kNTh, 0, st>>>(a);
+    } else if (aligned) {
+        merge_tile_dma<E, false><<<grid, kNTh, 0, st>>>(a);
+    }
+    else {
         merge_tile<E, false><<<grid, kNTh, 0, st>>>(a);
+    }
     return hipGetLastError();
 }
 
