@@ -134,3 +134,18 @@ def test_merged_weight_serves_the_adapted_layer():
     y_ref = oracle.compose_forward(x64 @ host64(L.W0).T, (x64 @ host64(L.A).T) @ host64(L.B).T, host64(g), 1.0)
     scale = np.abs(x64) @ np.abs(host64(W)).T
     assert np.all(np.abs(y_merged - y_ref) <= 2.0 ** -8 * scale + 1e-6)
+
+
+@pytest.mark.parametrize("r", [8, 16, 32])
+def test_merge_low_rank_stages_A_directly(r):
+    # bf16 with r <= 32: the tile kernel builds its A^T stage from A itself.
+    # An A that is not 16-byte aligned goes through the transpose instead;
+    # the products and their order are the same, so W is bitwise equal.
+    say(f"[merge] low rank r={r}: A staged directly vs transposed")
+    L = DI.make_layer(DI.custom_spec(320, 1032, r, 1, s=1.5, b_std=0.1), 82 + r, device=DEV, activations=False)
+    g = gpu_g(L)
+    W_direct = D.merge(L.W0, L.A, L.B, g, 1.5)
+    W_transposed = D.merge(L.W0, _misaligned(L.A), L.B, g, 1.5)
+    torch.cuda.synchronize()
+    assert torch.equal(W_direct, W_transposed)
+    _check_layer(L, g, W_direct, tag=f"direct r{r}")
