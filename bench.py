@@ -94,7 +94,7 @@ def norm_roofline(flop, nbytes, t, peak_mm, traffic):
     """The norm call against the roof its arithmetic intensity puts it under:
     MFMA when FLOP per algorithmic byte is above the ridge (peak FLOP/s over
     peak HBM bytes/s), HBM otherwise (low rank)."""
-    kernel = "dora_factored_norm (Gram partials, Gram finalize, W0 pass, norm finalize)"
+    kernel = "dora_factored_norm (every kernel of one call)"
     if flop / nbytes >= peak_mm * 1e12 / (PEAK_HBM_GBS * 1e9):
         ach = flop / t / 1e12
         return {"kernel": kernel, "bound": "mfma", "achieved": round(ach, 2), "peak": peak_mm, "unit": "TFLOP/s",
