@@ -446,3 +446,46 @@ def test_sweep_layer_modules():
         check_rel(host64(g)[rows], ref_g, 2e-3, f"{spec.name} g")
         del L
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("d_out,d_in,r", [(1024, 2048, 384), (2048, 4096, 16)])
+def test_graph_capture_replays_match_eager(d_out, d_in, r):
+    # norm, compose forward and backward captured in one HIP graph (the
+    # library records no memsets): every replay, with eager work and a
+    # synchronisation in between, gives bitwise the eager results
+    say(f"[parity] graph capture {d_out}x{d_in} r={r}")
+    L = DI.make_layer(DI.custom_spec(d_out, d_in, r, 256, s=1.0, b_std=0.02), 71 + r, device=DEV)
+    s, eps = L.spec.s, D.default_eps(L.W0.dtype)
+    ws_n = torch.empty(D.norm_workspace_size(d_out, d_in, r, L.W0.dtype), dtype=torch.uint8, device=DEV)
+    ws_b = torch.empty(max(1, D.compose_backward_workspace_size(256, d_out)), dtype=torch.uint8, device=DEV)
+    wn, g = torch.empty(d_out, device=DEV), torch.empty(d_out, device=DEV)
+    y, db, dl = (torch.empty_like(L.base_out) for _ in range(3))
+    dm = torch.empty(d_out, device=DEV)
+
+    def run():
+        D.factored_norm(L.W0, L.A, L.B, s, L.m, eps, wnorm=wn, g=g, ws=ws_n)
+        D.compose(L.base_out, L.lora_out, g, s, out=y)
+        D.compose_backward(L.dy, L.base_out, L.lora_out, g, wn, s, eps, d_base=db, d_lora=dl, d_m=dm, ws=ws_b)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (wn, g, y, db, dl, dm)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    other = DI.make_layer(DI.custom_spec(512, 1024, 64, 1), 72, device=DEV, activations=False)
+    for rep in range(3):
+        for t in (wn, g, y, db, dl, dm):
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, ref, name in zip((wn, g, y, db, dl, dm), eager, ("wnorm", "g", "y", "d_base", "d_lora", "d_m")):
+            assert torch.equal(got, ref), f"replay {rep}: {name}"
+        D.factored_norm(other.W0, other.A, other.B, 1.0, other.m)   # eager work between replays
+        torch.cuda.synchronize()
