@@ -11,7 +11,9 @@
 // bounds the call.  Both MFMA operands must hold K contiguously per lane: B
 // does ([d_out][r] row-major), A does not ([r][d_in]), so transpose_a first
 // writes A^T into the workspace as [d_in][r_pad], zero-padded to whole 64-byte
-// k-tiles (the tail k-tile then needs no masking on that side).
+// k-tiles (the tail k-tile then needs no masking on that side).  With bf16
+// and r <= 32 (one k-tile) the tile kernel builds that A^T tile from A itself
+// and no transpose runs.
 //
 // merge_tile: one workgroup per 128 x 128 output tile, 4 waves (2 x 2), each a
 // 64 x 64 block of 32 x 32 MFMA tiles with fp32 accumulators.  k-tiles of 64
