@@ -9,8 +9,9 @@
 // 2s * B_i . (U_i + B_i Gs) where U = W0 A^T.  U_i + B_i Gs is one GEMM row
 // over the extended contraction [W0_i | B_i] x [A | Gs]^T (K = d_in + r), and
 // its dot with B_i is linear in every K-chunk and every slice of r.  So:
-//   1. gram_partial / gram_finalize: Gs = (s/2) A A^T (MFMA, split-K partial
-//      tiles summed in a fixed order, rounded once to the operand dtype).
+//   1. gram_partial / gram_finalize: Gs = (s/2) A A^T (MFMA, split-K partials
+//      of the upper 64 x 64 tiles summed in a fixed order, rounded once to
+//      the operand dtype).
 //   2. w0_pass: one streaming pass over W0.  Each workgroup owns BM rows of
 //      W0, BN columns of r and a K-chunk of the extended contraction; W0 and A
 //      (then B and Gs) tiles are staged through LDS and fed to MFMA with fp32
@@ -1446,7 +1447,7 @@ struct GramArgs {
     Contraction c;     // left0 = right0 = A
     int ntiles, nsplit, nupper;
     int64_t rnp;       // ntiles * 64
-    float* part;       // [nsplit][rnp][rnp], full symmetric partials
+    float* part;       // [nsplit][rnp][rnp]; only tiles with ti <= tj are written
 };
 
 template <typename E, bool ALIGNED>
@@ -1474,8 +1475,6 @@ __global__ __launch_bounds__(256) void gram_partial(GramArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / 2, wn = wave % 2;
     float* out = a.part + (int64_t)split * a.rnp * a.rnp;
-    // Off-diagonal tiles are also written transposed, so the partial buffer
-    // holds the full symmetric matrix and the finalize reads it row-wise.
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -1485,7 +1484,6 @@ __global__ __launch_bounds__(256) void gram_partial(GramArgs a) {
                 const int64_t i = (int64_t)ti * kGramTile + wm * 32 + mt * 16 + 4 * (lane >> 4) + j;
                 const int64_t k = (int64_t)tj * kGramTile + wn * 32 + nt * 16 + (lane & 15);
                 out[i * a.rnp + k] = acc[mt][nt][j];
-                if (ti != tj) out[k * a.rnp + i] = acc[mt][nt][j];
             }
 }
 
@@ -1593,8 +1591,8 @@ __device__ __forceinline__ void gram_split_bf16_body(const GramArgs& a, const in
         issue_group(grp + 2);
     }
 
-    // Write the partial tile, and its transpose for off-diagonal tiles, as
-    // coalesced 16-byte row segments staged through LDS (the ring is free).
+    // Write the partial tile as coalesced 16-byte row segments staged through
+    // LDS (the ring is free).
     float* tl = reinterpret_cast<float*>(smem);   // [64][TP]
     constexpr int TP = kGramTile + 4;
 #pragma unroll
@@ -1620,42 +1618,75 @@ __device__ __forceinline__ void gram_split_bf16_body(const GramArgs& a, const in
         v[2] = tl[row * TP + c4 + 2];
         v[3] = tl[row * TP + c4 + 3];
         *reinterpret_cast<f32x4_t*>(out + ((int64_t)ti * kGramTile + row) * a.rnp + (int64_t)tj * kGramTile + c4) = v;
-        if (ti != tj) {
-            f32x4_t w;
-            w[0] = tl[(c4 + 0) * TP + row];
-            w[1] = tl[(c4 + 1) * TP + row];
-            w[2] = tl[(c4 + 2) * TP + row];
-            w[3] = tl[(c4 + 3) * TP + row];
-            *reinterpret_cast<f32x4_t*>(out + ((int64_t)tj * kGramTile + row) * a.rnp + (int64_t)ti * kGramTile + c4) = w;
-        }
     }
 }
 
 // Gs[i][j] = (s/2) * sum_split G[i][j] for i < r, j < r; zero for r <= j < ldg.
-// The split partials are summed in split order.
+// The partials hold only the upper 64 x 64 tiles (ti <= tj); G is symmetric,
+// so an element of a lower tile is read at its mirror position.  A workgroup
+// owns kGfRows rows of one 64 x 64 tile of Gs.  A lower tile reads 64 rows of
+// kGfRows columns of its mirror (64-byte pieces) and transposes them through
+// LDS, so reads and writes are both coalesced.  Each element sums its split
+// partials in split order.
+constexpr int kGfRows = 16;
+constexpr int kGfPerTile = kGramTile / kGfRows;
+static_assert(kGfRows * kGramTile == 4 * 256, "four elements per thread");
+
 template <typename E>
 __device__ __forceinline__ void gram_finalize_body(const float* __restrict__ part, int nsplit, int64_t rnp,
                                                    int64_t r, int64_t ldg, float half_s, E* __restrict__ gs,
-                                                   const int64_t idx) {
-    if (idx >= r * ldg) return;
-    const int64_t i = idx / ldg, j = idx % ldg;
-    float v = 0.0f;
-    if (j < r) {
-        const float* p = part + i * rnp + j;
-        const int64_t stride = rnp * rnp;
-        float sum = 0.0f;
-        int sp = 0;
-        for (; sp + 8 <= nsplit; sp += 8) {
-            float x[8];
+                                                   const int id, float (*tr)[kGramTile + 1]) {
+    const int ntiles = (int)(rnp / kGramTile);
+    const int tile = id / kGfPerTile, x0 = (id % kGfPerTile) * kGfRows;
+    const int ti = tile / ntiles, tj = tile % ntiles;
+    const bool mirror = ti > tj;   // uniform over the workgroup
+    const int t = threadIdx.x;
+    const int64_t stride = rnp * rnp;
+    int64_t src[4];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) x[t] = p[(sp + t) * stride];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) sum += x[t];
-        }
-        for (; sp < nsplit; ++sp) sum += p[sp * stride];
-        v = half_s * sum;
+    for (int e = 0; e < 4; ++e) {
+        const int idx = e * 256 + t;
+        if (!mirror)   // row idx / 64 of the block, column idx % 64
+            src[e] = ((int64_t)ti * kGramTile + x0 + idx / kGramTile) * rnp + (int64_t)tj * kGramTile + idx % kGramTile;
+        else           // mirror row idx / 16, column x0 + idx % 16
+            src[e] = ((int64_t)tj * kGramTile + idx / kGfRows) * rnp + (int64_t)ti * kGramTile + x0 + idx % kGfRows;
     }
-    gs[idx] = Cvt<E>::from_f(v);
+    float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int sp = 0; sp < nsplit; sp += 8) {
+        float x[4][8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e][q] = sp + q < nsplit ? part[(int64_t)(sp + q) * stride + src[e]] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (sp + q < nsplit) sum[e] += x[e][q];
+    }
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = half_s * sum[e];
+    if (mirror) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int idx = e * 256 + t;
+            tr[idx % kGfRows][idx / kGfRows] = v[e];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int idx = e * 256 + t;
+            v[e] = tr[idx / kGramTile][idx % kGramTile];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int idx = e * 256 + t;
+        const int64_t i = (int64_t)ti * kGramTile + x0 + idx / kGramTile;
+        const int64_t j = (int64_t)tj * kGramTile + idx % kGramTile;
+        if (i < r && j < ldg) gs[i * ldg + j] = Cvt<E>::from_f(j < r ? v[e] : 0.0f);
+    }
 }
 
 // ------------------------------------------------------------- base only
@@ -1733,7 +1764,8 @@ __global__ __launch_bounds__(256) void gram_split_bf16(GramArgs a) {
 template <typename E>
 __global__ __launch_bounds__(256) void gram_finalize(const float* __restrict__ part, int nsplit, int64_t rnp,
                                                      int64_t r, int64_t ldg, float half_s, E* __restrict__ gs) {
-    gram_finalize_body<E>(part, nsplit, rnp, r, ldg, half_s, gs, (int64_t)blockIdx.x * 256 + threadIdx.x);
+    __shared__ float tr[kGfRows][kGramTile + 1];
+    gram_finalize_body<E>(part, nsplit, rnp, r, ldg, half_s, gs, blockIdx.x, tr);
 }
 
 __global__ __launch_bounds__(256) void norm_finalize(const float* __restrict__ pbase, int nbase,
@@ -1791,10 +1823,11 @@ __global__ __launch_bounds__(256) void gram_split_bf16_group(Group<GramArgs> g) 
 }
 
 __global__ __launch_bounds__(256) void gram_finalize_group(Group<GramFinArgs> g) {
+    __shared__ float tr[kGfRows][kGramTile + 1];
     const int j = group_member(g, blockIdx.x);
     const GramFinArgs& a = g.a[j];
     gram_finalize_body<bf16_t>(a.part, a.nsplit, a.rnp, a.r, a.ldg, a.half_s, static_cast<bf16_t*>(a.gs),
-                               (int64_t)(blockIdx.x - g.start[j]) * 256 + threadIdx.x);
+                               blockIdx.x - g.start[j], tr);
 }
 
 __global__ __launch_bounds__(256) void norm_finalize_group(Group<NormFinArgs> g) {
@@ -1911,7 +1944,7 @@ NormLaunch make_norm_launch(const NormPlan& p, bool aligned, const void* W0, con
     else
         L.ggrid = (unsigned)(ga.nupper * ga.nsplit);
     L.gf = GramFinArgs{gpart, ga.nsplit, ga.rnp, r, p.ldg, 0.5f * s, w + p.off_gs};
-    L.gfgrid = (unsigned)((r * p.ldg + 255) / 256);
+    L.gfgrid = (unsigned)(p.gram_tiles * p.gram_tiles * kGfPerTile);
 
     W0PassArgs& wa = L.wa;
     wa.c.left0 = Operand{W0, d_in, d_out, d_in};
