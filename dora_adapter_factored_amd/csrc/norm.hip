@@ -1490,20 +1490,26 @@ __global__ __launch_bounds__(256) void gram_partial(GramArgs a) {
 // Gram partials for bf16 operands with 16-byte aligned rows.  Split s of the
 // K range runs on XCD s % 8 (workgroup ids are dealt to XCDs round-robin), so
 // each XCD streams only its own K-slices of A and the whole of A crosses HBM
-// once.  Each workgroup walks its slice through an LDS ring of kGramStages
-// stages (left and right 64-row tiles), kGramStages - 1 tiles ahead.
-constexpr int kGramStages = 8;
+// once.  Each workgroup walks its slice through an LDS ring of NS stages
+// (left and right 64-row tiles, 16 KB a stage), NS - 1 tiles ahead.  A single
+// call runs one round of workgroups and uses 8 stages; a group's Gram runs
+// several members' workgroups and uses 4, so that two workgroups share a CU.
+// The ring depth does not change the order of the K walk, so both give the
+// same partials bit for bit.
+template <int NS>
+constexpr int gram_split_lds() {
+    return NS * (Tile<bf16_t, 2, 2, 2, 2>::LBYTES + Tile<bf16_t, 2, 2, 2, 2>::RBYTES);
+}
+constexpr int kGramStages = 8, kGramStagesGroup = 4;
 
-constexpr int kGramSplitLds = kGramStages * (Tile<bf16_t, 2, 2, 2, 2>::LBYTES + Tile<bf16_t, 2, 2, 2, 2>::RBYTES);
-
+template <int NS>
 __device__ __forceinline__ void gram_split_bf16_body(const GramArgs& a, const int id, char* smem) {
     typedef Tile<bf16_t, 2, 2, 2, 2> TL;
     typedef Mma<bf16_t> M;
-    constexpr int NS = kGramStages;
     constexpr int STAGE = TL::LBYTES + TL::RBYTES;   // 8 KB + 8 KB
     constexpr int LPW = 2 * (TL::BM / 8 / TL::NW);   // DMA instructions per wave per tile (left + right)
     static_assert(LPW * (NS - 2) < 64, "vmcnt range");
-    static_assert(NS * STAGE == kGramSplitLds, "LDS size");
+    static_assert(NS * STAGE == gram_split_lds<NS>(), "LDS size");
     const int xcd = id % kNumXCD, slot = id / kNumXCD;
     const int split = xcd + kNumXCD * (slot / a.nupper);
     if (split >= a.nsplit) return;
@@ -1626,8 +1632,9 @@ __device__ __forceinline__ void gram_split_bf16_body(const GramArgs& a, const in
 // so an element of a lower tile is read at its mirror position.  A workgroup
 // owns kGfRows rows of one 64 x 64 tile of Gs.  A lower tile reads 64 rows of
 // kGfRows columns of its mirror (64-byte pieces) and transposes them through
-// LDS, so reads and writes are both coalesced.  Each element sums its split
-// partials in split order.
+// LDS, so reads and writes are both coalesced (a pitch of 66 floats keeps the
+// transposing writes of 32 lanes on distinct banks).  Each element sums its
+// split partials in split order.
 constexpr int kGfRows = 16;
 constexpr int kGfPerTile = kGramTile / kGfRows;
 static_assert(kGfRows * kGramTile == 4 * 256, "four elements per thread");
@@ -1635,7 +1642,7 @@ static_assert(kGfRows * kGramTile == 4 * 256, "four elements per thread");
 template <typename E>
 __device__ __forceinline__ void gram_finalize_body(const float* __restrict__ part, int nsplit, int64_t rnp,
                                                    int64_t r, int64_t ldg, float half_s, E* __restrict__ gs,
-                                                   const int id, float (*tr)[kGramTile + 1]) {
+                                                   const int id, float (*tr)[kGramTile + 2]) {
     const int ntiles = (int)(rnp / kGramTile);
     const int tile = id / kGfPerTile, x0 = (id % kGfPerTile) * kGfRows;
     const int ti = tile / ntiles, tj = tile % ntiles;
@@ -1757,14 +1764,14 @@ __global__ __launch_bounds__(Big::NTH) void w0_pass_big(W0PassArgs a) {
 }
 
 __global__ __launch_bounds__(256) void gram_split_bf16(GramArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[kGramSplitLds];
-    gram_split_bf16_body(a, blockIdx.x, smem);
+    __shared__ __attribute__((aligned(1024))) char smem[gram_split_lds<kGramStages>()];
+    gram_split_bf16_body<kGramStages>(a, blockIdx.x, smem);
 }
 
 template <typename E>
 __global__ __launch_bounds__(256) void gram_finalize(const float* __restrict__ part, int nsplit, int64_t rnp,
                                                      int64_t r, int64_t ldg, float half_s, E* __restrict__ gs) {
-    __shared__ float tr[kGfRows][kGramTile + 1];
+    __shared__ float tr[kGfRows][kGramTile + 2];
     gram_finalize_body<E>(part, nsplit, rnp, r, ldg, half_s, gs, blockIdx.x, tr);
 }
 
@@ -1817,13 +1824,13 @@ __global__ __launch_bounds__(Big::NTH) void w0_pass_big_group(Group<W0PassArgs> 
 }
 
 __global__ __launch_bounds__(256) void gram_split_bf16_group(Group<GramArgs> g) {
-    __shared__ __attribute__((aligned(1024))) char smem[kGramSplitLds];
+    __shared__ __attribute__((aligned(1024))) char smem[gram_split_lds<kGramStagesGroup>()];
     const int j = group_member(g, blockIdx.x);
-    gram_split_bf16_body(g.a[j], blockIdx.x - g.start[j], smem);
+    gram_split_bf16_body<kGramStagesGroup>(g.a[j], blockIdx.x - g.start[j], smem);
 }
 
 __global__ __launch_bounds__(256) void gram_finalize_group(Group<GramFinArgs> g) {
-    __shared__ float tr[kGfRows][kGramTile + 1];
+    __shared__ float tr[kGfRows][kGramTile + 2];
     const int j = group_member(g, blockIdx.x);
     const GramFinArgs& a = g.a[j];
     gram_finalize_body<bf16_t>(a.part, a.nsplit, a.rnp, a.r, a.ldg, a.half_s, static_cast<bf16_t*>(a.gs),
