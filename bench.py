@@ -390,9 +390,9 @@ SWEEP_METRIC = "many-module sweep: norm + compose fwd/bwd ms per step (64 layers
 
 def sweep_main(args, D, dev):
     """The many-module sweep: 64 layers x 7 adapted projections, every
-    module's weights resident; a step is every layer's norms (the six
-    projections reading the 5120-wide input in one grouped call, down on its
-    own) and compose forward and backward of every module, in model order.
+    module's weights resident; a step is every layer's norms (all seven
+    projections in one grouped call) and compose forward and backward of
+    every module, in model order.
     Activations are pooled per shape, two rotating copies."""
     nl, npj = DI.SWEEP_LAYERS, len(DI.SWEEP_PROJECTIONS)
     T, r = DI.SWEEP_T, DI.SWEEP_R
@@ -422,9 +422,9 @@ def sweep_main(args, D, dev):
                              dl=torch.empty(T, d_out, dtype=torch.bfloat16, device=dev),
                              dm=torch.empty(d_out, device=dev)))
         pool[d_out] = sets
-    grp = list(range(6))        # q, k, v, o, gate, up: d_in 5120
-    d_in_g = DI.SWEEP_PROJECTIONS[0][2]
-    ws_group = torch.empty(D.norm_group_workspace_size([DI.SWEEP_PROJECTIONS[j][1] for j in grp], d_in_g, r,
+    grp = list(range(npj))      # every projection of a layer in one grouped call
+    ws_group = torch.empty(D.norm_group_workspace_size([DI.SWEEP_PROJECTIONS[j][1] for j in grp],
+                                                       [DI.SWEEP_PROJECTIONS[j][2] for j in grp], r,
                                                        torch.bfloat16), dtype=torch.uint8, device=dev)
     ws_single = torch.empty(max(D.norm_workspace_size(d_out, d_in, r, torch.bfloat16)
                                 for _, d_out, d_in in DI.SWEEP_PROJECTIONS), dtype=torch.uint8, device=dev)
@@ -506,7 +506,7 @@ def sweep_main(args, D, dev):
             "compose_ms_per_step": round(t_comp * 1e3, 3),
             "compose_GBps": round(cbytes / t_comp / 1e9, 1),
             "norm_workspace_bytes_per_module": per_module_ws,
-            "norm_workspace_bytes_group_of_6": int(ws_group.numel()),
+            "norm_workspace_bytes_group": int(ws_group.numel()),
             "compose_bwd_workspace_bytes_max": int(ws_bwd.numel()),
         },
     }

@@ -27,7 +27,8 @@ _i64, _f32, _vp, _sz = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c
 class NormMember(ctypes.Structure):
     """DoraNormMember of include/dora.h."""
     _fields_ = [("W0", ctypes.c_void_p), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("m", ctypes.c_void_p),
-                ("wnorm", ctypes.c_void_p), ("g", ctypes.c_void_p), ("d_out", ctypes.c_int64), ("s", ctypes.c_float)]
+                ("wnorm", ctypes.c_void_p), ("g", ctypes.c_void_p), ("d_out", ctypes.c_int64), ("d_in", ctypes.c_int64),
+                ("s", ctypes.c_float)]
 
 
 MAX_NORM_GROUP = 8
@@ -43,9 +44,10 @@ _SIGNATURES = {
     "dora_compose_backward_workspace_size": (ctypes.c_int, [_i64, _i64, ctypes.POINTER(_sz)]),
     "dora_compose_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _f32, _i64, _i64, ctypes.c_int,
                                              ctypes.c_int, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "dora_factored_norm_group_workspace_size": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(_i64), _i64, _i64,
-                                                               ctypes.c_int, ctypes.POINTER(_sz)]),
-    "dora_factored_norm_group": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(NormMember), _i64, _i64, ctypes.c_int,
+    "dora_factored_norm_group_workspace_size": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(_i64),
+                                                               ctypes.POINTER(_i64), _i64, ctypes.c_int,
+                                                               ctypes.POINTER(_sz)]),
+    "dora_factored_norm_group": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(NormMember), _i64, ctypes.c_int,
                                                 _f32, _vp, _sz, _vp]),
     "dora_merge_workspace_size": (ctypes.c_int, [_i64, _i64, ctypes.c_int, ctypes.POINTER(_sz)]),
     "dora_merge": (ctypes.c_int, [_vp, _vp, _vp, _vp, _f32, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _sz, _vp]),
@@ -151,10 +153,14 @@ def compose_backward_workspace_size(T: int, d_out: int) -> int:
     return n.value
 
 
-def norm_group_workspace_size(d_outs, d_in: int, r: int, dtype: torch.dtype) -> int:
+def norm_group_workspace_size(d_outs, d_ins, r: int, dtype: torch.dtype) -> int:
+    """Workspace of a grouped norm whose member j is [d_outs[j], d_ins[j]]."""
+    if len(d_outs) != len(d_ins):
+        raise ValueError("d_outs and d_ins must have one entry per member")
     n = ctypes.c_size_t(0)
-    arr = (_i64 * len(d_outs))(*[int(d) for d in d_outs])
-    _check(load().dora_factored_norm_group_workspace_size(len(d_outs), arr, d_in, r, _DTYPE_CODE[dtype],
+    outs = (_i64 * len(d_outs))(*[int(d) for d in d_outs])
+    ins = (_i64 * len(d_ins))(*[int(d) for d in d_ins])
+    _check(load().dora_factored_norm_group_workspace_size(len(d_outs), outs, ins, r, _DTYPE_CODE[dtype],
                                                            ctypes.byref(n)),
            "dora_factored_norm_group_workspace_size")
     return n.value
@@ -203,11 +209,12 @@ def factored_norm(W0, A, B, s: float, m=None, eps: float | None = None, *, wnorm
 
 
 def factored_norm_group(members, eps: float | None = None, *, outs=None, ws=None):
-    """Factored norms of several projections sharing d_in and r in one call.
+    """Factored norms of several projections sharing r and the dtype in one call.
 
-    members: sequence of (W0, A, B, s, m) with m fp32 [d_out] or None.
-    Returns a list of (wnorm, g) per member, g None where m is None; each
-    equals factored_norm's result for that member bitwise.
+    members: sequence of (W0, A, B, s, m) with m fp32 [d_out] or None; each
+    member has its own [d_out, d_in].  Returns a list of (wnorm, g) per
+    member, g None where m is None; each equals factored_norm's result for
+    that member bitwise.
     """
     lib = load()
     n = len(members)
@@ -215,14 +222,14 @@ def factored_norm_group(members, eps: float | None = None, *, outs=None, ws=None
         raise ValueError(f"a group holds 1..{MAX_NORM_GROUP} members (got {n})")
     W0_0, A_0 = members[0][0], members[0][1]
     dev, dt = W0_0.device, W0_0.dtype
-    d_in, r = W0_0.shape[1], A_0.shape[0]
+    r = A_0.shape[0]
     if dt not in _DTYPE_CODE:
         raise ValueError(f"unsupported dtype {dt}")
     eps = default_eps(dt) if eps is None else float(eps)
     arr = (NormMember * n)()
     results = []
     for j, (W0, A, B, s, m) in enumerate(members):
-        d_out = W0.shape[0]
+        d_out, d_in = W0.shape
         _need(W0, f"W0[{j}]", dev, dt, (d_out, d_in))
         _need(A, f"A[{j}]", dev, dt, (r, d_in))
         _need(B, f"B[{j}]", dev, dt, (d_out, r))
@@ -237,12 +244,13 @@ def factored_norm_group(members, eps: float | None = None, *, outs=None, ws=None
         if m is not None:
             _need(g, f"g[{j}]", dev, torch.float32, (d_out,))
         arr[j] = NormMember(_ptr(W0), _ptr(A), _ptr(B), _ptr(m), _ptr(wnorm), _ptr(g) if m is not None else None,
-                            d_out, float(s))
+                            d_out, d_in, float(s))
         results.append((wnorm, g if m is not None else None))
     if ws is None:
-        ws = workspace(norm_group_workspace_size([mb[0].shape[0] for mb in members], d_in, r, dt), dev)
+        ws = workspace(norm_group_workspace_size([mb[0].shape[0] for mb in members],
+                                                 [mb[0].shape[1] for mb in members], r, dt), dev)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib.dora_factored_norm_group(n, arr, d_in, r, _DTYPE_CODE[dt], eps, _ptr(ws), nbytes, _stream(dev)),
+    _check(lib.dora_factored_norm_group(n, arr, r, _DTYPE_CODE[dt], eps, _ptr(ws), nbytes, _stream(dev)),
            "dora_factored_norm_group")
     return results
 

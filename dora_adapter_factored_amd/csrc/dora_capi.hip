@@ -58,7 +58,7 @@ const char* dora_status_string(int status) {
 
 const char* dora_last_error_detail(void) { return g_detail; }
 
-int dora_version(void) { return 100; }
+int dora_version(void) { return 200; }
 
 int dora_factored_norm_workspace_size(int64_t d_out, int64_t d_in, int64_t r, int dtype, size_t* bytes) {
     if (!bytes) return fail(DORA_ERR_INVALID_ARG, "bytes is NULL");
@@ -100,30 +100,29 @@ int dora_factored_norm(const void* W0, const void* A, const void* B, const float
 
 static_assert(DORA_MAX_NORM_GROUP == dora::kMaxNormGroup, "group size limit");
 
-int dora_factored_norm_group_workspace_size(int n, const int64_t* d_out, int64_t d_in, int64_t r, int dtype,
+int dora_factored_norm_group_workspace_size(int n, const int64_t* d_out, const int64_t* d_in, int64_t r, int dtype,
                                             size_t* bytes) {
-    if (!bytes || !d_out) return fail(DORA_ERR_INVALID_ARG, "bytes and d_out must be non-NULL");
+    if (!bytes || !d_out || !d_in) return fail(DORA_ERR_INVALID_ARG, "bytes, d_out and d_in must be non-NULL");
     if (n < 1 || n > DORA_MAX_NORM_GROUP) return fail(DORA_ERR_INVALID_ARG, "n must be in 1..%d", DORA_MAX_NORM_GROUP);
-    if (!dim_ok(d_in, 1) || !dim_ok(r, 1)) return fail(DORA_ERR_INVALID_ARG, "sizes must satisfy 1 <= d_in, r < 2^31");
+    if (!dim_ok(r, 1)) return fail(DORA_ERR_INVALID_ARG, "r must satisfy 1 <= r < 2^31");
     if (!dtype_ok(dtype)) return fail(DORA_ERR_INVALID_ARG, "unknown dtype code %d", dtype);
     if (dtype == DORA_F16) return fail(DORA_ERR_UNSUPPORTED, "factored norm supports bf16 and fp32 inputs");
     for (int j = 0; j < n; ++j)
-        if (!dim_ok(d_out[j], 1)) return fail(DORA_ERR_INVALID_ARG, "member %d: d_out out of range", j);
+        if (!dim_ok(d_out[j], 1) || !dim_ok(d_in[j], 1))
+            return fail(DORA_ERR_INVALID_ARG, "member %d: d_out or d_in out of range", j);
     *bytes = dora::norm_group_workspace_bytes(n, d_out, d_in, r, dtype);
     return ok();
 }
 
-int dora_factored_norm_group(int n, const DoraNormMember* members, int64_t d_in, int64_t r, int dtype, float eps,
+int dora_factored_norm_group(int n, const DoraNormMember* members, int64_t r, int dtype, float eps,
                              void* workspace, size_t workspace_bytes, void* stream) {
     if (!members) return fail(DORA_ERR_INVALID_ARG, "members must be non-NULL");
     if (n < 1 || n > DORA_MAX_NORM_GROUP) return fail(DORA_ERR_INVALID_ARG, "n must be in 1..%d", DORA_MAX_NORM_GROUP);
-    if (!dim_ok(d_in, 1) || !dim_ok(r, 1))
-        return fail(DORA_ERR_INVALID_ARG, "sizes must satisfy 1 <= d_in, r < 2^31 (got %lld, %lld)", (long long)d_in,
-                    (long long)r);
+    if (!dim_ok(r, 1)) return fail(DORA_ERR_INVALID_ARG, "r must satisfy 1 <= r < 2^31 (got %lld)", (long long)r);
     if (!dtype_ok(dtype)) return fail(DORA_ERR_INVALID_ARG, "unknown dtype code %d", dtype);
     if (dtype == DORA_F16) return fail(DORA_ERR_UNSUPPORTED, "factored norm supports bf16 and fp32 inputs");
     if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(DORA_ERR_INVALID_ARG, "eps must be finite and >= 0");
-    int64_t d_outs[DORA_MAX_NORM_GROUP];
+    int64_t d_outs[DORA_MAX_NORM_GROUP], d_ins[DORA_MAX_NORM_GROUP];
     dora::NormMember mem[DORA_MAX_NORM_GROUP];
     for (int j = 0; j < n; ++j) {
         const DoraNormMember& M = members[j];
@@ -131,15 +130,17 @@ int dora_factored_norm_group(int n, const DoraNormMember* members, int64_t d_in,
         if (!M.wnorm) return fail(DORA_ERR_INVALID_ARG, "member %d: wnorm must be non-NULL", j);
         if (M.m && !M.g) return fail(DORA_ERR_INVALID_ARG, "member %d: g must be non-NULL when m is given", j);
         if (!dim_ok(M.d_out, 1)) return fail(DORA_ERR_INVALID_ARG, "member %d: d_out out of range", j);
+        if (!dim_ok(M.d_in, 1)) return fail(DORA_ERR_INVALID_ARG, "member %d: d_in out of range", j);
         if (!std::isfinite(M.s)) return fail(DORA_ERR_INVALID_ARG, "member %d: s must be finite", j);
         d_outs[j] = M.d_out;
-        mem[j] = dora::NormMember{M.W0, M.A, M.B, M.m, M.wnorm, M.m ? M.g : nullptr, M.d_out, M.s};
+        d_ins[j] = M.d_in;
+        mem[j] = dora::NormMember{M.W0, M.A, M.B, M.m, M.wnorm, M.m ? M.g : nullptr, M.d_out, M.d_in, M.s};
     }
-    const size_t need = dora::norm_group_workspace_bytes(n, d_outs, d_in, r, dtype);
+    const size_t need = dora::norm_group_workspace_bytes(n, d_outs, d_ins, r, dtype);
     if (!workspace) return fail(DORA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
     if (workspace_bytes < need) return fail(DORA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
     if (!aligned256(workspace)) return fail(DORA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    hipError_t e = dora::launch_norm_group(n, mem, d_in, r, dtype, eps, workspace, static_cast<hipStream_t>(stream));
+    hipError_t e = dora::launch_norm_group(n, mem, r, dtype, eps, workspace, static_cast<hipStream_t>(stream));
     return hip_status(e, "dora_factored_norm_group launch");
 }
 

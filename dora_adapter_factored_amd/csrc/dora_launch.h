@@ -51,14 +51,15 @@ struct NormMember {
     float* wnorm;
     float* g;
     int64_t d_out;
+    int64_t d_in;
     float s;
 };
 
 // Workspace of a group: each member's own region, 256-byte aligned, in order.
-size_t norm_group_workspace_bytes(int n, const int64_t* d_out, int64_t d_in, int64_t r, int dtype);
+size_t norm_group_workspace_bytes(int n, const int64_t* d_out, const int64_t* d_in, int64_t r, int dtype);
 
-hipError_t launch_norm_group(int n, const NormMember* mem, int64_t d_in, int64_t r, int dtype, float eps,
-                             void* workspace, hipStream_t stream);
+hipError_t launch_norm_group(int n, const NormMember* mem, int64_t r, int dtype, float eps, void* workspace,
+                             hipStream_t stream);
 
 hipError_t launch_norm(const NormPlan& p, const void* W0, const void* A, const void* B,
                        const float* m, float s, float eps, float* wnorm, float* g,

@@ -2198,20 +2198,20 @@ hipError_t launch_norm(const NormPlan& p, const void* W0, const void* A, const v
     return norm_typed<bf16_t>(p, W0, A, B, m, s, eps, wnorm, g, workspace, stream);
 }
 
-size_t norm_group_workspace_bytes(int n, const int64_t* d_out, int64_t d_in, int64_t r, int dtype) {
+size_t norm_group_workspace_bytes(int n, const int64_t* d_out, const int64_t* d_in, int64_t r, int dtype) {
     size_t total = 0;
-    for (int j = 0; j < n; ++j) total += align_up(plan_norm(d_out[j], d_in, r, dtype, false).bytes_needed, 256);
+    for (int j = 0; j < n; ++j) total += align_up(plan_norm(d_out[j], d_in[j], r, dtype, false).bytes_needed, 256);
     return total;
 }
 
-// One call for several norms that share d_in and r (the projections of one
-// layer that read the same input).  When every member takes the aligned bf16
-// large-tile path, each stage runs once for the whole group (four launches in
-// all); otherwise the members run one after another.  Either way a member's
-// kernels, tiling and summation order are those of its own single call, so
-// the results are bitwise the same.
-hipError_t launch_norm_group(int n, const NormMember* mem, int64_t d_in, int64_t r, int dtype, float eps,
-                             void* workspace, hipStream_t st) {
+// One call for several norms that share r (for example all projections of
+// one layer).  When every member takes the aligned bf16 large-tile path, each
+// stage runs once for the whole group (four launches in all); otherwise the
+// members run one after another.  Either way a member's kernels, tiling and
+// summation order are those of its own single call, so the results are
+// bitwise the same.
+hipError_t launch_norm_group(int n, const NormMember* mem, int64_t r, int dtype, float eps, void* workspace,
+                             hipStream_t st) {
     static_assert(sizeof(Group<W0PassArgs>) <= 4096 && sizeof(Group<GramArgs>) <= 4096, "kernel argument size");
     NormPlan plans[kMaxNormGroup];
     char* wsj[kMaxNormGroup];
@@ -2219,9 +2219,9 @@ hipError_t launch_norm_group(int n, const NormMember* mem, int64_t d_in, int64_t
     bool grouped = dtype == kBF16;
     for (int j = 0; j < n; ++j) {
         const NormMember& M = mem[j];
-        plans[j] = plan_norm(M.d_out, d_in, r, dtype, M.s == 0.0f);
+        plans[j] = plan_norm(M.d_out, M.d_in, r, dtype, M.s == 0.0f);
         wsj[j] = static_cast<char*>(workspace) + off;
-        off += align_up(plan_norm(M.d_out, d_in, r, dtype, false).bytes_needed, 256);
+        off += align_up(plan_norm(M.d_out, M.d_in, r, dtype, false).bytes_needed, 256);
         grouped = grouped && plans[j].big && plans[j].gram_xcd && !plans[j].base_only &&
                   operands_aligned<bf16_t>(plans[j], M.W0, M.A, M.B);
     }
@@ -2244,33 +2244,39 @@ hipError_t launch_norm_group(int n, const NormMember* mem, int64_t d_in, int64_t
     for (int j = 0; j < n; ++j) {
         const NormMember& M = mem[j];
         L[j] = make_norm_launch<bf16_t>(plans[j], true, M.W0, M.A, M.B, M.m, M.s, eps, M.wnorm, M.g, wsj[j]);
-        gg.a[j] = L[j].ga;
-        gg.start[j + 1] = gg.start[j] + pad8((int)L[j].ggrid);
         gf.a[j] = L[j].gf;
         gf.start[j + 1] = gf.start[j] + (int)L[j].gfgrid;
         gn.a[j] = L[j].nf;
         gn.start[j + 1] = gn.start[j] + (int)L[j].nfgrid;
     }
-    // W0 pass: members with the longest workgroups (most k-tiles per K-chunk)
-    // go first, so the short workgroups of the others fill the last round's
-    // idle CUs instead of the long ones running alone at the end.  Each
-    // member keeps its own plan, so its result is unchanged.
-    int ord[kMaxNormGroup];
-    auto kt_per_wg = [&](int j) {
-        const int nkt = plans[j].nkt_w0 + plans[j].nkt_g;
-        return (nkt + plans[j].ksplit - 1) / plans[j].ksplit;
-    };
-    for (int i = 0; i < n; ++i) {
-        int k = i;
-        while (k > 0 && kt_per_wg(ord[k - 1]) < kt_per_wg(i)) {
-            ord[k] = ord[k - 1];
-            --k;
+    // Gram and W0 pass: members with the longest workgroups (most k-tiles per
+    // K-chunk) go first, so the short workgroups of the others fill the last
+    // round's idle CUs instead of the long ones running alone at the end (a
+    // stable order: ties keep member order).  Each member keeps its own plan,
+    // so its result is unchanged.
+    auto longest_first = [&](auto kt_per_wg, int (&ord)[kMaxNormGroup]) {
+        for (int i = 0; i < n; ++i) {
+            int k = i;
+            while (k > 0 && kt_per_wg(ord[k - 1]) < kt_per_wg(i)) {
+                ord[k] = ord[k - 1];
+                --k;
+            }
+            ord[k] = i;
         }
-        ord[k] = i;
-    }
+    };
+    int og[kMaxNormGroup], ow[kMaxNormGroup];
+    longest_first([&](int j) { return (L[j].ga.c.nkt0 + L[j].ga.nsplit - 1) / L[j].ga.nsplit; }, og);
+    longest_first(
+        [&](int j) {
+            const int nkt = plans[j].nkt_w0 + plans[j].nkt_g;
+            return (nkt + plans[j].ksplit - 1) / plans[j].ksplit;
+        },
+        ow);
     for (int i = 0; i < n; ++i) {
-        gw.a[i] = L[ord[i]].wa;
-        gw.start[i + 1] = gw.start[i] + pad8(L[ord[i]].wgrid);
+        gg.a[i] = L[og[i]].ga;
+        gg.start[i + 1] = gg.start[i] + pad8((int)L[og[i]].ggrid);
+        gw.a[i] = L[ow[i]].wa;
+        gw.start[i + 1] = gw.start[i] + pad8(L[ow[i]].wgrid);
     }
     hipError_t e;
     gram_split_bf16_group<<<gg.start[n], 256, 0, st>>>(gg);

@@ -108,6 +108,7 @@ typedef struct DoraNormMember {
     float* wnorm;
     float* g;
     int64_t d_out;
+    int64_t d_in;
     float s;
 } DoraNormMember;
 
@@ -116,31 +117,34 @@ typedef struct DoraNormMember {
 
 /*
  * Workspace bytes needed by dora_factored_norm_group for members of these
- * row counts (host call, launches nothing).
+ * sizes (host call, launches nothing): d_out and d_in are host arrays of n
+ * entries, member j being [d_out[j], d_in[j]].
  */
-int dora_factored_norm_group_workspace_size(int n, const int64_t* d_out, int64_t d_in, int64_t r, int dtype,
+int dora_factored_norm_group_workspace_size(int n, const int64_t* d_out, const int64_t* d_in, int64_t r, int dtype,
                                             size_t* bytes);
 
 /*
  * Factored row norms of up to DORA_MAX_NORM_GROUP adapted projections that
- * share d_in and r (the projections of one layer reading the same input),
- * in one call.  Each member computes exactly what dora_factored_norm
- * computes for it, with bitwise the same result; when every member is bf16
- * with 16-byte aligned operands and r > 192, each stage of the method
- * ([ScalingDoRA] §2: Gram, the W0 pass with its row epilogue, assembly)
- * runs as one launch for the whole group, so small projections (k/v rows)
- * share the chip instead of paying launch and tail costs one by one.
+ * share r and the dtype (for example every projection of one layer, whose
+ * norms depend on its weights alone), in one call.  Each member computes
+ * exactly what dora_factored_norm computes for it, with bitwise the same
+ * result; when every member is bf16 with 16-byte aligned operands and
+ * r > 192, each stage of the method ([ScalingDoRA] §2: Gram, the W0 pass with
+ * its row epilogue, assembly) runs as one launch for the whole group, so
+ * small projections (k/v rows) share the chip instead of paying launch and
+ * tail costs one by one, and long ones fill each other's last round.
  *
  *   n         1 .. DORA_MAX_NORM_GROUP.
- *   members   host array of n members; every member's pointers are device
- *             pointers, validated as in dora_factored_norm.  Outputs of
- *             different members must not overlap.
- *   d_in, r, dtype, eps   shared by all members.
+ *   members   host array of n members, each with its own d_out and d_in;
+ *             every member's pointers are device pointers, validated as in
+ *             dora_factored_norm.  Outputs of different members must not
+ *             overlap.
+ *   r, dtype, eps   shared by all members.
  *   workspace device scratch of at least
  *             dora_factored_norm_group_workspace_size() bytes, 256-byte
  *             aligned.
  */
-int dora_factored_norm_group(int n, const DoraNormMember* members, int64_t d_in, int64_t r, int dtype, float eps,
+int dora_factored_norm_group(int n, const DoraNormMember* members, int64_t r, int dtype, float eps,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -30,6 +30,27 @@ def test_header_and_binding_agree():
     assert declared_functions() == sorted(D.EXPORTED)
 
 
+def test_member_struct_layout_matches_the_header(tmp_path):
+    # the binding's ctypes copy of DoraNormMember against the C compiler's
+    # layout of the header's struct
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f for f, _ in Bn.NormMember._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "dora.h"\nint main(void) {\n'
+                   '    printf("%zu", sizeof(DoraNormMember));\n'
+                   + "".join(f'    printf(" %zu", offsetof(DoraNormMember, {f}));\n' for f in fields)
+                   + "    return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    want = [ctypes.sizeof(Bn.NormMember)] + [getattr(Bn.NormMember, f).offset for f in fields]
+    assert got == want
+
+
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
@@ -258,20 +279,29 @@ def test_merge_validation(lib):
 
 def test_norm_group_workspace_size(lib):
     n = ctypes.c_size_t()
-    d = (ctypes.c_int64 * 3)(5120, 1024, 1024)
-    assert lib.dora_factored_norm_group_workspace_size(3, d, 5120, 384, 1, ctypes.byref(n)) == 0
+    sizes = ((5120, 5120), (1024, 5120), (5120, 27648))   # members may differ in d_in
+    d = (ctypes.c_int64 * 3)(*[o for o, _ in sizes])
+    k = (ctypes.c_int64 * 3)(*[i for _, i in sizes])
+    assert lib.dora_factored_norm_group_workspace_size(3, d, k, 384, 1, ctypes.byref(n)) == 0
     total = 0
-    for d_out in (5120, 1024, 1024):   # each member's own region, 256-byte aligned
+    for d_out, d_in in sizes:   # each member's own region, 256-byte aligned
         one = ctypes.c_size_t()
-        assert lib.dora_factored_norm_workspace_size(d_out, 5120, 384, 1, ctypes.byref(one)) == 0
+        assert lib.dora_factored_norm_workspace_size(d_out, d_in, 384, 1, ctypes.byref(one)) == 0
         total += (one.value + 255) // 256 * 256
     assert n.value == total
-    assert lib.dora_factored_norm_group_workspace_size(0, d, 5120, 384, 1, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
-    assert lib.dora_factored_norm_group_workspace_size(9, d, 5120, 384, 1, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
-    assert lib.dora_factored_norm_group_workspace_size(3, None, 5120, 384, 1, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
-    assert lib.dora_factored_norm_group_workspace_size(3, d, 5120, 384, 2, ctypes.byref(n)) == Bn.DORA_ERR_UNSUPPORTED
+    E = Bn
+    assert lib.dora_factored_norm_group_workspace_size(0, d, k, 384, 1, ctypes.byref(n)) == E.DORA_ERR_INVALID_ARG
+    assert lib.dora_factored_norm_group_workspace_size(9, d, k, 384, 1, ctypes.byref(n)) == E.DORA_ERR_INVALID_ARG
+    assert lib.dora_factored_norm_group_workspace_size(3, None, k, 384, 1, ctypes.byref(n)) == E.DORA_ERR_INVALID_ARG
+    assert lib.dora_factored_norm_group_workspace_size(3, d, None, 384, 1, ctypes.byref(n)) == E.DORA_ERR_INVALID_ARG
+    assert lib.dora_factored_norm_group_workspace_size(3, d, k, 0, 1, ctypes.byref(n)) == E.DORA_ERR_INVALID_ARG
+    assert lib.dora_factored_norm_group_workspace_size(3, d, k, 384, 2, ctypes.byref(n)) == E.DORA_ERR_UNSUPPORTED
     bad = (ctypes.c_int64 * 2)(64, 0)
-    assert lib.dora_factored_norm_group_workspace_size(2, bad, 48, 8, 1, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
+    ok_in = (ctypes.c_int64 * 2)(48, 48)
+    assert lib.dora_factored_norm_group_workspace_size(2, bad, ok_in, 8, 1, ctypes.byref(n)) == E.DORA_ERR_INVALID_ARG
+    bad_in = (ctypes.c_int64 * 2)(48, 0)
+    assert lib.dora_factored_norm_group_workspace_size(2, (ctypes.c_int64 * 2)(64, 64), bad_in, 8, 1,
+                                                       ctypes.byref(n)) == E.DORA_ERR_INVALID_ARG
 
 
 def _group(lib, members=None, **kw):
@@ -280,13 +310,13 @@ def _group(lib, members=None, **kw):
     arr = (Bn.NormMember * max(1, len(members)))()
     for j, over in enumerate(members):
         mb = dict(W0=0x10000, A=0x20000, B=0x30000, m=0x40000, wnorm=0x50000 + 0x1000 * j, g=0x60000 + 0x1000 * j,
-                  d_out=64, s=1.0)
+                  d_out=64, d_in=48, s=1.0)
         mb.update(over)
-        arr[j] = Bn.NormMember(mb["W0"], mb["A"], mb["B"], mb["m"], mb["wnorm"], mb["g"], mb["d_out"], mb["s"])
-    a = dict(n=len(members), arr=arr, d_in=48, r=8, dtype=1, eps=1e-6, ws=FAKE_WS, nbytes=1 << 30)
+        arr[j] = Bn.NormMember(mb["W0"], mb["A"], mb["B"], mb["m"], mb["wnorm"], mb["g"], mb["d_out"], mb["d_in"],
+                               mb["s"])
+    a = dict(n=len(members), arr=arr, r=8, dtype=1, eps=1e-6, ws=FAKE_WS, nbytes=1 << 30)
     a.update(kw)
-    return lib.dora_factored_norm_group(a["n"], a["arr"], a["d_in"], a["r"], a["dtype"], a["eps"], a["ws"],
-                                        a["nbytes"], None)
+    return lib.dora_factored_norm_group(a["n"], a["arr"], a["r"], a["dtype"], a["eps"], a["ws"], a["nbytes"], None)
 
 
 def test_norm_group_validation(lib):
@@ -299,7 +329,8 @@ def test_norm_group_validation(lib):
     assert _group(lib, [dict(g=None)]) == E.DORA_ERR_INVALID_ARG            # m given without g
     assert _group(lib, [dict(), dict(d_out=0)]) == E.DORA_ERR_INVALID_ARG
     assert _group(lib, [dict(s=float("nan"))]) == E.DORA_ERR_INVALID_ARG
-    assert _group(lib, d_in=0) == E.DORA_ERR_INVALID_ARG
+    assert _group(lib, [dict(), dict(d_in=0)]) == E.DORA_ERR_INVALID_ARG
+    assert _group(lib, r=0) == E.DORA_ERR_INVALID_ARG
     assert _group(lib, dtype=2) == E.DORA_ERR_UNSUPPORTED
     assert _group(lib, dtype=7) == E.DORA_ERR_INVALID_ARG
     assert _group(lib, eps=-1.0) == E.DORA_ERR_INVALID_ARG

@@ -1,6 +1,6 @@
-"""GPU parity of the grouped norm (several projections sharing d_in and r in
-one call): every member's result is bitwise that of its own single call, and
-agrees with the fp64 oracle on sampled rows."""
+"""GPU parity of the grouped norm (several projections sharing r in one call,
+each with its own d_out and d_in): every member's result is bitwise that of
+its own single call, and agrees with the fp64 oracle on sampled rows."""
 import sys
 
 import numpy as np
@@ -46,14 +46,15 @@ def _check_oracle(L, wn, g, nrows, seed, rtol):
 
 
 def test_group_of_one_layer_of_the_sweep():
-    # the six projections of one layer that read the 5120-wide input
+    # all seven projections of one layer: q, k, v, o, gate, up read the
+    # 5120-wide input, down the 27648-wide one
     layers = []
-    for proj in range(6):
+    for proj in range(len(DI.SWEEP_PROJECTIONS)):
         spec = DI.sweep_spec(proj)
         say(f"[group] generating {spec.name}")
         layers.append(DI.make_layer(spec, DI.sweep_seed(3, proj), device=DEV, activations=False,
                                     gen_device="cuda"))
-    say("[group] sweep layer, 6 members")
+    say(f"[group] sweep layer, {len(layers)} members")
     res = D.factored_norm_group(_members(layers))
     _check_against_single_calls(layers, res)
     for j, (L, (wn, g)) in enumerate(zip(layers, res)):
@@ -61,20 +62,21 @@ def test_group_of_one_layer_of_the_sweep():
 
 
 GROUP_CASES = [
-    # (d_outs, d_in, r, dtype): grouped kernels when bf16, aligned, r > 192
-    ((300, 1000, 520), 4096, 256, "bf16"),
-    ((64, 8, 1), 1024, 384, "bf16"),
-    ((257, 129), 2048, 200, "bf16"),
-    ((64, 48), 48, 8, "f32"),          # member by member
-    ((500, 33), 640, 16, "bf16"),      # r <= 192: member by member
+    # (members as (d_out, d_in), r, dtype): grouped kernels when bf16, aligned, r > 192
+    (((300, 4096), (1000, 4096), (520, 4096)), 256, "bf16"),
+    (((64, 1024), (8, 1024), (1, 1024)), 384, "bf16"),
+    (((257, 2048), (129, 2048)), 200, "bf16"),
+    (((300, 1000), (520, 4096), (64, 2048), (96, 8200)), 256, "bf16"),   # different d_in
+    (((64, 48), (40, 100)), 8, "f32"),             # member by member
+    (((500, 640), (33, 640)), 16, "bf16"),         # r <= 192: member by member
 ]
 
 
-@pytest.mark.parametrize("d_outs,d_in,r,dt", GROUP_CASES)
-def test_group_shapes(d_outs, d_in, r, dt):
-    say(f"[group] d_outs={d_outs} d_in={d_in} r={r} {dt}")
-    layers = [DI.make_layer(DI.custom_spec(d, d_in, r, 1, dtype=dt, s=1.5, b_std=0.05), 700 + j, device=DEV,
-                            activations=False) for j, d in enumerate(d_outs)]
+@pytest.mark.parametrize("sizes,r,dt", GROUP_CASES)
+def test_group_shapes(sizes, r, dt):
+    say(f"[group] members={sizes} r={r} {dt}")
+    layers = [DI.make_layer(DI.custom_spec(d_out, d_in, r, 1, dtype=dt, s=1.5, b_std=0.05), 700 + j, device=DEV,
+                            activations=False) for j, (d_out, d_in) in enumerate(sizes)]
     res = D.factored_norm_group(_members(layers))
     _check_against_single_calls(layers, res)
     rtol = 2e-3 if dt == "bf16" else 1e-4
