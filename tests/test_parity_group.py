@@ -120,6 +120,36 @@ def test_group_mixed_members_and_no_magnitude():
     _check_oracle(layers[2], res[2][0], res[2][1], 128, 7, 2e-3)
 
 
+def test_group_of_eight_members_with_their_own_d_in():
+    # the largest group, every member with its own [d_out, d_in], one of a
+    # single row; members fall in four sizes of k-tiles per workgroup
+    sizes = ((1, 4096), (300, 1000), (1024, 2048), (64, 8200), (513, 512), (2048, 3000), (257, 6144), (96, 1024))
+    say(f"[group] eight members {sizes}")
+    layers = [DI.make_layer(DI.custom_spec(d_out, d_in, 320, 1, s=0.75, b_std=0.05), 950 + j, device=DEV,
+                            activations=False) for j, (d_out, d_in) in enumerate(sizes)]
+    res = D.factored_norm_group(_members(layers))
+    _check_against_single_calls(layers, res)
+    for j, (L, (wn, g)) in enumerate(zip(layers, res)):
+        _check_oracle(L, wn, g, 64, 30 + j, 2e-3)
+
+
+def test_group_mixed_d_in_with_s_zero_and_no_magnitude():
+    say("[group] different d_in; an s = 0 member; m = None members")
+    layers = [DI.make_layer(DI.custom_spec(d_out, d_in, 256, 1, s=1.0, b_std=0.05), 990 + j, device=DEV,
+                            activations=False) for j, (d_out, d_in) in enumerate(((384, 1024), (200, 5000), (640, 2048)))]
+    members = [(L.W0, L.A, L.B, L.spec.s, None) for L in layers]
+    members[1] = (layers[1].W0, layers[1].A, layers[1].B, 0.0, layers[1].m)
+    res = D.factored_norm_group(members)
+    torch.cuda.synchronize()
+    for j, (W0, A, B, s, m) in enumerate(members):
+        wn, g = D.factored_norm(W0, A, B, s, m)
+        torch.cuda.synchronize()
+        assert torch.equal(res[j][0], wn), j
+        assert (res[j][1] is None) == (m is None) and (m is None or torch.equal(res[j][1], g)), j
+    ref = torch.linalg.vector_norm(layers[1].W0.double(), dim=1).cpu().numpy()
+    check_rel(host64(res[1][0]), ref, 2e-3, "s = 0 member")
+
+
 def test_group_of_one_and_repeated_calls():
     say("[group] one member; repeated calls")
     L = DI.make_layer(DI.custom_spec(1024, 2048, 384, 1, b_std=0.05), 901, device=DEV, activations=False)
