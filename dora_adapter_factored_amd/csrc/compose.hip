@@ -226,6 +226,8 @@ __global__ __launch_bounds__(kThreads) void dm_finalize(const float* __restrict_
     __shared__ float red[kFinLanes][kFinCols];
     const int c = threadIdx.x % kFinCols, w = threadIdx.x / kFinCols;
     const int64_t j = (int64_t)blockIdx.x * kFinCols + c;
+    // wnorm is requested with the partials, not after them
+    const float wn = (w == 0 && j < d_out) ? wnorm[j] : 1.0f;
     float acc = 0.0f;
     if (j < d_out) {
         for (int p0 = w; p0 < nparts; p0 += kFinLanes * kFinBatch) {
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void dm_finalize(const float* __restrict_
         float v = red[0][c];
 #pragma unroll
         for (int q = 1; q < kFinLanes; ++q) v += red[q][c];
-        d_m[j] = nparts > 0 ? v / fmaxf(wnorm[j], eps) : 0.0f;
+        d_m[j] = nparts > 0 ? v / fmaxf(wn, eps) : 0.0f;
     }
 }
 

@@ -965,6 +965,11 @@ __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) 
 #pragma unroll
     for (int q = 0; q < GIP::NG; ++q) gacc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float bsum[1];
+    // m of this workgroup's rows, requested before the K walk so that its
+    // latency hides under it (loads retire in issue order, so the walk's
+    // first wait covers it)
+    float m_row = 0.0f;
+    if (threadIdx.x < kRowsPerWg && a.m && m0 + threadIdx.x < a.d_out) m_row = a.m[m0 + threadIdx.x];
     mainloop_w0_narrow<E, 1, NT, true, GIP::NG>(a.c, m0, 0, kt_begin, kt_end, 0, true, acc, gacc, bsum);
 
     // B rows [m0, m0 + 16), columns [0, BN) (zeros past r and past d_out)
@@ -1050,7 +1055,7 @@ __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) 
             const float n2 = fmaxf(fmaf(a.two_s, cd, base), 0.0f);
             const float wn = sqrtf(n2);
             a.wnorm[i] = wn;
-            if (a.m) a.g[i] = a.m[i] / fmaxf(wn, a.eps);
+            if (a.m) a.g[i] = m_row / fmaxf(wn, a.eps);
         }
     }
 }
@@ -1726,8 +1731,10 @@ __device__ __forceinline__ void norm_finalize_body(const float* __restrict__ pba
                                                   float two_s, const float* __restrict__ m, float eps,
                                                   float* __restrict__ wnorm, float* __restrict__ g, const int64_t i) {
     if (i >= d_out) return;
-    // partials are loaded in batches of 16 (both kinds together) before they
-    // are summed, each kind in partial order
+    // m is loaded ahead of the partials, so both come back in one memory
+    // round trip; partials are loaded in batches of 16 (both kinds together)
+    // before they are summed, each kind in partial order
+    const float mi = m ? m[i] : 0.0f;
     float base = 0.0f, cd = 0.0f;
     const int total = nbase + ncross;
     for (int c0 = 0; c0 < total; c0 += 16) {
@@ -1750,7 +1757,7 @@ __device__ __forceinline__ void norm_finalize_body(const float* __restrict__ pba
     const float n2 = fmaxf(fmaf(two_s, cd, base), 0.0f);
     const float wn = sqrtf(n2);
     wnorm[i] = wn;
-    if (m) g[i] = m[i] / fmaxf(wn, eps);
+    if (m) g[i] = mi / fmaxf(wn, eps);
 }
 
 // ------------------------------------------------------------- launches
