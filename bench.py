@@ -122,6 +122,47 @@ def stored_traffic(workload):
         return None
 
 
+NORM_KERNELS = ("w0_pass", "w0_rows", "gram_split", "gram_partial", "gram_finalize", "norm_finalize", "row_sumsq")
+
+
+def stored_norm_kernels(workload):
+    """Average duration in us of each norm kernel in the committed rocprofv3
+    kernel-trace summary of this workload's bench command, or None when
+    absent or traced on other kernel sources.  The bench times the norm as
+    one call (its kernels run back to back inside it), so a single kernel's
+    time comes from the trace."""
+    path = os.path.join(PROFILE_DIR, f"kernels_{workload}.txt")
+    try:
+        with open(path) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    digest = [l.split(":", 1)[1].strip() for l in lines if l.startswith("source_sha256:")]
+    if not digest or digest[0] != norm_source_digest():
+        return None
+    out = {}
+    for l in lines:
+        if not l.startswith("| "):
+            continue
+        cells = [c.strip() for c in l.strip("|").split("|")]
+        if len(cells) == 6 and cells[0] not in out:   # the averages table: kernel, calls, avg, min, max, %
+            name = cells[0].split("<")[0]
+            if name in NORM_KERNELS:
+                try:
+                    out[name] = float(cells[2])
+                except ValueError:
+                    pass
+        elif l.startswith("| kernel | dispatches"):
+            break
+    return out or None
+
+
+def w0_pass_flops(d_out, d_in, r):
+    """The W0 pass alone: U over the extended contraction [W0 | B] x [A | Gs]^T
+    and the base squares."""
+    return 2 * d_out * d_in * r + 2 * d_out * d_in + 2 * d_out * r * r
+
+
 def copy_calibration(dev, reps=10):
     """A plain device-to-device copy of known size (int32, so its kernel is
     told apart from the bf16 copies that build the rotating input sets).
@@ -340,6 +381,12 @@ def main():
     norm_tflops = F / t_norm / 1e12
     fwd_gbs, bwd_gbs = fb / t_fwd / 1e9, bb / t_bwd / 1e9
     peak_mm = PEAK_BF16_TFLOPS if dt != torch.float32 else PEAK_F32_MFMA_TFLOPS
+    kern = stored_norm_kernels(spec.name)
+    traced = None
+    if kern:
+        traced = {"source": f"profiles/kernels_{spec.name}.txt (rocprofv3 kernel trace)", "avg_us": kern}
+        if "w0_pass" in kern:
+            traced["w0_pass_TFLOPs"] = round(w0_pass_flops(d_out, d_in, r) / (kern["w0_pass"] * 1e-6) / 1e12, 1)
 
     out = {
         "metric": METRIC,
@@ -361,7 +408,7 @@ def main():
                  "frac_mfma_peak": round(norm_tflops / peak_mm, 4), "algorithmic_flop": F,
                  "algorithmic_bytes": nb, "GBps": round(nb / t_norm / 1e9, 1),
                  "frac_hbm_peak": round(nb / t_norm / 1e9 / PEAK_HBM_GBS, 4),
-                 "workspace_bytes": int(ws_norm.numel())},
+                 "workspace_bytes": int(ws_norm.numel()), "kernels_traced": traced},
         "compose_fwd": {"ms": round(t_fwd * 1e3, 4), "GBps": round(fwd_gbs, 1),
                         "frac_hbm_peak": round(fwd_gbs / PEAK_HBM_GBS, 4),
                         "frac_measured_copy": round(fwd_gbs / calib["GBps"], 4), "algorithmic_bytes": fb},

@@ -69,3 +69,20 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert p.returncode == 2
     assert "one GPU" in p.stderr and p.stdout == ""
+
+
+def test_traced_kernel_times_are_read_only_for_the_current_sources(tmp_path, monkeypatch):
+    table = ["# Kernel durations, workload w, one MI355X", "", "| kernel | calls | avg us | min us | max us | % of GPU time |",
+             "|---|---|---|---|---|---|", "| w0_pass | 48 | 60.4 | 58.0 | 66.6 | 16.9 |",
+             "| gram_finalize<...> | 48 | 4.8 | 3.9 | 5.8 | 1.3 |", "| compose_fwd_vec (y) | 48 | 18.5 | 17.5 | 21.0 | 5.1 |",
+             "", "| kernel | dispatches | p10 | median | p90 |", "|---|---|---|---|---|", "| w0_pass | 48 | 58.3 | 59.1 | 63.2 |",
+             "", "source_sha256: abc"]
+    (tmp_path / "kernels_w.txt").write_text("\n".join(table) + "\n")
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    monkeypatch.setattr(bench, "norm_source_digest", lambda: "abc")
+    assert bench.stored_norm_kernels("w") == {"w0_pass": 60.4, "gram_finalize": 4.8}
+    monkeypatch.setattr(bench, "norm_source_digest", lambda: "other")
+    assert bench.stored_norm_kernels("w") is None
+    assert bench.stored_norm_kernels("absent") is None
+    # the W0 pass's own work at 8192^2 r = 384: the extended contraction and the base squares
+    assert bench.w0_pass_flops(8192, 8192, 384) / 1e9 == pytest.approx(54.09, rel=1e-3)
