@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     default_eps,
     factored_norm,
     factored_norm_group,
+    factored_norm_noalloc,
     library_path,
     load,
     merge,

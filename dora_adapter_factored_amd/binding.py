@@ -40,6 +40,8 @@ _SIGNATURES = {
     "dora_factored_norm_workspace_size": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(_sz)]),
     "dora_factored_norm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _f32, _f32,
                                           _vp, _vp, _vp, _sz, _vp]),
+    "dora_factored_norm_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _f32, _f32,
+                                                  _vp, _vp, _vp]),
     "dora_compose": (ctypes.c_int, [_vp, _vp, _vp, _f32, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp]),
     "dora_compose_backward_workspace_size": (ctypes.c_int, [_i64, _i64, ctypes.POINTER(_sz)]),
     "dora_compose_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _f32, _i64, _i64, ctypes.c_int,
@@ -205,6 +207,37 @@ def factored_norm(W0, A, B, s: float, m=None, eps: float | None = None, *, wnorm
     _check(lib.dora_factored_norm(_ptr(W0), _ptr(A), _ptr(B), _ptr(m), d_out, d_in, r, _DTYPE_CODE[W0.dtype],
                                   float(s), eps, _ptr(wnorm), _ptr(g), _ptr(ws), nbytes, _stream(dev)),
            "dora_factored_norm")
+    return wnorm, (g if m is not None else None)
+
+
+def factored_norm_noalloc(W0, A, B, s: float, m=None, eps: float | None = None, *, wnorm=None, g=None):
+    """factored_norm through dora_factored_norm_noalloc: no workspace, the
+    library's static per-GPU scratch instead (same kernels, bitwise the same
+    result).  Outputs are allocated here unless given."""
+    lib = load()
+    dev = W0.device
+    d_out, d_in = W0.shape
+    r = A.shape[0]
+    _need(W0, "W0", dev)
+    _need(A, "A", dev, W0.dtype, (r, d_in))
+    _need(B, "B", dev, W0.dtype, (d_out, r))
+    if m is not None:
+        _need(m, "m", dev, torch.float32, (d_out,))
+    if W0.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {W0.dtype}")
+    eps = default_eps(W0.dtype) if eps is None else float(eps)
+    if wnorm is None:
+        wnorm = torch.empty(d_out, dtype=torch.float32, device=dev)
+    _need(wnorm, "wnorm", dev, torch.float32, (d_out,))
+    if m is not None and g is None:
+        g = torch.empty(d_out, dtype=torch.float32, device=dev)
+    if g is not None:
+        _need(g, "g", dev, torch.float32, (d_out,))
+    with torch.cuda.device(dev):
+        _check(lib.dora_factored_norm_noalloc(_ptr(W0), _ptr(A), _ptr(B), _ptr(m), d_out, d_in, r,
+                                              _DTYPE_CODE[W0.dtype], float(s), eps, _ptr(wnorm), _ptr(g),
+                                              _stream(dev)),
+               "dora_factored_norm_noalloc")
     return wnorm, (g if m is not None else None)
 
 

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "../../include/dora.h"
 #include "dora_launch.h"
@@ -41,6 +42,50 @@ bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255) =
 // the transpose of A runs one grid row per 64 values of r
 constexpr int64_t kMaxMergeRank = (int64_t)65535 * 64 - 64;
 
+int check_norm_args(const void* W0, const void* A, const void* B, const float* m, int64_t d_out, int64_t d_in,
+                    int64_t r, int dtype, float s, float eps, const float* wnorm, const float* g) {
+    if (!W0 || !A || !B) return fail(DORA_ERR_INVALID_ARG, "W0, A and B must be non-NULL");
+    if (!wnorm) return fail(DORA_ERR_INVALID_ARG, "wnorm must be non-NULL");
+    if (m && !g) return fail(DORA_ERR_INVALID_ARG, "g must be non-NULL when m is given");
+    if (!dim_ok(d_out, 1) || !dim_ok(d_in, 1) || !dim_ok(r, 1))
+        return fail(DORA_ERR_INVALID_ARG, "sizes must satisfy 1 <= d_out, d_in, r < 2^31 (got %lld, %lld, %lld)",
+                    (long long)d_out, (long long)d_in, (long long)r);
+    if (!dtype_ok(dtype)) return fail(DORA_ERR_INVALID_ARG, "unknown dtype code %d", dtype);
+    if (dtype == DORA_F16) return fail(DORA_ERR_UNSUPPORTED, "factored norm supports bf16 and fp32 inputs");
+    if (!std::isfinite(s)) return fail(DORA_ERR_INVALID_ARG, "s must be finite");
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(DORA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    return DORA_OK;
+}
+
+// Scratch of the allocation-free norm entry point: one array per GPU, held
+// by the loaded code object until the process ends.  In host code `scratch`
+// names a host-side shadow, not device memory, so its device address is taken
+// once per device with hipGetSymbolAddress (with that device current) and
+// only that address is handed to kernels.
+constexpr size_t kScratchBytes = DORA_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(DORA_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (!p || !aligned256(p)) return fail(DORA_ERR_HIP, "scratch address %p is not 256-byte aligned", p);
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return DORA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -75,16 +120,8 @@ int dora_factored_norm_workspace_size(int64_t d_out, int64_t d_in, int64_t r, in
 int dora_factored_norm(const void* W0, const void* A, const void* B, const float* m, int64_t d_out, int64_t d_in,
                        int64_t r, int dtype, float s, float eps, float* wnorm, float* g, void* workspace,
                        size_t workspace_bytes, void* stream) {
-    if (!W0 || !A || !B) return fail(DORA_ERR_INVALID_ARG, "W0, A and B must be non-NULL");
-    if (!wnorm) return fail(DORA_ERR_INVALID_ARG, "wnorm must be non-NULL");
-    if (m && !g) return fail(DORA_ERR_INVALID_ARG, "g must be non-NULL when m is given");
-    if (!dim_ok(d_out, 1) || !dim_ok(d_in, 1) || !dim_ok(r, 1))
-        return fail(DORA_ERR_INVALID_ARG, "sizes must satisfy 1 <= d_out, d_in, r < 2^31 (got %lld, %lld, %lld)",
-                    (long long)d_out, (long long)d_in, (long long)r);
-    if (!dtype_ok(dtype)) return fail(DORA_ERR_INVALID_ARG, "unknown dtype code %d", dtype);
-    if (dtype == DORA_F16) return fail(DORA_ERR_UNSUPPORTED, "factored norm supports bf16 and fp32 inputs");
-    if (!std::isfinite(s)) return fail(DORA_ERR_INVALID_ARG, "s must be finite");
-    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(DORA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    const int st = check_norm_args(W0, A, B, m, d_out, d_in, r, dtype, s, eps, wnorm, g);
+    if (st != DORA_OK) return st;
     const dora::NormPlan plan = dora::plan_norm(d_out, d_in, r, dtype, s == 0.0f);
     if (plan.bytes_needed > 0) {
         if (!workspace) return fail(DORA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", plan.bytes_needed);
@@ -96,6 +133,22 @@ int dora_factored_norm(const void* W0, const void* A, const void* B, const float
     hipError_t e = dora::launch_norm(plan, W0, A, B, m, s, eps, wnorm, g, workspace,
                                      static_cast<hipStream_t>(stream));
     return hip_status(e, "dora_factored_norm launch");
+}
+
+int dora_factored_norm_noalloc(const void* W0, const void* A, const void* B, const float* m, int64_t d_out,
+                               int64_t d_in, int64_t r, int dtype, float s, float eps, float* wnorm, float* g,
+                               void* stream) {
+    const int st = check_norm_args(W0, A, B, m, d_out, d_in, r, dtype, s, eps, wnorm, g);
+    if (st != DORA_OK) return st;
+    const dora::NormPlan plan = dora::plan_norm(d_out, d_in, r, dtype, s == 0.0f);
+    if (plan.bytes_needed > kScratchBytes)
+        return fail(DORA_ERR_WORKSPACE, "these sizes need %zu bytes of scratch; the static scratch holds %zu",
+                    plan.bytes_needed, kScratchBytes);
+    void* ws = nullptr;
+    const int sst = scratch_of_current_device(&ws);
+    if (sst != DORA_OK) return sst;
+    hipError_t e = dora::launch_norm(plan, W0, A, B, m, s, eps, wnorm, g, ws, static_cast<hipStream_t>(stream));
+    return hip_status(e, "dora_factored_norm_noalloc launch");
 }
 
 static_assert(DORA_MAX_NORM_GROUP == dora::kMaxNormGroup, "group size limit");

@@ -16,8 +16,10 @@
  *     B [d_out, r]; activations [T, d_out] with the per-feature vectors
  *     (g, wnorm, m, d_m) broadcast along the last axis.
  *   - Ownership: the caller owns every buffer, workspace included.  The
- *     library allocates nothing and keeps no mutable global state, so calls
- *     are re-entrant; calls that share a workspace must not overlap.
+ *     library allocates nothing and keeps no mutable global state beyond the
+ *     static scratch of dora_factored_norm_noalloc (and its per-device
+ *     address), so calls are re-entrant; calls that share a workspace must
+ *     not overlap.
  *   - Execution: work is enqueued on `stream` (a hipStream_t; NULL is the
  *     null stream) and the call returns without synchronising.  Arguments are
  *     validated on the host before anything is enqueued; on any error nothing
@@ -94,6 +96,32 @@ int dora_factored_norm(const void* W0, const void* A, const void* B, const float
                        int64_t d_out, int64_t d_in, int64_t r, int dtype, float s, float eps,
                        float* wnorm, float* g, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* Bytes of the static per-GPU scratch behind dora_factored_norm_noalloc. */
+#define DORA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * dora_factored_norm without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, outputs, kernels and results
+ * are those of dora_factored_norm (bitwise the same); the workspace is a
+ * static array of DORA_NOALLOC_SCRATCH_BYTES in the library's code object,
+ * one per GPU, held until the process ends.  Its device address is looked up
+ * once per device on the first call made with that device current; the call
+ * itself allocates nothing.
+ *
+ *   The call runs on the current device; `stream` must belong to it.
+ *   Sizes whose dora_factored_norm_workspace_size() exceeds
+ *   DORA_NOALLOC_SCRATCH_BYTES return DORA_ERR_WORKSPACE before anything is
+ *   launched; r <= 512 with d_out, d_in <= 32768 fits in bf16 and fp32.
+ *   Every call on one GPU shares that GPU's scratch and leaves its contents
+ *   behind; the kernels initialise what they read.  Calls that overlap in
+ *   time on one GPU (different streams, or threads without ordering) race on
+ *   the scratch and give undefined results: order them on one stream.
+ */
+int dora_factored_norm_noalloc(const void* W0, const void* A, const void* B, const float* m,
+                               int64_t d_out, int64_t d_in, int64_t r, int dtype, float s, float eps,
+                               float* wnorm, float* g, void* stream);
 
 /*
  * One member of a grouped norm call: the operands and outputs of one

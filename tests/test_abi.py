@@ -129,6 +129,42 @@ def test_norm_validation(lib):
     assert b"256-byte" in lib.dora_last_error_detail()
 
 
+def _norm_noalloc(lib, **kw):
+    a = dict(W0=FAKE, A=FAKE, B=FAKE, m=FAKE, d_out=8, d_in=16, r=4, dtype=1, s=1.0, eps=1e-6,
+             wnorm=FAKE, g=FAKE, stream=None)
+    a.update(kw)
+    return lib.dora_factored_norm_noalloc(a["W0"], a["A"], a["B"], a["m"], a["d_out"], a["d_in"], a["r"],
+                                          a["dtype"], a["s"], a["eps"], a["wnorm"], a["g"], a["stream"])
+
+
+def test_norm_noalloc_validation(lib):
+    """Same argument checks as dora_factored_norm; sizes whose workspace is
+    larger than the static scratch are refused before any device call."""
+    E = Bn
+    assert _norm_noalloc(lib, W0=None) == E.DORA_ERR_INVALID_ARG
+    assert _norm_noalloc(lib, wnorm=None) == E.DORA_ERR_INVALID_ARG
+    assert _norm_noalloc(lib, g=None) == E.DORA_ERR_INVALID_ARG
+    assert _norm_noalloc(lib, d_out=0) == E.DORA_ERR_INVALID_ARG
+    assert _norm_noalloc(lib, dtype=2) == E.DORA_ERR_UNSUPPORTED
+    assert _norm_noalloc(lib, eps=-1.0) == E.DORA_ERR_INVALID_ARG
+    limit = 16 << 20
+    big = dict(d_out=8192, d_in=16384, r=1024)
+    assert D.norm_workspace_size(big["d_out"], big["d_in"], big["r"], torch.bfloat16) > limit
+    assert _norm_noalloc(lib, **big) == E.DORA_ERR_WORKSPACE
+    assert b"static scratch" in lib.dora_last_error_detail()
+    # every workload of the pages' shapes fits the scratch
+    for d_out, d_in, r in ((8192, 8192, 384), (28672, 8192, 384), (27648, 5120, 384), (5120, 27648, 384),
+                           (32768, 32768, 512)):
+        for dt in (torch.bfloat16, torch.float32):
+            assert D.norm_workspace_size(d_out, d_in, r, dt) <= limit
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define DORA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == 16 << 20
+
+
 def _compose(lib, **kw):
     a = dict(base=FAKE, lora=ctypes.c_void_p(0x20000), g=FAKE, s=1.0, T=4, d_out=8, dtype=1, delta=0,
              y=ctypes.c_void_p(0x30000), stream=None)
