@@ -1081,11 +1081,7 @@ struct Big {
     static constexpr int BM = 256, BN = 384, BK = 32;
     static constexpr int WM = 2, WN = 4, NW = WM * WN, NTH = NW * 64;
     static constexpr int MT = 4, NT = 3;   // 32 x 32 blocks per wave
-#ifndef DORA_BIG_LS
-#define DORA_BIG_LS 4
-#define DORA_BIG_RS 3
-#endif
-    static constexpr int LS = DORA_BIG_LS, RS = DORA_BIG_RS;   // ring stages (left W0 | B, right A | Gs)
+    static constexpr int LS = 4, RS = 3;   // ring stages (left W0 | B, right A | Gs)
     static_assert(LS > RS && RS >= 2, "left tiles are issued before right tiles of the same step");
     static constexpr int ROWB = BK * 2;    // bytes of K per tile row
     static constexpr int LBYTES = BM * ROWB, RBYTES = BN * ROWB;
@@ -1917,9 +1913,6 @@ constexpr int64_t kRowsFormMaxElems = int64_t(1) << 25;
 
 template <typename E>
 bool rows_form(const NormPlan& p, bool aligned) {
-#ifdef DORA_NO_ROWS_FORM
-    return false;   // tile sweeps only
-#endif
     return gram_in_pass<E>(p, aligned) && p.d_out * p.d_in <= kRowsFormMaxElems;
 }
 
@@ -2093,9 +2086,6 @@ NormPlan plan_norm_impl(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool 
         p.bytes = align_up((size_t)d_out * 4, 256);
         return p;
     }
-#ifdef DORA_W0_NO_BIG
-    allow_big = false;
-#endif
     p.big = allow_big && dtype == kBF16 && r > 192;
     int ks = 1;
     if (p.big) {
@@ -2139,9 +2129,6 @@ NormPlan plan_norm_impl(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool 
         while (ks < kNumXCD && nkt / (2 * ks) >= 8) ks *= 2;
         while (ks < 64 && (int64_t)p.n_mtiles * p.n_ntiles * ks < 2 * kNumCU && nkt / (2 * ks) >= 8) ks *= 2;
     }
-#ifdef DORA_W0_FORCE_KSPLIT
-    ks = DORA_W0_FORCE_KSPLIT;   // tile sweeps only
-#endif
     p.ksplit = ks;
     // Gram
     const int gram_nkt = (int)((d_in + gram_bk - 1) / gram_bk);
@@ -2155,11 +2142,7 @@ NormPlan plan_norm_impl(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool 
     // (at most 256 / nupper workgroups' worth, each >= 4 k-tiles)
     p.gram_xcd = false;
     if (dtype == kBF16 && gram_nkt >= 4 * kNumXCD) {
-#ifdef DORA_GRAM_SPLIT
-        int x = DORA_GRAM_SPLIT;   // tuning sweeps only
-#else
         int x = kNumXCD;
-#endif
         while (x + kNumXCD <= 64 && (int64_t)(x + kNumXCD) * nupper <= kNumCU && gram_nkt / (x + kNumXCD) >= 4)
             x += kNumXCD;
         gs = x;

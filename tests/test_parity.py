@@ -146,6 +146,46 @@ def test_norm_dominated_by_low_rank_term(dt, r, d_in):
     check_rel(host64(wn), ref, NORM_RTOL[L.W0.dtype], "wnorm W0=0")
 
 
+@pytest.mark.parametrize("d_out,d_in,r", [(96, 2048, 1536), (64, 512, 2048), (64, 512, 2056), (40, 9000, 448)])
+def test_norm_wide_rank(d_out, d_in, r):
+    # r from 1536 to 2048 takes the large-tile form with several slices of r,
+    # Gram tiles of A over many 64-row blocks (several Gram units per W0-pass
+    # workgroup) and an assembly kernel whose LDS holds B rows of more than
+    # 64 KB; r = 2056 is past that form and runs the 128-row plan.
+    say(f"[parity] norm wide rank {d_out}x{d_in} r={r}")
+    spec = DI.custom_spec(d_out, d_in, r, 1, dtype="bf16", s=0.5, b_std=0.02)
+    L = DI.make_layer(spec, 90 + r, device=DEV, activations=False)
+    wn, g = gpu_norm(L)
+    ref_wn, ref_g = oracle_norm(L)
+    check_rel(host64(wn), ref_wn, NORM_RTOL[L.W0.dtype], "wnorm")
+    check_rel(host64(g), ref_g, NORM_RTOL[L.W0.dtype], "g")
+
+
+@pytest.mark.parametrize("r", [16, 64, 384])
+def test_norm_gram_term_dominant_with_cancellation(r):
+    # A bf16 layer built so that s^2 B_i G B_i^T is about twice the base term
+    # and the cross term cancels most of it: W0 = round(W1 - (s/2) B A) with
+    # ||s (BA)_i|| about 2 ||W1_i||, so base ~ 2, 2s cross ~ -4, s^2 ba ~ 4 and
+    # n^2 ~ 2.  An error of the Gram term relative to itself is multiplied by
+    # about 2 in n^2 here, so this is where its rounding shows first.
+    say(f"[parity] Gram-dominant bf16 layer r={r}")
+    s = 1.0
+    spec = DI.custom_spec(512, 2048, r, 1, dtype="bf16", s=s, b_std=math.sqrt(12.0 / r))
+    L = DI.make_layer(spec, 40 + r, device=DEV, activations=False)
+    W1, A, B = (t.cpu().to(torch.float64) for t in (L.W0, L.A, L.B))
+    L.W0 = (W1 - 0.5 * s * (B @ A)).to(torch.bfloat16).to(DEV)
+    wn, g = gpu_norm(L)
+    ref_wn, ref_g = oracle_norm(L)
+    # the construction did what it says: the Gram term is large against n^2
+    W0d = L.W0.cpu().to(torch.float64)
+    base = (W0d * W0d).sum(1)
+    ba = ((B @ A) ** 2).sum(1) * s * s
+    assert float((ba / torch.as_tensor(ref_wn ** 2)).median()) > 1.5
+    assert float((base / torch.as_tensor(ref_wn ** 2)).median()) > 0.8
+    check_rel(host64(wn), ref_wn, NORM_RTOL[L.W0.dtype], "wnorm")
+    check_rel(host64(g), ref_g, NORM_RTOL[L.W0.dtype], "g")
+
+
 def test_norm_zero_row_eps_clamp():
     say("[parity] zero row / eps clamp")
     spec = DI.custom_spec(64, 128, 8, 1, dtype="bf16")
@@ -446,6 +486,38 @@ def test_sweep_layer_modules():
         check_rel(host64(g)[rows], ref_g, 2e-3, f"{spec.name} g")
         del L
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("proj", [1, 0, 4])
+def test_sweep_shapes_compose(proj):
+    # compose forward, backward and the (dy, inner) tier at the sweep's own
+    # activation shapes, T = 2048 with d_out = 1024 (k), 5120 (q) and 27648
+    # (gate): sampled tokens for the element-wise outputs, sampled columns
+    # (over all tokens) for d_m
+    spec = DI.sweep_spec(proj)
+    say(f"[parity] sweep-shape compose {spec.name}")
+    L = DI.make_layer(spec, DI.sweep_seed(0, proj), device=DEV, gen_device="cuda")
+    wn, g = gpu_norm(L)
+    g32, wn32 = g.cpu(), wn.cpu()
+    rows = sample_rows(spec.T, 128, seed=100 + proj)
+    cols = sample_rows(spec.d_out, 256, seed=110 + proj)
+    _compose_check(L, g32, rows=rows, tag=spec.name)
+    _bwd_check(L, g32, wn32, rows=rows, cols=cols, tag=spec.name)
+    s, eps = spec.s, D.default_eps(L.dy.dtype)
+    y, inner = D.compose_dual(L.base_out, L.lora_out, g, s)
+    db, dl, dm = D.compose_backward_inner(L.dy, inner, g, wn, s, eps)
+    torch.cuda.synchronize()
+    b64, l64 = host64(L.base_out[rows]), host64(L.lora_out[rows])
+    r_y, r_i = oracle.compose_forward_inner(b64, l64, host64(g), s)
+    check_act(host64(y[rows]), r_y, L.dy.dtype, f"{spec.name} dual y")
+    check_act(host64(inner[rows]), r_i, L.dy.dtype, f"{spec.name} inner")
+    d64, i64 = host64(L.dy)[:, cols], host64(inner)[:, cols]
+    r_db, r_dl, r_dm = oracle.compose_backward_inner(d64, i64, host64(g)[cols], host64(wn)[cols], s, eps)
+    check_act(host64(db)[:, cols][rows], r_db[rows], L.dy.dtype, f"{spec.name} inner d_base")
+    check_act(host64(dl)[:, cols][rows], r_dl[rows], L.dy.dtype, f"{spec.name} inner d_lora")
+    check_act(host64(dm)[cols], r_dm, L.dy.dtype, f"{spec.name} inner d_m")
+    del L
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("d_out,d_in,r", [(1024, 2048, 384), (2048, 4096, 16)])
