@@ -1078,10 +1078,13 @@ struct IntC {
 };
 
 struct Big {
-    static constexpr int BM = 256, BN = 384, BK = 32;
-    static constexpr int WM = 2, WN = 4, NW = WM * WN, NTH = NW * 64;
+    static constexpr int WG_PER_CU = 1;                 // workgroups resident on one CU
+    static constexpr int WM = WG_PER_CU == 2 ? 1 : 2, WN = 4, NW = WM * WN, NTH = NW * 64;
     static constexpr int MT = 4, NT = 3;   // 32 x 32 blocks per wave
-    static constexpr int LS = 4, RS = 3;   // ring stages (left W0 | B, right A | Gs)
+    static constexpr int WROWS = MT * 32;  // rows of one wave row
+    static constexpr int BM = WM * WROWS, BN = WN * NT * 32, BK = 32;
+    static constexpr int LS = 4, RS = WG_PER_CU == 2 ? 2 : 3;   // ring stages (left W0 | B, right A | Gs)
+    static constexpr int ER = WM * 32;     // epilogue rows per round
     static_assert(LS > RS && RS >= 2, "left tiles are issued before right tiles of the same step");
     static constexpr int ROWB = BK * 2;    // bytes of K per tile row
     static constexpr int LBYTES = BM * ROWB, RBYTES = BN * ROWB;
@@ -1091,9 +1094,12 @@ struct Big {
     // and the per-row partials of all four rounds
     static constexpr int EB_SLOTS = BN * 2 / 16 + 1;
     static constexpr int EB_PITCH = EB_SLOTS * 16;
-    static constexpr int EPI_BYTES = 2 * 64 * EB_PITCH + MT * WN * 64 * 4;
+    // a staging buffer is filled by whole 1 KiB DMA instructions
+    static constexpr int EB_BYTES = (ER * EB_PITCH + 1023) / 1024 * 1024;
+    static constexpr int EPI_BYTES = 2 * EB_BYTES + MT * WN * ER * 4;
     static constexpr int LDS_BYTES = RING > EPI_BYTES ? RING : EPI_BYTES;
     static_assert(BM / 16 % NW == 0 && BN / 16 % NW == 0, "DMA groups split evenly across waves");
+    static_assert(LBYTES % 1024 == 0 && RBYTES % 1024 == 0, "ring stages hold whole 1 KiB DMA instructions");
     static_assert(MT == WN, "each wave sums the base term of one 32-row block");
 };
 
@@ -1211,7 +1217,7 @@ __device__ __forceinline__ void w0_pass_big_body(const W0PassArgs& a, const int 
         const int h = (lane >> 5) ^ sw;
         const int fo0 = (lane & 31) * G::ROWB + (h << 4);
         const int fo1 = (lane & 31) * G::ROWB + ((h ^ 2) << 4);
-        const int lrow0 = wm * 128 * G::ROWB, rrow0 = wn * 96 * G::ROWB;
+        const int lrow0 = wm * G::WROWS * G::ROWB, rrow0 = wn * 96 * G::ROWB;
         const float base_on = base_dst != nullptr ? 1.0f : 0.0f;
 
         // k-tile visited at step i (the walk starts at a rotated tile)
@@ -1371,10 +1377,10 @@ __device__ __forceinline__ void w0_pass_big_body(const W0PassArgs& a, const int 
         brs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(baddr >> 32));
         brs[2] = __builtin_amdgcn_readfirstlane((int)bbytes);
         brs[3] = 0x00020000;
-        constexpr int ER = 64;                                // rows per round
-        constexpr int EBUF = ER * G::EB_PITCH;                // one staging buffer
+        constexpr int ER = G::ER;                             // rows per round
+        constexpr int EBUF = G::EB_BYTES;                     // one staging buffer
         float* red = reinterpret_cast<float*>(smem + 2 * EBUF);   // [MT][WN][ER]
-        // staged row r of round mt is tile row (r / 32) * 128 + mt * 32 + r % 32
+        // staged row r of round mt is tile row (r / 32) * WROWS + mt * 32 + r % 32
         auto stage_b = [&](int mt, char* buf) __attribute__((always_inline)) {
             constexpr int NINS = (ER * G::EB_SLOTS + 63) / 64;
 #pragma unroll
@@ -1383,7 +1389,7 @@ __device__ __forceinline__ void w0_pass_big_body(const W0PassArgs& a, const int 
                 if (ins < NINS) {
                     const int slot = ins * 64 + lane;
                     const int row = slot / G::EB_SLOTS, ch = slot % G::EB_SLOTS;
-                    const int trow = (row >> 5) * 128 + mt * 32 + (row & 31);
+                    const int trow = (row >> 5) * G::WROWS + mt * 32 + (row & 31);
                     const int colb = colb0 + ch * 16;
                     const bool ok = ch < G::EB_SLOTS - 1 && row < ER && colb < (int)rb;
                     const int voff = ok ? trow * (int)rb + colb : kOutOfRange;
@@ -1419,22 +1425,22 @@ __device__ __forceinline__ void w0_pass_big_body(const W0PassArgs& a, const int 
     }
 
     // Publish this workgroup's partials: the base term of rows
-    // wm*128 + wn*32 + l (l < 32), and for every row the sum of the four
+    // wm*WROWS + wn*32 + l (l < 32), and for every row the sum of the four
     // column waves' dots, in wave order.
     {
-        const float* red = reinterpret_cast<const float*>(smem + 2 * 64 * G::EB_PITCH);
+        const float* red = reinterpret_cast<const float*>(smem + 2 * G::EB_BYTES);
         if (base_dst) {
-            const int64_t mrow = m0 + wm * 128 + wn * 32 + lane;
+            const int64_t mrow = m0 + wm * G::WROWS + wn * 32 + lane;
             if (lane < 32 && mrow < a.d_out) base_dst[mrow] = base_part;
         }
         for (int t = threadIdx.x; t < G::BM; t += G::NTH) {
-            const int mt = t >> 6, r = t & 63;
-            const int64_t mrow = m0 + (r >> 5) * 128 + mt * 32 + (r & 31);
+            const int mt = t / G::ER, r = t % G::ER;
+            const int64_t mrow = m0 + (r >> 5) * G::WROWS + mt * 32 + (r & 31);
             if (mrow < a.d_out) {
-                const float* rd = red + mt * G::WN * 64;
+                const float* rd = red + mt * G::WN * G::ER;
                 float v = rd[r];
 #pragma unroll
-                for (int w = 1; w < G::WN; ++w) v += rd[w * 64 + r];
+                for (int w = 1; w < G::WN; ++w) v += rd[w * G::ER + r];
                 a.part_cross[((int64_t)ntile * a.ksplit + kc) * a.d_out + mrow] = v;
             }
         }
@@ -1761,7 +1767,7 @@ __device__ __forceinline__ void norm_finalize_body(const float* __restrict__ pba
 // group runs each stage of every member in a single grid: member j owns
 // workgroups [start[j], start[j+1]), and its starts are multiples of the XCD
 // count, so member-local workgroup ids keep their XCD.
-__global__ __launch_bounds__(Big::NTH) void w0_pass_big(W0PassArgs a) {
+__global__ __launch_bounds__(Big::NTH, Big::WG_PER_CU * Big::NW / 4) void w0_pass_big(W0PassArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[Big::LDS_BYTES];
     w0_pass_big_body(a, blockIdx.x, smem);
 }
@@ -1820,7 +1826,7 @@ __device__ __forceinline__ int group_member(const Group<A>& g, int id) {
     return j;
 }
 
-__global__ __launch_bounds__(Big::NTH) void w0_pass_big_group(Group<W0PassArgs> g) {
+__global__ __launch_bounds__(Big::NTH, Big::WG_PER_CU * Big::NW / 4) void w0_pass_big_group(Group<W0PassArgs> g) {
     __shared__ __attribute__((aligned(1024))) char smem[Big::LDS_BYTES];
     const int j = group_member(g, blockIdx.x);
     w0_pass_big_body(g.a[j], blockIdx.x - g.start[j], smem);
@@ -2098,12 +2104,12 @@ NormPlan plan_norm_impl(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool 
         p.nkt_w0 = (int)((d_in + p.bk - 1) / p.bk);
         p.nkt_g = (int)((r + p.bk - 1) / p.bk);
         const int nkt = p.nkt_w0 + p.nkt_g;
-        // One 136 KB workgroup fits a CU.  Measured: a single round of
-        // workgroups beats several, whose every round pays the cold start and
-        // the epilogue again; so split K as far as one round allows (at most
-        // 256 workgroups), keeping >= 8 k-tiles per workgroup.
+        // Measured: a single round of workgroups beats several, whose every
+        // round pays the cold start and the epilogue again; so split K as far
+        // as one round allows, keeping >= 8 k-tiles per workgroup.
         const int64_t tiles = (int64_t)p.n_mtiles * p.n_ntiles;
-        ks = tiles >= kNumCU ? 1 : (int)(kNumCU / tiles);
+        const int64_t round = (int64_t)kNumCU * Big::WG_PER_CU;
+        ks = tiles >= round ? 1 : (int)(round / tiles);
         if (ks > 64) ks = 64;
         while (ks > 1 && nkt / ks < 8) --ks;
     } else {
