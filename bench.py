@@ -80,13 +80,21 @@ NORM_SOURCES = ("dora_adapter_factored_amd/csrc/norm.hip", "dora_adapter_factore
 
 
 def norm_source_digest():
-    """sha256 over the sources the norm kernels are built from; a stored
-    traffic figure is only valid for the kernels it was counted on."""
+    """sha256 over what the norm kernels are built from (their sources, the
+    hipcc flags and the ROCm version); a stored traffic or kernel-trace
+    figure is only valid for the kernels it was taken on."""
     import hashlib
+    from dora_adapter_factored_amd.build import HIPCC_FLAGS
     h = hashlib.sha256()
     for rel in NORM_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(HIPCC_FLAGS).encode())
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            h.update(f.read().strip().encode())
+    except OSError:
+        h.update(b"rocm-version-unknown")
     return h.hexdigest()
 
 
@@ -245,6 +253,9 @@ def main():
     ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--ceilings", action="store_true",
+                    help="measure the ceilings only (MFMA-only loops, streams, one CU's reads, the W0 pass's "
+                         "access pattern) and print them as one JSON line")
     args = ap.parse_args()
     args.steps_given = any(a.startswith("--steps") for a in sys.argv[1:])
     args.warmup_given = any(a.startswith("--warmup") for a in sys.argv[1:])
@@ -257,6 +268,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.ceilings:
+        from dora_adapter_factored_amd import ceilings as CL
+        print(json.dumps({"metric": "measured ceilings (MI355X)", "ceilings": CL.measure(dev, full=True)}), flush=True)
+        return
     if args.config == 5:
         return sweep_main(args, D, dev)
     spec = DI.CONFIGS[args.config]
@@ -352,18 +367,30 @@ def main():
     ms_per_mcycle = max(cal[0].elapsed_time(cal[1]), 1e-3)
     spin = int(1_000_000 * (0.06 * args.steps + 2.0) / ms_per_mcycle)   # ~60 us of host time per call
 
+    nbatch = 10 if args.steps >= 20 else 1   # batches: their means give p10 / p90
+
     def per_call(fn):
+        """Mean seconds per call over K back-to-back calls, and p10 / p90 of
+        the means of nbatch consecutive batches of those calls (events between
+        batches only)."""
         for i in range(3):
             fn(sets[i % nsets])
         torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nbatch + 1)]
         torch.cuda._sleep(spin)
         ev[0].record(stream)
-        for i in range(args.steps):
-            fn(sets[i % nsets])
-        ev[1].record(stream)
+        for b in range(nbatch):
+            for i in range(b * args.steps // nbatch, (b + 1) * args.steps // nbatch):
+                fn(sets[i % nsets])
+            ev[b + 1].record(stream)
         torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) * 1e-3 / args.steps
+        total = ev[0].elapsed_time(ev[nbatch]) * 1e-3 / args.steps
+        per = [ev[b].elapsed_time(ev[b + 1]) * 1e-3 / ((b + 1) * args.steps // nbatch - b * args.steps // nbatch)
+               for b in range(nbatch)]
+        per_call.spread[fn.__name__] = (float(np.percentile(per, 10)), float(np.percentile(per, 90)))
+        return total
+
+    per_call.spread = {}
 
     t_norm = per_call(run_norm)
     t_fwd = per_call(run_fwd)
@@ -373,6 +400,10 @@ def main():
     t_bwdi = per_call(run_bwd_inner)
     # the merge for serving: measured beside the step
     t_merge = per_call(run_merge)
+    # measured ceilings (MFMA-only loops, streams, one CU's reads), same process
+    from dora_adapter_factored_amd import ceilings as CL
+    ceil = CL.measure(dev, full=False)
+    print(f"[bench] ceilings {ceil}", file=sys.stderr, flush=True)
     mb = merge_bytes(d_out, d_in, r, esz)
     db_, bib = compose_dual_bytes(T, d_out, esz), compose_bwd_inner_bytes(T, d_out, esz)
     F = norm_flops(d_out, d_in, r)
@@ -388,6 +419,14 @@ def main():
         if "w0_pass" in kern:
             traced["w0_pass_TFLOPs"] = round(w0_pass_flops(d_out, d_in, r) / (kern["w0_pass"] * 1e-6) / 1e12, 1)
 
+    hbm_read_ceiling = ceil["cu_read_hbm"]["chip_GBps"]
+    spread = per_call.spread
+
+    def ms_spread(name):
+        lo, hi = spread.get(name, (None, None))
+        return None if lo is None else [round(lo * 1e3, 4), round(hi * 1e3, 4)]
+
+    norm_ceiling = (ceil["mfma_32x32x16_bf16_TFLOPs"] if dt != torch.float32 else None)
     out = {
         "metric": METRIC,
         "value": round(norm_tflops, 2),
@@ -404,28 +443,45 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
         "config": {"workload": spec.name, "d_out": d_out, "d_in": d_in, "r": r, "tokens": T, "s": s,
                    "rotating_input_sets": nsets},
-        "norm": {"ms": round(t_norm * 1e3, 4), "TFLOPs": round(norm_tflops, 2),
-                 "frac_mfma_peak": round(norm_tflops / peak_mm, 4), "algorithmic_flop": F,
+        "norm": {"ms": round(t_norm * 1e3, 4), "ms_p10_p90": ms_spread("run_norm"), "TFLOPs": round(norm_tflops, 2),
+                 "frac_mfma_peak": round(norm_tflops / peak_mm, 4),
+                 "frac_measured_ceiling": (round(norm_tflops / norm_ceiling, 4) if norm_ceiling else None),
+                 "frac_measured_hbm_read": round(nb / t_norm / 1e9 / hbm_read_ceiling, 4),
+                 "algorithmic_flop": F,
                  "algorithmic_bytes": nb, "GBps": round(nb / t_norm / 1e9, 1),
                  "frac_hbm_peak": round(nb / t_norm / 1e9 / PEAK_HBM_GBS, 4),
                  "workspace_bytes": int(ws_norm.numel()), "kernels_traced": traced},
-        "compose_fwd": {"ms": round(t_fwd * 1e3, 4), "GBps": round(fwd_gbs, 1),
+        "compose_fwd": {"ms": round(t_fwd * 1e3, 4), "ms_p10_p90": ms_spread("run_fwd"), "GBps": round(fwd_gbs, 1),
                         "frac_hbm_peak": round(fwd_gbs / PEAK_HBM_GBS, 4),
+                        "frac_measured_ceiling": round(fwd_gbs / ceil["stream_2r1w_GBps"], 4),
                         "frac_measured_copy": round(fwd_gbs / calib["GBps"], 4), "algorithmic_bytes": fb},
-        "compose_bwd": {"ms": round(t_bwd * 1e3, 4), "GBps": round(bwd_gbs, 1),
+        "compose_bwd": {"ms": round(t_bwd * 1e3, 4), "ms_p10_p90": ms_spread("run_bwd"), "GBps": round(bwd_gbs, 1),
                         "frac_hbm_peak": round(bwd_gbs / PEAK_HBM_GBS, 4),
+                        "frac_measured_ceiling": round(bwd_gbs / ceil["stream_3r2w_GBps"], 4),
                         "frac_measured_copy": round(bwd_gbs / calib["GBps"], 4), "algorithmic_bytes": bb},
-        "compose_dual": {"ms": round(t_dual * 1e3, 4), "GBps": round(db_ / t_dual / 1e9, 1),
-                         "frac_hbm_peak": round(db_ / t_dual / 1e9 / PEAK_HBM_GBS, 4), "algorithmic_bytes": db_},
-        "compose_bwd_inner": {"ms": round(t_bwdi * 1e3, 4), "GBps": round(bib / t_bwdi / 1e9, 1),
+        "compose_dual": {"ms": round(t_dual * 1e3, 4), "ms_p10_p90": ms_spread("run_dual"),
+                         "GBps": round(db_ / t_dual / 1e9, 1),
+                         "frac_hbm_peak": round(db_ / t_dual / 1e9 / PEAK_HBM_GBS, 4),
+                         "frac_measured_ceiling": round(db_ / t_dual / 1e9 / ceil["stream_2r2w_GBps"], 4),
+                         "algorithmic_bytes": db_},
+        "compose_bwd_inner": {"ms": round(t_bwdi * 1e3, 4), "ms_p10_p90": ms_spread("run_bwd_inner"),
+                              "GBps": round(bib / t_bwdi / 1e9, 1),
                               "frac_hbm_peak": round(bib / t_bwdi / 1e9 / PEAK_HBM_GBS, 4),
+                              "frac_measured_ceiling": round(bib / t_bwdi / 1e9 / ceil["stream_2r2w_GBps"], 4),
                               "algorithmic_bytes": bib},
-        "merge": {"ms": round(t_merge * 1e3, 4), "GBps": round(mb / t_merge / 1e9, 1),
-                  "frac_hbm_peak": round(mb / t_merge / 1e9 / PEAK_HBM_GBS, 4), "algorithmic_bytes": mb,
-                  "TFLOPs": round(2 * d_out * d_in * r / t_merge / 1e12, 1)},
+        "merge": {"ms": round(t_merge * 1e3, 4), "ms_p10_p90": ms_spread("run_merge"), "GBps": round(mb / t_merge / 1e9, 1),
+                  "frac_hbm_peak": round(mb / t_merge / 1e9 / PEAK_HBM_GBS, 4),
+                  "frac_measured_ceiling": round(mb / t_merge / 1e9 / ceil["stream_2r1w_GBps"], 4),
+                  "algorithmic_bytes": mb, "TFLOPs": round(2 * d_out * d_in * r / t_merge / 1e12, 1)},
         "copy_calibration": calib,
+        "measured_ceilings": {k: (round(v, 1) if isinstance(v, float) else {kk: round(vv, 1) for kk, vv in v.items()})
+                              for k, v in ceil.items()},
         "roofline": norm_roofline(F, nb, t_norm, peak_mm, stored_traffic(spec.name)),
     }
+    rf = out["roofline"]
+    ceiling = norm_ceiling if rf["bound"] == "mfma" else hbm_read_ceiling
+    rf["measured_ceiling"] = round(ceiling, 1) if ceiling else None
+    rf["frac_measured_ceiling"] = round(rf["achieved"] / ceiling, 4) if ceiling else None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(layer, args.cpu_budget)

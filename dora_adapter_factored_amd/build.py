@@ -21,6 +21,9 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libdora_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ("dora_capi.hip", "compose.hip", "norm.hip", "merge.hip")
+# measurement-only kernels (bench.py --ceilings), a library of their own
+CEILINGS_LIB_PATH = os.path.join(PKG, "libdora_ceilings.so")
+CEILINGS_SOURCES = ("ceilings.hip",)
 ARCH = "gfx950"
 
 # Packed-fp32 VALU ops are kept out of the device code.  MFMA results are
@@ -52,22 +55,25 @@ def _run(cmd):
 
 
 def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every source and link the shared library; returns its path."""
+    """Compile every source and link the shared libraries (the DoRA library
+    and the measurement-only ceilings library); returns the DoRA library's
+    path."""
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     flags = HIPCC_FLAGS + list(extra_flags)
-    objs, cmds = [], []
-    for src in SOURCES:
+    objs, cmds = {}, []
+    for src in SOURCES + CEILINGS_SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        objs.append(obj)
+        objs[src] = obj
         cmds.append([hipcc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)
-    tmp = LIB_PATH + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB_PATH)
+    for path, srcs in ((LIB_PATH, SOURCES), (CEILINGS_LIB_PATH, CEILINGS_SOURCES)):
+        tmp = path + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *(objs[s] for s in srcs)])
+        os.replace(tmp, path)
     return LIB_PATH
 
 
