@@ -253,6 +253,10 @@ def main():
     ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--crossover", action="store_true",
+                    help="time the fused compose forward/backward against the eager op sequence (torch ops on "
+                         "the GPU, the pages' comparator) over the workloads' activation shapes and a small-shape "
+                         "grid, and print them as one JSON line")
     ap.add_argument("--ceilings", action="store_true",
                     help="measure the ceilings only (MFMA-only loops, streams, one CU's reads, the W0 pass's "
                          "access pattern) and print them as one JSON line")
@@ -268,6 +272,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.crossover:
+        return crossover_main(args, D, dev)
     if args.ceilings:
         from dora_adapter_factored_amd import ceilings as CL
         print(json.dumps({"metric": "measured ceilings (MI355X)", "ceilings": CL.measure(dev, full=True)}), flush=True)
@@ -486,6 +492,112 @@ def main():
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(layer, args.cpu_budget)
     print(json.dumps(out), flush=True)
+
+
+def eager_compose_fwd(base, lora, g, s):
+    """The compose as separate elementwise torch ops (the comparator the pages
+    time their fused kernel against): y = base + (g - 1) * base + (g * s) * lora,
+    each op a kernel over [T, d_out] in the activation dtype."""
+    gb = g.to(base.dtype)
+    return base + (gb - 1) * base + (gb * s) * lora
+
+
+def eager_compose_bwd(dy, base, lora, g, wnorm, s, eps):
+    """The backward as separate torch ops, norm detached: d_base = g dy,
+    d_lora = (g s) dy, d_m = sum_t dy (base + s lora) / max(wnorm, eps)."""
+    gb = g.to(dy.dtype)
+    d_base = gb * dy
+    d_lora = (gb * s) * dy
+    d_m = (dy * (base + s * lora)).float().sum(0) / wnorm.clamp_min(eps)
+    return d_base, d_lora, d_m
+
+
+CROSSOVER_SHAPES = (
+    # (tokens, d_out): the workloads' activation shapes ...
+    (2048, 4096), (2048, 8192), (4096, 28672), (2048, 1024), (2048, 5120), (2048, 27648),
+    # ... and a small-shape grid through 2048 x 6144, d_out down to 1024
+    (128, 1024), (128, 4096), (512, 1024), (512, 2048), (512, 6144), (1024, 1024), (1024, 4096),
+    (1024, 6144), (2048, 2048), (2048, 6144), (256, 8192), (8192, 8192),
+)
+
+
+def crossover_main(args, D, dev):
+    """Fused compose forward / backward (this library) against the eager op
+    sequence on the same GPU, per shape: time per call issued from the host,
+    time per call replayed from a captured HIP graph (no host issue cost),
+    and the ratios."""
+    eps = D.default_eps(torch.bfloat16)
+    gen = torch.Generator(device=dev).manual_seed(5)
+    stream = torch.cuda.current_stream(dev)
+    rows = []
+    for T, d_out in CROSSOVER_SHAPES:
+        act = T * d_out * 2
+        nsets = max(2, int(np.ceil(2 * MALL_BYTES / (5 * act))) + 1) if 5 * act < 2 * MALL_BYTES else 2
+        nsets = min(nsets, 64)
+        sets = []
+        for _ in range(nsets):
+            mk = lambda: torch.randn(T, d_out, device=dev, generator=gen).to(torch.bfloat16)  # noqa: E731
+            sets.append(dict(base=mk(), lora=mk(), dy=mk(), y=torch.empty(T, d_out, dtype=torch.bfloat16, device=dev),
+                             db=torch.empty(T, d_out, dtype=torch.bfloat16, device=dev),
+                             dl=torch.empty(T, d_out, dtype=torch.bfloat16, device=dev),
+                             dm=torch.empty(d_out, device=dev)))
+        g = 1 + 1e-3 * torch.randn(d_out, device=dev, generator=gen)
+        wn = 1 + 1e-3 * torch.randn(d_out, device=dev, generator=gen)
+        ws = torch.empty(max(1, D.compose_backward_workspace_size(T, d_out)), dtype=torch.uint8, device=dev)
+        s = 1.0
+        fns = {
+            "fused_fwd": lambda st: D.compose(st["base"], st["lora"], g, s, out=st["y"]),
+            "eager_fwd": lambda st: eager_compose_fwd(st["base"], st["lora"], g, s),
+            "fused_bwd": lambda st: D.compose_backward(st["dy"], st["base"], st["lora"], g, wn, s, eps,
+                                                       d_base=st["db"], d_lora=st["dl"], d_m=st["dm"], ws=ws),
+            "eager_bwd": lambda st: eager_compose_bwd(st["dy"], st["base"], st["lora"], g, wn, s, eps),
+        }
+        reps = max(20, min(400, int(2e9 / act)))
+        res = {}
+        for name, fn in fns.items():
+            # issued from the host, call after call (what a framework sees)
+            for i in range(3):
+                fn(sets[i % nsets])
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(int(1_000_000 * reps * 0.08))   # covers the host's issue of all reps calls
+            e0.record(stream)
+            for i in range(reps):
+                fn(sets[i % nsets])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) * 1e3 / reps   # us per call
+            # replayed from one captured HIP graph of 20 calls (the GPU's time alone)
+            side = torch.cuda.Stream(dev)
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                for i in range(3):
+                    fn(sets[i % nsets])
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(20):
+                    fn(sets[i % nsets])
+            graph.replay()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(10):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[name + "_graph"] = e0.elapsed_time(e1) * 1e3 / 200
+            del graph
+        rows.append({"tokens": T, "d_out": d_out, **{k: round(v, 2) for k, v in res.items()},
+                     "fwd_speedup": round(res["eager_fwd"] / res["fused_fwd"], 2),
+                     "bwd_speedup": round(res["eager_bwd"] / res["fused_bwd"], 2),
+                     "fwd_speedup_graph": round(res["eager_fwd_graph"] / res["fused_fwd_graph"], 2),
+                     "bwd_speedup_graph": round(res["eager_bwd_graph"] / res["fused_bwd_graph"], 2)})
+        print(f"[crossover] {rows[-1]}", file=sys.stderr, flush=True)
+        del sets, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "fused compose vs eager op sequence, us per call (bf16, one MI355X)",
+                      "rows": rows}), flush=True)
 
 
 SWEEP_METRIC = "many-module sweep: norm + compose fwd/bwd ms per step (64 layers x 7 projections, r=384 bf16)"

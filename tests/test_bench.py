@@ -86,3 +86,25 @@ def test_traced_kernel_times_are_read_only_for_the_current_sources(tmp_path, mon
     assert bench.stored_norm_kernels("absent") is None
     # the W0 pass's own work at 8192^2 r = 384: the extended contraction and the base squares
     assert bench.w0_pass_flops(8192, 8192, 384) / 1e9 == pytest.approx(54.09, rel=1e-3)
+
+
+def test_eager_comparator_computes_the_compose():
+    # the bench's eager op sequence (the pages' comparator) computes what the
+    # oracle does, here in fp32 on the CPU
+    import numpy as np
+    import torch
+
+    import bench
+    import oracle
+    rng = np.random.default_rng(3)
+    T, d = 7, 13
+    base, lora, dy = (rng.standard_normal((T, d)) for _ in range(3))
+    g, wn = 1 + 0.1 * rng.standard_normal(d), 1 + 0.1 * rng.standard_normal(d)
+    s, eps = 0.75, 1e-6
+    t = lambda a: torch.tensor(a, dtype=torch.float32)  # noqa: E731
+    y = bench.eager_compose_fwd(t(base), t(lora), t(g), s).double().numpy()
+    assert np.allclose(y, oracle.compose_forward(base, lora, g, s), rtol=1e-5, atol=1e-5)
+    db, dl, dm = bench.eager_compose_bwd(t(dy), t(base), t(lora), t(g), t(wn), s, eps)
+    r_db, r_dl, r_dm = oracle.compose_backward(dy, base, lora, g, wn, s, eps)
+    for got, ref in ((db, r_db), (dl, r_dl), (dm, r_dm)):
+        assert np.allclose(got.double().numpy(), ref, rtol=1e-5, atol=1e-5)
