@@ -535,10 +535,23 @@ __device__ __forceinline__ FragSrc make_frag_src(const Operand& o, int64_t row0,
     return f;
 }
 
+// f if p else g, field by field (p uniform: scalar selects, no branch).
+__device__ __forceinline__ FragSrc select_src(bool p, const FragSrc& f, const FragSrc& g) {
+    FragSrc o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o.rsrc[q] = p ? f.rsrc[q] : g.rsrc[q];
+    o.ld_bytes = p ? f.ld_bytes : g.ld_bytes;
+    o.kmax_bytes = p ? f.kmax_bytes : g.kmax_bytes;
+    o.lane_off = p ? f.lane_off : g.lane_off;
+    o.kq_bytes = f.kq_bytes;
+    return o;
+}
+
 // Load the fragments of NB consecutive 16-row blocks for every k-step of the
-// k-tile starting at element k0: regs[(ks * NB + b) * FL + h].
+// k-tile starting at element k0: regs[(ks * NB + b) * FL + h].  With live
+// false every offset is out of range: the loads read zeros and move no data.
 template <typename E, int NB>
-__device__ __forceinline__ void load_frags(const FragSrc& f, int64_t k0, u32x4_t* regs) {
+__device__ __forceinline__ void load_frags(const FragSrc& f, int64_t k0, u32x4_t* regs, bool live = true) {
     typedef Mma<E> M;
     constexpr int FR = M::BK / 32, FL = M::FL;
 #pragma unroll
@@ -548,7 +561,7 @@ __device__ __forceinline__ void load_frags(const FragSrc& f, int64_t k0, u32x4_t
         for (int b = 0; b < NB; ++b) {
 #pragma unroll
             for (int h = 0; h < FL; ++h) {
-                const bool ok = kb + f.kq_bytes + h * 16 < f.kmax_bytes;
+                const bool ok = live && kb + f.kq_bytes + h * 16 < f.kmax_bytes;
                 const int voff = ok ? f.lane_off + b * 16 * f.ld_bytes + kb + h * 16 : kOutOfRange;
                 regs[(ks * NB + b) * FL + h] =
                     __builtin_bit_cast(u32x4_t, raw_buffer_load_b128(f.rsrc, voff, 0, 0));
@@ -559,15 +572,22 @@ __device__ __forceinline__ void load_frags(const FragSrc& f, int64_t k0, u32x4_t
 
 // W0 pass main loop, narrow form (small r: 4 waves stacked along d_out, MT
 // blocks each, all NT blocks of r per wave).  Nothing is shared between
-// waves, so both operands are loaded straight into registers, four register
-// sets deep (three tiles in flight), with no LDS and no barrier.  K-walk
+// waves, so both operands are loaded straight into registers, D register
+// sets deep (D - 1 tiles in flight), with no LDS and no barrier.  K-walk
 // rotated as in the wide form.
+// Every step issues its loads unconditionally: the phase picks the operand
+// buffers by scalar selects, and the walk is padded to a multiple of D with
+// empty tiles whose loads are out of range (zeros, no data moved; they add
+// nothing to U, the base or the Gram blocks).  The load stream is then the
+// same every step, so the compiler's own waits on each register set stay at
+// (D - 2) tiles in flight; loads under a branch made it wait for every
+// outstanding load before each MFMA, i.e. one memory latency per k-tile.
 // One wave's rows [mrow0, mrow0 + 16 MT) over k-tiles [kt_begin, kt_end).
 // With GIP, the right fragments (rows of A) also feed this K range's Gram
 // blocks G_c = A_c A_c^T: gacc holds the upper blocks (b1 <= b2) in order.
 // bsum[mt] receives the base partial of row mrow0 + mt * 16 + lane % 16 in
 // every lane (zero without want_base or for an empty range).
-template <typename E, int MT, int NT, bool GIP, int NG>
+template <typename E, int MT, int NT, bool GIP, int NG, int D>
 __device__ __forceinline__ void mainloop_w0_narrow(const Contraction& c, int64_t mrow0, int64_t n0, int kt_begin,
                                                    int kt_end, int rot, bool want_base, f32x4_t (&acc)[MT][NT],
                                                    f32x4_t (&gacc)[NG], float (&bsum)[MT]) {
@@ -588,20 +608,18 @@ __device__ __forceinline__ void mainloop_w0_narrow(const Contraction& c, int64_t
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) bs[mt] = 0.0f;
 
+    // k-tile of walk step i (steps past the walk: its first tile, loaded empty)
     auto tile = [&](int i) __attribute__((always_inline)) {
         int t = i + rot;
         if (t >= n) t -= n;
-        return kt_begin + t;
+        return i < n ? kt_begin + t : kt_begin;
     };
     auto load = [&](int i, u32x4_t* regs) __attribute__((always_inline)) {
         const int kt = tile(i);
-        if (kt < c.nkt0) {
-            load_frags<E, MT>(L0, (int64_t)kt * M::BK, regs);
-            load_frags<E, NT>(R0, (int64_t)kt * M::BK, regs + NLW);
-        } else {
-            load_frags<E, MT>(L1, (int64_t)(kt - c.nkt0) * M::BK, regs);
-            load_frags<E, NT>(R1, (int64_t)(kt - c.nkt0) * M::BK, regs + NLW);
-        }
+        const bool ph0 = kt < c.nkt0;
+        const int64_t k0 = (int64_t)(ph0 ? kt : kt - c.nkt0) * M::BK;
+        load_frags<E, MT>(select_src(ph0, L0, L1), k0, regs, i < n);
+        load_frags<E, NT>(select_src(ph0, R0, R1), k0, regs + NLW, i < n);
     };
     auto compute = [&](const u32x4_t* regs, bool base, bool gram) __attribute__((always_inline)) {
 #pragma unroll
@@ -629,31 +647,24 @@ __device__ __forceinline__ void mainloop_w0_narrow(const Contraction& c, int64_t
             }
         }
     };
-    auto step = [&](int i, u32x4_t* cur, u32x4_t* nxt3) __attribute__((always_inline)) {
-        if (i + 2 < n)
-            wait_vmcnt<2 * PER>();
-        else if (i + 1 < n)
-            wait_vmcnt<PER>();
-        else
-            wait_vmcnt<0>();
-        if (i + 3 < n) load(i + 3, nxt3);   // set of tile i - 1, already consumed
-        const bool ph0 = tile(i) < c.nkt0;
-        compute(cur, want_base && ph0, ph0);
-    };
-
-    u32x4_t s0[PER], s1[PER], s2[PER], s3[PER];
-    load(0, s0);
-    if (n > 1) load(1, s1);
-    if (n > 2) load(2, s2);
-    for (int i = 0; i < n; i += 4) {
-        step(i, s0, s3);
-        if (i + 1 >= n) break;
-        step(i + 1, s1, s0);
-        if (i + 2 >= n) break;
-        step(i + 2, s2, s1);
-        if (i + 3 >= n) break;
-        step(i + 3, s3, s2);
+    static_assert(D >= 2 && (D - 1) * PER < 64, "register ring depth");
+    // step t waits until only steps t + 1 .. t + D - 2 are in flight, then
+    // step t + D - 1 goes into the set of step t - 1 (already consumed)
+    const int nsteps = (n + D - 1) / D * D;
+    u32x4_t sets[D][PER];
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j) load(j, sets[j]);
+    for (int i = 0; i < nsteps; i += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const int t = i + j;
+            wait_vmcnt<(D - 2) * PER>();
+            load(t + D - 1, sets[(j + D - 1) % D]);
+            const bool ph0 = tile(t) < c.nkt0;
+            compute(sets[j], want_base && ph0, ph0);
+        }
     }
+    wait_vmcnt<0>();   // the empty loads issued past the walk
     if (want_base) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -692,6 +703,15 @@ struct W0Form {
     static constexpr bool WIDE = ALIGNED && WM == 1 && WN >= 4 && MT == 8;
     static constexpr bool NARROW = ALIGNED && WN == 1;
 };
+
+// Register sets per wave of the narrow loops: two, i.e. one k-tile in flight
+// while the previous one is computed.  Measured on MI355X at r <= 64: two
+// sets were the fastest or within 2% of it on every shape tried (4096^2
+// r = 32: 16.7 us against 17.6 with four; 28672 x 8192 r = 32: 130 against
+// 131; 8192^2 r = 64: 70.7 against 74.1), three and six were slower: with
+// hundreds of waves streaming W0, more requests in flight per wave only add
+// contention in the memory system.
+constexpr int kNarrowDepth = 2;
 
 // Narrow bf16 tiles with r <= 32 form the Gram term inside the W0 pass.  The
 // norm's Gram term is a sum over K of per-chunk terms,
@@ -771,7 +791,7 @@ __global__ __launch_bounds__(WM * WN * 64, (ALIGNED && WN == 1 && NT == 1) ? 3 :
     else if constexpr (F::NARROW) {
         const int64_t mrow0 = m0 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * MT * 16;
         float bsum[MT];
-        mainloop_w0_narrow<E, MT, NT, GIP::value, GIP::NG>(a.c, mrow0, n0, kt_begin, kt_end, rot,
+        mainloop_w0_narrow<E, MT, NT, GIP::value, GIP::NG, kNarrowDepth>(a.c, mrow0, n0, kt_begin, kt_end, rot,
                                                            base_dst != nullptr, acc, gacc, bsum);
         if (base_dst) {
             const int lane = threadIdx.x & 63;
@@ -935,6 +955,7 @@ struct W0RowsArgs {
 
 constexpr int kRowsWaves = 8;
 constexpr int kRowsPerWg = 16;
+constexpr int kRowsDepth = kNarrowDepth;
 
 template <int NT>
 __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) {
@@ -970,9 +991,8 @@ __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) 
     // first wait covers it)
     float m_row = 0.0f;
     if (threadIdx.x < kRowsPerWg && a.m && m0 + threadIdx.x < a.d_out) m_row = a.m[m0 + threadIdx.x];
-    mainloop_w0_narrow<E, 1, NT, true, GIP::NG>(a.c, m0, 0, kt_begin, kt_end, 0, true, acc, gacc, bsum);
-
-    // B rows [m0, m0 + 16), columns [0, BN) (zeros past r and past d_out)
+    // B rows [m0, m0 + 16), columns [0, BN) (zeros past r and past d_out),
+    // staged by wave 0 ahead of the K walk, which uses no LDS
     if (wave == 0) {
         const int64_t rb = a.r * 2;
         const uint64_t addr = reinterpret_cast<uint64_t>(static_cast<const char*>(a.B) + m0 * rb);
@@ -993,6 +1013,8 @@ __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) 
             raw_buffer_load_lds(rs, (lds_void_t*)(smem + ins * 1024), 16, voff, 0, 0, 0);
         }
     }
+    mainloop_w0_narrow<E, 1, NT, true, GIP::NG, kRowsDepth>(a.c, m0, 0, kt_begin, kt_end, 0, true, acc, gacc, bsum);
+
     // this wave's Gs_w = (s/2) G_w as bf16 [RP][RP], zero past BN
     {
         char* gs = smem + GS_OFF + wave * GIP::BYTES;
@@ -1914,12 +1936,15 @@ bool gram_in_pass(const NormPlan& p, bool aligned) {
 // Measured on MI355X at r <= 32: up to 2^25 W0 elements (4096 x 8192,
 // 16384 x 2048, ...) it beats the K-split pass plus assembly by 10-25%; at
 // 6144^2 they tie, and from 8192^2 up the K-split pass is faster (its
-// 128-row workgroups keep more bytes in flight than 16-row ones).
+// 128-row workgroups keep more bytes in flight than 16-row ones).  Below one
+// 16-row workgroup per CU the K-split pass wins as well: 2048 x 8192 r = 16
+// 17.5 against 19.0 us, 1024 x 16384 r = 16 20.6 against 33.3 us.
 constexpr int64_t kRowsFormMaxElems = int64_t(1) << 25;
+constexpr int64_t kRowsFormMinRows = int64_t(kRowsPerWg) * kNumCU;
 
 template <typename E>
 bool rows_form(const NormPlan& p, bool aligned) {
-    return gram_in_pass<E>(p, aligned) && p.d_out * p.d_in <= kRowsFormMaxElems;
+    return gram_in_pass<E>(p, aligned) && p.d_out * p.d_in <= kRowsFormMaxElems && p.d_out >= kRowsFormMinRows;
 }
 
 // Arguments and grids of the three stages of one norm (not base-only).

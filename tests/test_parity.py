@@ -101,11 +101,14 @@ def test_norm_edge_shapes(d_out, d_in, r, dt):
     check_rel(host64(g), ref_g, NORM_RTOL[L.W0.dtype], "g")
 
 
-@pytest.mark.parametrize("d_out,d_in,r", [(4096, 8192, 16), (4100, 8200, 16), (8192, 4104, 24)])
+@pytest.mark.parametrize("d_out,d_in,r", [(4096, 8192, 16), (4111, 2056, 24), (4100, 8200, 16), (8192, 4104, 24),
+                                          (1024, 16384, 16)])
 def test_norm_low_rank_forms_at_scale(d_out, d_in, r):
-    # bf16 r <= 32: up to 2^25 W0 elements (4096 x 8192) one whole-row kernel
-    # assembles wnorm and g; above it the K-split W0 pass (each K-chunk's
-    # Gram term formed in the pass) and the assembly kernel run.  Sampled rows.
+    # bf16 r <= 32: from 4096 rows up to 2^25 W0 elements (4096 x 8192; 4111 x
+    # 2056 with a ragged last workgroup and a K tail) one whole-row kernel
+    # assembles wnorm and g; above it, and below 4096 rows (1024 x 16384), the
+    # K-split W0 pass (each K-chunk's Gram term formed in the pass) and the
+    # assembly kernel run.  Sampled rows.
     say(f"[parity] low-rank norm {d_out}x{d_in} r={r}")
     spec = DI.custom_spec(d_out, d_in, r, 1, dtype="bf16", s=1.5, b_std=0.05)
     L = DI.make_layer(spec, 60 + r + d_out % 7, device=DEV, activations=False, gen_device="cuda")
@@ -287,6 +290,51 @@ def test_compose_forward_config(cfg):
     rows = None if cfg in (1, 2) else sample_rows(L.spec.T, 256, seed=cfg)
     _compose_check(L, g32, rows=rows, tag=f"cfg{cfg}")
     _compose_check(L, g32, rows=rows, delta=True, tag=f"cfg{cfg}")
+
+
+def _peak_error(got, ref):
+    """Largest |got - ref|, absolute and relative to the largest |ref|."""
+    err = np.abs(np.asarray(got, np.float64) - ref)
+    return float(err.max()), float(err.max() / np.abs(ref).max())
+
+
+def test_compose_error_near_unit_g():
+    # [ScalingDoRA] §3 (compose stability) compares, in bf16 at [2048, 8192]
+    # with g close to 1, the peak error of the composition evaluated as
+    # g * (base + s lora) against the form base + (g - 1) base + g s lora,
+    # both against fp64.  Here three evaluations share the bf16 branch
+    # outputs and the fp32 g of the 8192^2 r=384 layer (g = 1 + O(1e-3)):
+    #   naive   g * (base + s lora), each op a bf16 torch op (g rounded to bf16)
+    #   stable  base + (g - 1) base + (g s) lora, each op a bf16 torch op
+    #           ((g - 1) and g s formed in fp32, then rounded to bf16)
+    #   fused   the compose kernel: the stable form in fp32, rounded once.
+    # The kernel's error must be the smallest of the three, within bf16's
+    # half-spacing at the result plus fp32 rounding, and the test prints the
+    # three peaks so the ratio can be set beside the pages' figure.
+    L = config_layer(3)
+    g32 = oracle_g_f32(L)
+    s = L.spec.s
+    assert abs(float(g32.mean()) - 1.0) < 1e-2 and float(g32.std()) < 1e-2
+    gd = g32.to(DEV)
+    base, lora = L.base_out, L.lora_out
+    y_fused = D.compose(base, lora, gd, s)
+    bf = torch.bfloat16
+    y_naive = gd.to(bf)[None, :] * (base + s * lora)
+    y_stable = base + (gd - 1.0).to(bf)[None, :] * base + (gd * s).to(bf)[None, :] * lora
+    torch.cuda.synchronize()
+    ref = oracle.compose_forward(host64(base), host64(lora), oracle.as_f64(g32), s)
+    peaks = {k: _peak_error(host64(v), ref) for k, v in
+             (("fused", y_fused), ("stable", y_stable), ("naive", y_naive))}
+    for k, (a, rel) in peaks.items():
+        say(f"[compose error] {k:6s} peak |err| {a:.4e}  ({rel:.3e} of max |ref|)")
+    say(f"[compose error] naive/fused {peaks['naive'][0] / peaks['fused'][0]:.2f}x  "
+        f"naive/stable {peaks['naive'][0] / peaks['stable'][0]:.2f}x  |ref| max {np.abs(ref).max():.3f}")
+    assert peaks["fused"][0] <= peaks["stable"][0] <= peaks["naive"][0]
+    # one rounding to bf16 plus the fp32 evaluation of three terms
+    err = np.abs(host64(y_fused) - ref)
+    scale = np.abs(host64(base)) * (1 + np.abs(oracle.as_f64(g32) - 1)) + np.abs(oracle.as_f64(g32) * s * host64(lora))
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+    assert np.all(err <= 0.5 * ulp + 2.0 ** -21 * scale)
 
 
 def _bwd_check(L, g32, wn32, delta=False, rows=None, cols=None, tag=""):
