@@ -125,7 +125,7 @@ def stored_traffic(workload):
     if kv.get("source_sha256") != norm_source_digest():
         return None
     try:
-        return int(kv["traffic_bytes_per_call"])
+        return int(kv["traffic_bytes_per_call"]), kv.get("captured", "unknown")
     except (KeyError, ValueError):
         return None
 
@@ -148,7 +148,8 @@ def stored_norm_kernels(workload):
     digest = [l.split(":", 1)[1].strip() for l in lines if l.startswith("source_sha256:")]
     if not digest or digest[0] != norm_source_digest():
         return None
-    out = {}
+    captured = [l.split(":", 1)[1].strip() for l in lines if l.startswith("captured:")]
+    out = {"captured": captured[0] if captured else "unknown"}
     for l in lines:
         if not l.startswith("| "):
             continue
@@ -162,7 +163,7 @@ def stored_norm_kernels(workload):
                     pass
         elif l.startswith("| kernel | dispatches"):
             break
-    return out or None
+    return out if len(out) > 1 else None
 
 
 def w0_pass_flops(d_out, d_in, r):
@@ -409,7 +410,10 @@ def main():
     # measured ceilings (MFMA-only loops, streams, one CU's reads), same process
     from dora_adapter_factored_amd import ceilings as CL
     ceil = CL.measure(dev, full=False)
-    print(f"[bench] ceilings {ceil}", file=sys.stderr, flush=True)
+    # the same streams over arrays the size of one activation: the compose
+    # kernels' fractions are taken against these (per-launch cost included)
+    act = CL.streams(dev, nbytes=T * d_out * esz)
+    print(f"[bench] ceilings {ceil}; at the activation size {act}", file=sys.stderr, flush=True)
     mb = merge_bytes(d_out, d_in, r, esz)
     db_, bib = compose_dual_bytes(T, d_out, esz), compose_bwd_inner_bytes(T, d_out, esz)
     F = norm_flops(d_out, d_in, r)
@@ -421,9 +425,12 @@ def main():
     kern = stored_norm_kernels(spec.name)
     traced = None
     if kern:
-        traced = {"source": f"profiles/kernels_{spec.name}.txt (rocprofv3 kernel trace)", "avg_us": kern}
+        captured = kern.pop("captured")
+        traced = {"stored": True, "source": f"profiles/kernels_{spec.name}.txt (rocprofv3 kernel trace)",
+                  "captured": captured, "avg_us": kern}
         if "w0_pass" in kern:
             traced["w0_pass_TFLOPs"] = round(w0_pass_flops(d_out, d_in, r) / (kern["w0_pass"] * 1e-6) / 1e12, 1)
+    traffic = stored_traffic(spec.name)
 
     hbm_read_ceiling = ceil["cu_read_hbm"]["chip_GBps"]
     spread = per_call.spread
@@ -459,31 +466,36 @@ def main():
                  "workspace_bytes": int(ws_norm.numel()), "kernels_traced": traced},
         "compose_fwd": {"ms": round(t_fwd * 1e3, 4), "ms_p10_p90": ms_spread("run_fwd"), "GBps": round(fwd_gbs, 1),
                         "frac_hbm_peak": round(fwd_gbs / PEAK_HBM_GBS, 4),
-                        "frac_measured_ceiling": round(fwd_gbs / ceil["stream_2r1w_GBps"], 4),
+                        "frac_measured_ceiling": round(fwd_gbs / act["stream_2r1w"], 4),
                         "frac_measured_copy": round(fwd_gbs / calib["GBps"], 4), "algorithmic_bytes": fb},
         "compose_bwd": {"ms": round(t_bwd * 1e3, 4), "ms_p10_p90": ms_spread("run_bwd"), "GBps": round(bwd_gbs, 1),
                         "frac_hbm_peak": round(bwd_gbs / PEAK_HBM_GBS, 4),
-                        "frac_measured_ceiling": round(bwd_gbs / ceil["stream_3r2w_GBps"], 4),
+                        "frac_measured_ceiling": round(bwd_gbs / act["stream_3r2w"], 4),
                         "frac_measured_copy": round(bwd_gbs / calib["GBps"], 4), "algorithmic_bytes": bb},
         "compose_dual": {"ms": round(t_dual * 1e3, 4), "ms_p10_p90": ms_spread("run_dual"),
                          "GBps": round(db_ / t_dual / 1e9, 1),
                          "frac_hbm_peak": round(db_ / t_dual / 1e9 / PEAK_HBM_GBS, 4),
-                         "frac_measured_ceiling": round(db_ / t_dual / 1e9 / ceil["stream_2r2w_GBps"], 4),
+                         "frac_measured_ceiling": round(db_ / t_dual / 1e9 / act["stream_2r2w"], 4),
                          "algorithmic_bytes": db_},
         "compose_bwd_inner": {"ms": round(t_bwdi * 1e3, 4), "ms_p10_p90": ms_spread("run_bwd_inner"),
                               "GBps": round(bib / t_bwdi / 1e9, 1),
                               "frac_hbm_peak": round(bib / t_bwdi / 1e9 / PEAK_HBM_GBS, 4),
-                              "frac_measured_ceiling": round(bib / t_bwdi / 1e9 / ceil["stream_2r2w_GBps"], 4),
+                              "frac_measured_ceiling": round(bib / t_bwdi / 1e9 / act["stream_2r2w"], 4),
                               "algorithmic_bytes": bib},
         "merge": {"ms": round(t_merge * 1e3, 4), "ms_p10_p90": ms_spread("run_merge"), "GBps": round(mb / t_merge / 1e9, 1),
                   "frac_hbm_peak": round(mb / t_merge / 1e9 / PEAK_HBM_GBS, 4),
                   "frac_measured_ceiling": round(mb / t_merge / 1e9 / ceil["stream_2r1w_GBps"], 4),
                   "algorithmic_bytes": mb, "TFLOPs": round(2 * d_out * d_in * r / t_merge / 1e12, 1)},
         "copy_calibration": calib,
-        "measured_ceilings": {k: (round(v, 1) if isinstance(v, float) else {kk: round(vv, 1) for kk, vv in v.items()})
-                              for k, v in ceil.items()},
-        "roofline": norm_roofline(F, nb, t_norm, peak_mm, stored_traffic(spec.name)),
+        "measured_ceilings": dict({k: (round(v, 1) if isinstance(v, float) else {kk: round(vv, 1) for kk, vv in v.items()})
+                                   for k, v in ceil.items()},
+                                  streams_at_activation_size={"array_bytes": T * d_out * esz,
+                                                              **{k + "_GBps": round(v, 1) for k, v in act.items()}}),
+        "roofline": norm_roofline(F, nb, t_norm, peak_mm, traffic[0] if traffic else None),
     }
+    if traffic:
+        out["roofline"]["traffic_source"] = {"stored": True, "source": f"profiles/norm_traffic_{spec.name}.txt "
+                                             "(rocprofv3 FETCH_SIZE + WRITE_SIZE)", "captured": traffic[1]}
     rf = out["roofline"]
     ceiling = norm_ceiling if rf["bound"] == "mfma" else hbm_read_ceiling
     rf["measured_ceiling"] = round(ceiling, 1) if ceiling else None

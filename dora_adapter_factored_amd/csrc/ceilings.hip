@@ -135,6 +135,37 @@ __global__ __launch_bounds__(256) void stream_r3w2(const u32x4_t* a, const u32x4
     }
 }
 
+// The same three streams, blocked: workgroup w owns packets
+// [w * 256 * kStreamU, (w + 1) * 256 * kStreamU) and every thread issues all
+// of its kStreamU loads per input before its stores (the compose kernels'
+// shape: many workgroups, several 16-byte loads in flight per thread).
+constexpr int kStreamU = 4;
+
+template <int PATTERN>
+__global__ __launch_bounds__(256) void stream_blocked(const u32x4_t* a, const u32x4_t* b, const u32x4_t* c,
+                                                      u32x4_t* y, u32x4_t* z, int64_t n16) {
+    const int64_t i0 = (int64_t)blockIdx.x * (256 * kStreamU) + threadIdx.x;
+    u32x4_t av[kStreamU], bv[kStreamU], cv[kStreamU];
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) {
+        const int64_t i = i0 + (int64_t)u * 256;
+        if (i < n16) {
+            av[u] = __builtin_nontemporal_load(a + i);
+            bv[u] = __builtin_nontemporal_load(b + i);
+            if (PATTERN == 1) cv[u] = __builtin_nontemporal_load(c + i);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) {
+        const int64_t i = i0 + (int64_t)u * 256;
+        if (i < n16) {
+            __builtin_nontemporal_store(av[u] + bv[u], y + i);
+            if (PATTERN == 1) __builtin_nontemporal_store(av[u] ^ cv[u], z + i);
+            if (PATTERN == 2) __builtin_nontemporal_store(av[u] ^ bv[u], z + i);
+        }
+    }
+}
+
 // ------------------------------------------------------------- one CU's read rate
 // Workgroup w reads bytes_per_wg bytes starting at w * stride (stride 0: all
 // workgroups read the same region), reps times, 8 loads of 16 bytes in
@@ -261,12 +292,29 @@ int dora_ceiling_mfma(int kind, int iters, int workgroups, float* out, void* str
 
 // pattern 0: y = f(a, b) (2 reads + 1 write); pattern 1: y, z = f(a, b, c)
 // (3 reads + 2 writes); pattern 2: y, z = f(a, b) (2 reads + 2 writes).
-// Every array holds bytes bytes, a multiple of 16.
+// Every array holds bytes bytes, a multiple of 16.  workgroups >= 1: that
+// many workgroups stride over the arrays; 0: the blocked form, one
+// workgroup per 256 * 4 packets.
 int dora_ceiling_stream(int pattern, const void* a, const void* b, const void* c, void* y, void* z, int64_t bytes,
                         int workgroups, void* stream) {
-    if (!a || !b || !y || bytes <= 0 || bytes % 16 || workgroups < 1) return 1;
+    if (!a || !b || !y || bytes <= 0 || bytes % 16 || workgroups < 0) return 1;
+    if ((pattern == 1 && (!c || !z)) || (pattern == 2 && !z) || pattern < 0 || pattern > 2) return 1;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     typedef dora::u32x4_t V;
+    if (workgroups == 0) {
+        const int64_t n16 = bytes / 16, per = 256 * dora::kStreamU;
+        const int64_t grid = (n16 + per - 1) / per;
+        if (grid > 0x7fffffff) return 1;
+        const V *pa = static_cast<const V*>(a), *pb = static_cast<const V*>(b), *pc = static_cast<const V*>(c);
+        V *py = static_cast<V*>(y), *pz = static_cast<V*>(z);
+        if (pattern == 0)
+            dora::stream_blocked<0><<<(unsigned)grid, 256, 0, st>>>(pa, pb, pc, py, pz, n16);
+        else if (pattern == 1)
+            dora::stream_blocked<1><<<(unsigned)grid, 256, 0, st>>>(pa, pb, pc, py, pz, n16);
+        else
+            dora::stream_blocked<2><<<(unsigned)grid, 256, 0, st>>>(pa, pb, pc, py, pz, n16);
+        return hipGetLastError() == hipSuccess ? 0 : 4;
+    }
     if (pattern == 0) {
         dora::stream_r2w1<<<workgroups, 256, 0, st>>>(static_cast<const V*>(a), static_cast<const V*>(b),
                                                       static_cast<V*>(y), bytes / 16);

@@ -109,7 +109,9 @@ __global__ __launch_bounds__(kThreads) void compose_bwd_vec(const T* dy, const T
     constexpr int N = Pack<T>::N;
     static_assert(kBwdTokenBlock % (kTR * kRPT) == 0, "token block is whole steps");
     constexpr int kSteps = kBwdTokenBlock / (kTR * kRPT);
-    __shared__ float red[kTR - 1][kTC * N];
+    // d_m partials of row lanes 1 .. kTR - 1, element-major: lane tc of a
+    // wave writes and reads consecutive words (no bank conflicts)
+    __shared__ float red[kTR - 1][N][kTC];
     const int tc = threadIdx.x % kTC, tr = threadIdx.x / kTC;
     const int64_t col = ((int64_t)blockIdx.x * kTC + tc) * N;
     const bool active = col < d_out;
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void compose_bwd_vec(const T* dy, const T
     if (DM) {
         if (tr > 0) {
 #pragma unroll
-            for (int e = 0; e < N; ++e) red[tr - 1][tc * N + e] = acc[e];
+            for (int e = 0; e < N; ++e) red[tr - 1][e][tc] = acc[e];
         }
         lds_barrier();   // the d_base / d_lora stores stay in flight
         if (tr == 0 && active) {
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void compose_bwd_vec(const T* dy, const T
             for (int e = 0; e < N; ++e) {
                 float v = acc[e];
 #pragma unroll
-                for (int q = 0; q < kTR - 1; ++q) v += red[q][tc * N + e];
+                for (int q = 0; q < kTR - 1; ++q) v += red[q][e][tc];
                 dm_part[(int64_t)blockIdx.y * d_out + col + e] = v;
             }
         }

@@ -28,6 +28,8 @@ def test_argument_checks(lib):
     assert lib.dora_ceiling_stream(1, FAKE, FAKE, None, FAKE, FAKE, 32, 16, None) == 1   # 3 reads need c
     assert lib.dora_ceiling_stream(2, FAKE, FAKE, None, FAKE, None, 32, 16, None) == 1   # 2 writes need z
     assert lib.dora_ceiling_stream(3, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 16, None) == 1
+    assert lib.dora_ceiling_stream(0, FAKE, FAKE, None, FAKE, None, 32, -1, None) == 1   # negative grid
+    assert lib.dora_ceiling_stream(1, FAKE, FAKE, None, FAKE, FAKE, 32, 0, None) == 1    # blocked form needs c too
     assert lib.dora_ceiling_cu_read(FAKE, 8, 0, 1, 256, 8, FAKE, None) == 1             # under 16 bytes
     assert lib.dora_ceiling_cu_read(FAKE, 1024, 0, 1, 256, 9, FAKE, None) == 1          # more than 8 waves
     assert lib.dora_ceiling_w0_stream(FAKE, FAKE, 8193 * 32, 8192, 384, 1, FAKE, None) == 1   # beyond 32 row tiles
