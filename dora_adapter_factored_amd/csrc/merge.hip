@@ -574,7 +574,188 @@ __global__ __launch_bounds__(kNTh, sizeof(E) == 2 ? 3 : 2) void merge_tile_dma(M
     }
 }
 
+// ------------------------------------------------- large tiles (bf16, aligned)
+// The same pipeline on 256 x 256 output tiles with 8 waves in a 2 x 4 grid,
+// each a 128 x 64 block (4 x 2 blocks of 32 x 32).  Per output element the
+// operand tiles that cross L2 -> LDS halve against 128 x 128 tiles (6 against
+// 12 bytes at r = 384), and each k-step's fragment reads feed 8 MFMAs per
+// wave instead of 4.  One workgroup per CU: 96 KB of ring, the W0 tile (128
+// KB) prefetched into registers after the last stage, the epilogue in four
+// 64-row rounds through the ring's LDS.
+struct BigMerge {
+    static constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NW = WM * WN, NTH = NW * 64;
+    static constexpr int WR = BM / WM, WC = BN / WN;     // rows, columns of one wave
+    static constexpr int MT = WR / 32, NT = WC / 32;      // 32 x 32 blocks of one wave
+    static constexpr int STAGE = (BM + BN) * kRowB;      // 32 KB
+    static constexpr int LDMA = BM / 16 / NW, RDMA = BN / 16 / NW;   // DMA groups per wave and stage
+    static constexpr int DMA = LDMA + RDMA;
+    static constexpr int ER = 64;                        // epilogue rows per round
+    static constexpr int ROUNDS = BM / ER;
+    static constexpr int PITCH = BN + 4;                 // floats per epilogue row (16-byte writes, no conflicts)
+    static constexpr int CPR = BN / 8;                   // 16-byte chunks per output row
+    static constexpr int NH = ER * CPR / NTH;            // output chunks per thread per round
+    static constexpr int NW0 = ROUNDS * NH;
+    static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "DMA groups split evenly across waves");
+    static_assert(kRing * STAGE >= ER * PITCH * 4, "an epilogue round fits in the ring");
+    static_assert(ER % 32 == 0 && WR % ER == 0, "a round takes whole row blocks of one wave row");
+};
+
+template <int NW0, int A>
+__device__ __forceinline__ void wait_stage_big(int after, bool w0) {
+    if constexpr (A < 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (after == A) {
+            if (w0)
+                wait_vmcnt<A * BigMerge::DMA + NW0>();
+            else
+                wait_vmcnt<A * BigMerge::DMA>();
+            return;
+        }
+        wait_stage_big<NW0, A - 1>(after, w0);
+    }
+}
+
+__global__ __launch_bounds__(BigMerge::NTH, 1) void merge_tile_big(MergeArgs a) {
+    typedef bf16_t E;
+    typedef BigMerge G;
+    int mt, nt;
+    if (!merge_tile_of(a, mt, nt)) return;
+    constexpr int VEC = 8;
+    constexpr int NLD = G::NW0 + 1;                      // W0 chunks and one g per thread
+    static_assert(G::NTH >= G::BM, "one thread per tile row fetches its g");
+    __shared__ __attribute__((aligned(1024))) char lds[kRing * G::STAGE + G::BM * 4];
+    float* gsm = reinterpret_cast<float*>(lds + kRing * G::STAGE);   // g of the tile's rows
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / G::WN, wn = wave % G::WN;
+    const int64_t m0 = (int64_t)mt * G::BM, n0 = (int64_t)nt * G::BN;
+    const DmaOp lop = make_dma_op(a.B, a.r * 2, a.d_out, m0, a.r * 2);
+    const DmaOp rop = make_dma_op(a.At, a.r_pad * 2, a.d_in, n0, a.r_pad * 2);
+    const int grow = lane >> 2, slot = lane & 3;
+    const int chunk_b = (slot ^ swz64(grow)) * 16;
+    const int loff = grow * lop.ld_bytes + chunk_b, roff = grow * rop.ld_bytes + chunk_b;
+    const int nk = (int)(a.r_pad / MergeMma<E>::KT);
+
+    auto issue = [&](int kt) {
+        char* st = lds + (kt % kRing) * G::STAGE;
+#pragma unroll
+        for (int q = 0; q < G::LDMA; ++q) dma_group(lop, wave + q * G::NW, kt, loff, chunk_b, st);
+#pragma unroll
+        for (int q = 0; q < G::RDMA; ++q) dma_group(rop, wave + q * G::NW, kt, roff, chunk_b, st + G::BM * kRowB);
+    };
+    const E* W0 = static_cast<const E*>(a.W0);
+    // W0 chunks and the g of one tile row per thread, loaded unconditionally
+    // (addresses clamped into the tensors) so that every wave issues the same
+    // count; g goes to LDS when the epilogue starts
+    u32x4_t w0v[G::NW0];
+    float grow_v;
+    auto issue_w0 = [&]() {
+#pragma unroll
+        for (int i = 0; i < G::NW0; ++i) {
+            const int h = i / G::NH, c = tid + G::NTH * (i % G::NH);
+            const int64_t gm = min(m0 + h * G::ER + c / G::CPR, a.d_out - 1);
+            const int64_t gn = min(n0 + (int64_t)(c % G::CPR) * VEC, a.d_in - VEC);
+            w0v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(W0 + gm * a.d_in + gn));
+        }
+        grow_v = a.g[min(m0 + (tid % G::BM), a.d_out - 1)];
+    };
+
+    f32x16_t acc[G::MT][G::NT];
+#pragma unroll
+    for (int i = 0; i < G::MT; ++i)
+#pragma unroll
+        for (int j = 0; j < G::NT; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    for (int t = 0; t < kRing - 1; ++t)
+        if (t < nk) issue(t);
+    const int kt_w0 = max(0, nk - kRing);
+    const int fr = lane & 31, fh = lane >> 5;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int after = min(nk, kt + kRing - 1) - kt - 1;
+        wait_stage_big<NLD, kRing - 2>(after, kt > kt_w0);
+        lds_barrier();
+        if (kt + kRing - 1 < nk) issue(kt + kRing - 1);
+        if (kt == kt_w0) issue_w0();
+        const char* st = lds + (kt % kRing) * G::STAGE;
+#pragma unroll
+        for (int step = 0; step < 2; ++step) {
+            const int q = 2 * step + fh;
+            u32x4_t av[G::MT], bv[G::NT];
+#pragma unroll
+            for (int i = 0; i < G::MT; ++i) {
+                const int row = wm * G::WR + i * 32 + fr;
+                av[i] = *reinterpret_cast<const u32x4_t*>(st + row * kRowB + ((q ^ swz64(row)) << 4));
+            }
+#pragma unroll
+            for (int j = 0; j < G::NT; ++j) {
+                const int row = wn * G::WC + j * 32 + fr;
+                bv[j] = *reinterpret_cast<const u32x4_t*>(st + (G::BM + row) * kRowB + ((q ^ swz64(row)) << 4));
+            }
+#pragma unroll
+            for (int i = 0; i < G::MT; ++i)
+#pragma unroll
+                for (int j = 0; j < G::NT; ++j) MergeMma<E>::mma(acc[i][j], bv[j], av[i]);
+        }
+    }
+    lds_barrier();   // every wave is done with the ring
+
+    // epilogue, one 64-row round at a time (as in merge_tile_dma: acc[i][j]
+    // is the transposed block, lane l owning row l % 32 of row block i and
+    // columns 8g + 4 (l / 32) .. + 3 of column block j in registers 4g ..)
+    float* epi = reinterpret_cast<float*>(lds);
+    E* W = static_cast<E*>(a.W);
+    const float s = a.s;
+    if (tid < G::BM) gsm[tid] = grow_v;
+#pragma unroll
+    for (int h = 0; h < G::ROUNDS; ++h) {
+#pragma unroll
+        for (int i = 0; i < G::MT; ++i) {
+            if (wm * G::WR + i * 32 >= h * G::ER && wm * G::WR + i * 32 < (h + 1) * G::ER) {
+#pragma unroll
+                for (int j = 0; j < G::NT; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int row = wm * G::WR + i * 32 - h * G::ER + fr;
+                        const int col = wn * G::WC + j * 32 + 8 * g + 4 * fh;
+                        *reinterpret_cast<f32x4_t*>(epi + row * G::PITCH + col) =
+                            f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    }
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < G::NH; ++i) {
+            const int c = tid + G::NTH * i, row = c / G::CPR, cc = c % G::CPR;
+            const int64_t gm = m0 + h * G::ER + row, gn = n0 + (int64_t)cc * VEC;
+            if (gm < a.d_out && gn < a.d_in) {
+                const float gi = gsm[h * G::ER + row];
+                const float* src = epi + row * G::PITCH + cc * VEC;
+                Pack<E> w, o;
+                w.u = w0v[h * G::NH + i];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) o.e[e] = Cvt<E>::from_f(gi * fmaf(s, src[e], Cvt<E>::to_f(w.e[e])));
+                __builtin_nontemporal_store(o.u, reinterpret_cast<u32x4_t*>(W + gm * a.d_in + gn));
+            }
+        }
+        lds_barrier();
+    }
+}
+
 inline const bf16_t* A_bf16(const void* p) { return static_cast<const bf16_t*>(p); }
+
+// Large tiles run one workgroup per CU, so a tile's W0 stream and epilogue
+// overlap nothing of its own; with several tiles per CU the 128 x 128 kernel,
+// three workgroups per CU hiding each other's phases, is faster (measured on
+// MI355X at r = 384: 8192^2 104 against 110 us, 5120 x 27648 219 against 229
+// us).  When the large grid is a single round that fills most CUs, its
+// halved operand traffic wins (4096^2 35.6 -> 29.3 us, 2048 x 8192 37.5 ->
+// 30.9 us, 2560 x 5120 32.6 -> 28.8 us); at 192 tiles it ties (3072 x 4096)
+// and at 128 it loses (1024 x 8192 21.6 against 26.9 us).
+constexpr int64_t kMergeBigMinTiles = 200, kMergeBigMaxTiles = 256;
 
 template <typename E>
 hipError_t merge_typed(const void* W0, const void* A, const void* B, const float* g, float s, int64_t d_out,
@@ -598,6 +779,11 @@ hipError_t merge_typed(const void* W0, const void* A, const void* B, const float
     else
         transpose_a<E><<<tgrid, 256, 0, st>>>(static_cast<const E*>(A), r, d_in, At, r_pad);
 
+    // 256 x 256 tiles where they make one round of workgroups
+    const int64_t big_tiles = ((d_out + BigMerge::BM - 1) / BigMerge::BM) * ((d_in + BigMerge::BN - 1) / BigMerge::BN);
+    const bool big = sizeof(E) == 2 && aligned && !a_direct && big_tiles >= kMergeBigMinTiles &&
+                     big_tiles <= kMergeBigMaxTiles;
+    const int64_t bm = big ? BigMerge::BM : kBM, bn = big ? BigMerge::BN : kBN;
     MergeArgs a;
     a.W0 = W0;
     a.At = a_direct ? static_cast<const E*>(A) : At;   // merge_tile_dma<E, true> reads A [r][d_in]
@@ -609,12 +795,14 @@ hipError_t merge_typed(const void* W0, const void* A, const void* B, const float
     a.d_in = d_in;
     a.r = r;
     a.r_pad = r_pad;
-    a.n_mt = (int)((d_out + kBM - 1) / kBM);
-    a.n_nt = (int)((d_in + kBN - 1) / kBN);
+    a.n_mt = (int)((d_out + bm - 1) / bm);
+    a.n_nt = (int)((d_in + bn - 1) / bn);
     const int64_t tiles = (int64_t)a.n_mt * a.n_nt;
     a.per_xcd = (int)((tiles + kNumXCD - 1) / kNumXCD);
     const unsigned grid = (unsigned)(a.per_xcd * kNumXCD);
-    if (a_direct) {
+    if (big) {
+        merge_tile_big<<<grid, BigMerge::NTH, 0, st>>>(a);
+    } else if (a_direct) {
         if constexpr (sizeof(E) == 2) merge_tile_dma<E, true><<<grid, kNTh, 0, st>>>(a);
     } else if (aligned) {
         merge_tile_dma<E, false><<<grid, kNTh, 0, st>>>(a);

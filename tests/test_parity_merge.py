@@ -149,3 +149,23 @@ def test_merge_low_rank_stages_A_directly(r):
     torch.cuda.synchronize()
     assert torch.equal(W_direct, W_transposed)
     _check_layer(L, g, W_direct, tag=f"direct r{r}")
+
+
+@pytest.mark.parametrize("d_out,d_in,r", [(4096, 4096, 384), (3900, 3952, 104), (2048, 8192, 200), (4096, 4096, 64)])
+def test_merge_large_tiles(d_out, d_in, r):
+    # bf16, aligned, r > 32 and 200-256 tiles of 256 x 256: the large-tile
+    # kernel (8 waves of 128 x 64, four 64-row epilogue rounds); ragged rows,
+    # columns and k-tiles in the second shape.  Sampled rows, then in place.
+    say(f"[merge] large tiles {d_out}x{d_in} r={r}")
+    spec = DI.custom_spec(d_out, d_in, r, 1, dtype="bf16", s=1.5, b_std=0.05)
+    L = DI.make_layer(spec, 950 + r, device=DEV, activations=False, gen_device="cuda")
+    g = gpu_g(L)
+    W = D.merge(L.W0, L.A, L.B, g, spec.s)
+    torch.cuda.synchronize()
+    rows = sample_rows(d_out, 96, seed=r)
+    rows = np.unique(np.concatenate([rows, np.arange(d_out - 40, d_out)]))   # the ragged last row tile
+    _check_layer(L, g, W, rows=rows, tag=f"large tiles {d_out}x{d_in} r{r}")
+    Wi = L.W0.clone()
+    D.merge(Wi, L.A, L.B, g, spec.s, out=Wi)
+    torch.cuda.synchronize()
+    assert torch.equal(Wi, W)
