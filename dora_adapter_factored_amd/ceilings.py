@@ -16,10 +16,12 @@ stream, several launches back to back after a warm-up:
                                            one L2-resident region / each its own),
                                            and the whole chip's sum
   w0_stream, w0_stream_with_a              GB/s of the W0 pass's access pattern
-                                           (256 x 64-byte row pieces per k-tile
+  (w0_stream_with_a_tiled)                 (256 x 64-byte row pieces per k-tile
                                            through a 4-stage LDS-DMA ring, one
                                            barrier per tile) without MFMA, W0 alone
                                            and with the 384-row A tile per k-tile
+                                           (A row-major, or k-tile-major so that
+                                           each tile is one contiguous run)
 """
 from __future__ import annotations
 
@@ -145,7 +147,7 @@ def w0_stream(dev, d_out: int = 8192, d_in: int = 8192, r: int = 384) -> dict:
             for _ in range(3)]
     out = torch.empty(256 * 512, dtype=torch.int32, device=dev)
     res = {}
-    for name, with_a in (("w0_stream", 0), ("w0_stream_with_a", 1)):
+    for name, with_a in (("w0_stream", 0), ("w0_stream_with_a", 1), ("w0_stream_with_a_tiled", 2)):
         i = [0]
 
         def run():

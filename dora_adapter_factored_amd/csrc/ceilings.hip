@@ -195,15 +195,18 @@ __global__ __launch_bounds__(512) void cu_read(const u32x4_t* buf, int64_t bytes
 // (workgroup ids are dealt to XCDs round robin).  Each k-tile moves 256 rows
 // x 64 bytes of W0 (and, with_a, 384 rows x 64 bytes of A) into a 4-stage
 // LDS ring by DMA, three tiles ahead; a barrier per tile; every thread reads
-// 16 bytes of the landed tile so the data is consumed.
+// 16 bytes of the landed tile so the data is consumed.  AMODE 1 reads A
+// row-major ([r][d_in], each k-tile 384 pieces of 64 bytes a row apart), as
+// the W0 pass does; AMODE 2 reads the same bytes k-tile-major ([k-tile][r][32
+// elements], each k-tile's A tile one contiguous 24 KB run).
 constexpr int kRows = 256, kArows = 384, kStages = 4, kRowB = 64;
 constexpr int kStageBytes = (kRows + kArows) * kRowB;
 
-template <bool WITH_A>
+template <int AMODE>
 __global__ __launch_bounds__(512) void w0_stream(const bf16_t* W0, const bf16_t* A, int64_t d_out, int64_t d_in,
                                                  int64_t r, uint32_t* out) {
     // DMA instructions per wave per tile: 16 (W0) and 24 (A) groups of 16 rows over 8 waves
-    constexpr int PER = kRows / 16 / 8 + (WITH_A ? kArows / 16 / 8 : 0);
+    constexpr int PER = kRows / 16 / 8 + (AMODE ? kArows / 16 / 8 : 0);
     __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -248,12 +251,20 @@ __global__ __launch_bounds__(512) void w0_stream(const bf16_t* W0, const bf16_t*
             raw_buffer_load_lds(rw, (lds_void_t*)(st + g * 1024), 16, in ? loff + kb + g * 16 * ldb : kOutOfRange, 0,
                                 0, 0);
         }
-        if (WITH_A) {
+        if (AMODE == 1) {
 #pragma unroll
             for (int g0 = 0; g0 < kArows / 16; g0 += 8) {
                 const int g = g0 + wave;
                 raw_buffer_load_lds(ra, (lds_void_t*)(st + kRows * kRowB + g * 1024), 16,
                                     in ? loff + kb + g * 16 * ldb : kOutOfRange, 0, 0, 0);
+            }
+        } else if (AMODE == 2) {
+            const int tb = (kt0 + t) * kArows * kRowB;   // the k-tile's contiguous A tile
+#pragma unroll
+            for (int g0 = 0; g0 < kArows / 16; g0 += 8) {
+                const int g = g0 + wave;
+                raw_buffer_load_lds(ra, (lds_void_t*)(st + kRows * kRowB + g * 1024), 16,
+                                    valid ? tb + g * 1024 + lane * 16 : kOutOfRange, 0, 0, 0);
             }
         }
     };
@@ -347,7 +358,8 @@ int dora_ceiling_cu_read(const void* buf, int64_t bytes_per_wg, int64_t stride, 
 
 // W0 [d_out, d_in] and A [r, d_in] bf16, d_in a multiple of 8 and d_out up
 // to 32 row tiles of 256 (rows of A past r read zeros); out holds 256 x 512
-// words.
+// words.  with_a: 0 W0 alone, 1 A row-major, 2 A k-tile-major (offsets past
+// A's r * d_in elements read zeros).
 int dora_ceiling_w0_stream(const void* W0, const void* A, int64_t d_out, int64_t d_in, int64_t r, int with_a,
                            void* out, void* stream) {
     if (!W0 || !A || !out || d_out < 1 || d_out > 32 * 256 || d_in < 8 || d_in % 8 || r < 1 ||
@@ -355,12 +367,16 @@ int dora_ceiling_w0_stream(const void* W0, const void* A, int64_t d_out, int64_t
         return 1;
     const auto* w = static_cast<const dora::bf16_t*>(W0);
     const auto* a = static_cast<const dora::bf16_t*>(A);
-    if (with_a)
-        dora::w0_stream<true><<<256, 512, 0, static_cast<hipStream_t>(stream)>>>(w, a, d_out, d_in, r,
-                                                                              static_cast<uint32_t*>(out));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    uint32_t* o = static_cast<uint32_t*>(out);
+    if (with_a == 1)
+        dora::w0_stream<1><<<256, 512, 0, st>>>(w, a, d_out, d_in, r, o);
+    else if (with_a == 2)
+        dora::w0_stream<2><<<256, 512, 0, st>>>(w, a, d_out, d_in, r, o);
+    else if (with_a == 0)
+        dora::w0_stream<0><<<256, 512, 0, st>>>(w, a, d_out, d_in, r, o);
     else
-        dora::w0_stream<false><<<256, 512, 0, static_cast<hipStream_t>(stream)>>>(w, a, d_out, d_in, r,
-                                                                               static_cast<uint32_t*>(out));
+        return 1;
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
