@@ -394,7 +394,8 @@ def main():
         total = ev[0].elapsed_time(ev[nbatch]) * 1e-3 / args.steps
         per = [ev[b].elapsed_time(ev[b + 1]) * 1e-3 / ((b + 1) * args.steps // nbatch - b * args.steps // nbatch)
                for b in range(nbatch)]
-        per_call.spread[fn.__name__] = (float(np.percentile(per, 10)), float(np.percentile(per, 90)))
+        per_call.spread[fn.__name__] = (float(np.percentile(per, 10)), float(np.percentile(per, 90)),
+                                        float(np.median(per)))
         return total
 
     per_call.spread = {}
@@ -436,8 +437,12 @@ def main():
     spread = per_call.spread
 
     def ms_spread(name):
-        lo, hi = spread.get(name, (None, None))
+        lo, hi, _ = spread.get(name, (None, None, None))
         return None if lo is None else [round(lo * 1e3, 4), round(hi * 1e3, 4)]
+
+    def ms_median(name):
+        med = spread.get(name, (None, None, None))[2]
+        return None if med is None else round(med * 1e3, 4)
 
     norm_ceiling = (ceil["mfma_32x32x16_bf16_TFLOPs"] if dt != torch.float32 else None)
     out = {
@@ -456,7 +461,7 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
         "config": {"workload": spec.name, "d_out": d_out, "d_in": d_in, "r": r, "tokens": T, "s": s,
                    "rotating_input_sets": nsets},
-        "norm": {"ms": round(t_norm * 1e3, 4), "ms_p10_p90": ms_spread("run_norm"), "TFLOPs": round(norm_tflops, 2),
+        "norm": {"ms": round(t_norm * 1e3, 4), "ms_p10_p90": ms_spread("run_norm"), "ms_median": ms_median("run_norm"), "TFLOPs": round(norm_tflops, 2),
                  "frac_mfma_peak": round(norm_tflops / peak_mm, 4),
                  "frac_measured_ceiling": (round(norm_tflops / norm_ceiling, 4) if norm_ceiling else None),
                  "frac_measured_hbm_read": round(nb / t_norm / 1e9 / hbm_read_ceiling, 4),
@@ -464,25 +469,25 @@ def main():
                  "algorithmic_bytes": nb, "GBps": round(nb / t_norm / 1e9, 1),
                  "frac_hbm_peak": round(nb / t_norm / 1e9 / PEAK_HBM_GBS, 4),
                  "workspace_bytes": int(ws_norm.numel()), "kernels_traced": traced},
-        "compose_fwd": {"ms": round(t_fwd * 1e3, 4), "ms_p10_p90": ms_spread("run_fwd"), "GBps": round(fwd_gbs, 1),
+        "compose_fwd": {"ms": round(t_fwd * 1e3, 4), "ms_p10_p90": ms_spread("run_fwd"), "ms_median": ms_median("run_fwd"), "GBps": round(fwd_gbs, 1),
                         "frac_hbm_peak": round(fwd_gbs / PEAK_HBM_GBS, 4),
                         "frac_measured_ceiling": round(fwd_gbs / act["stream_2r1w"], 4),
                         "frac_measured_copy": round(fwd_gbs / calib["GBps"], 4), "algorithmic_bytes": fb},
-        "compose_bwd": {"ms": round(t_bwd * 1e3, 4), "ms_p10_p90": ms_spread("run_bwd"), "GBps": round(bwd_gbs, 1),
+        "compose_bwd": {"ms": round(t_bwd * 1e3, 4), "ms_p10_p90": ms_spread("run_bwd"), "ms_median": ms_median("run_bwd"), "GBps": round(bwd_gbs, 1),
                         "frac_hbm_peak": round(bwd_gbs / PEAK_HBM_GBS, 4),
                         "frac_measured_ceiling": round(bwd_gbs / act["stream_3r2w"], 4),
                         "frac_measured_copy": round(bwd_gbs / calib["GBps"], 4), "algorithmic_bytes": bb},
-        "compose_dual": {"ms": round(t_dual * 1e3, 4), "ms_p10_p90": ms_spread("run_dual"),
+        "compose_dual": {"ms": round(t_dual * 1e3, 4), "ms_p10_p90": ms_spread("run_dual"), "ms_median": ms_median("run_dual"),
                          "GBps": round(db_ / t_dual / 1e9, 1),
                          "frac_hbm_peak": round(db_ / t_dual / 1e9 / PEAK_HBM_GBS, 4),
                          "frac_measured_ceiling": round(db_ / t_dual / 1e9 / act["stream_2r2w"], 4),
                          "algorithmic_bytes": db_},
-        "compose_bwd_inner": {"ms": round(t_bwdi * 1e3, 4), "ms_p10_p90": ms_spread("run_bwd_inner"),
+        "compose_bwd_inner": {"ms": round(t_bwdi * 1e3, 4), "ms_p10_p90": ms_spread("run_bwd_inner"), "ms_median": ms_median("run_bwd_inner"),
                               "GBps": round(bib / t_bwdi / 1e9, 1),
                               "frac_hbm_peak": round(bib / t_bwdi / 1e9 / PEAK_HBM_GBS, 4),
                               "frac_measured_ceiling": round(bib / t_bwdi / 1e9 / act["stream_2r2w"], 4),
                               "algorithmic_bytes": bib},
-        "merge": {"ms": round(t_merge * 1e3, 4), "ms_p10_p90": ms_spread("run_merge"), "GBps": round(mb / t_merge / 1e9, 1),
+        "merge": {"ms": round(t_merge * 1e3, 4), "ms_p10_p90": ms_spread("run_merge"), "ms_median": ms_median("run_merge"), "GBps": round(mb / t_merge / 1e9, 1),
                   "frac_hbm_peak": round(mb / t_merge / 1e9 / PEAK_HBM_GBS, 4),
                   "frac_measured_ceiling": round(mb / t_merge / 1e9 / ceil["stream_2r1w_GBps"], 4),
                   "algorithmic_bytes": mb, "TFLOPs": round(2 * d_out * d_in * r / t_merge / 1e12, 1)},
