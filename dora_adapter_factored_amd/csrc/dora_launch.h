@@ -28,6 +28,12 @@ struct NormPlan {
     int n_mtiles, n_ntiles;
     int nkt_w0, nkt_g;  // K tiles over d_in, then over the Gram block (r)
     int ksplit;
+    // balanced K split of the large-tile pass (bal_nwg > 0): workgroup w of
+    // bal_nwg owns an equal range of the m-tile-major (m-tile, k-tile) pairs,
+    // bal_units of them, bal_nkt k-tiles per m-tile; ksplit is then the most
+    // partial slots any m-tile has
+    int bal_nwg, bal_nkt;
+    int64_t bal_units;
     // Gram
     int gram_tiles;     // tiles per side (64 wide)
     int gram_split;

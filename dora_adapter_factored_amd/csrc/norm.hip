@@ -687,7 +687,25 @@ __device__ __forceinline__ void mainloop(const Contraction& c, int64_t m0, int64
 }
 
 // ------------------------------------------------------------- W0 pass
+// Balanced K split of the large-tile pass.  Workgroup w of nwg owns units
+// [w U / nwg, (w + 1) U / nwg) of the m-tile-major sequence of (m-tile,
+// k-tile) pairs, U = units = n_mtiles * nkt.  A range is shorter than one
+// m-tile's K, so it covers the tail of one m-tile and the head of the next
+// at most: two segments, each with its own epilogue, whose partials go to
+// slot (w - first workgroup of that m-tile).  nwg = 0: the uniform split.
+struct Balance {
+    int64_t units;
+    int nwg, nkt;
+    // the workgroup whose range holds unit u
+    __host__ __device__ int wg_of(int64_t u) const { return (int)(((u + 1) * nwg + units - 1) / units) - 1; }
+    // partial slots of m-tile mt (workgroups whose ranges meet it)
+    __host__ __device__ int slots(int mt) const {
+        return wg_of((int64_t)(mt + 1) * nkt - 1) - wg_of((int64_t)mt * nkt) + 1;
+    }
+};
+
 struct W0PassArgs {
+    Balance bal;          // large-tile pass only
     Contraction c;
     const void* B;          // [d_out, r], for the row-dot epilogue
     int64_t d_out, r;
@@ -1184,30 +1202,16 @@ __device__ __forceinline__ void dma64_tile(const Dma64& d, int lane_off, int chu
     }
 }
 
-__device__ __forceinline__ void w0_pass_big_body(const W0PassArgs& a, const int id, char* smem) {
+// One segment of the large-tile pass: rows of m-tile mtile, columns of
+// n-tile ntile, k-tiles [kt_begin, kt_end); its partials go to slot kc.
+__device__ __forceinline__ void w0_pass_big_seg(const W0PassArgs& a, const int id, const int mtile, const int ntile,
+                                                const int kc, const int kt_begin, const int kt_end, char* smem) {
     typedef Big G;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / G::WN, wn = wave % G::WN;
-
-    // workgroup -> (m-tile, n-tile, k-chunk), K-chunks mapped to XCDs
-    const int Q = a.n_ntiles * a.ksplit;
-    int q, mtile;
-    if (a.xcd_map) {
-        const int xcd = id % kNumXCD, slot = id / kNumXCD;
-        q = xcd % Q;
-        mtile = slot * (kNumXCD / Q) + xcd / Q;
-    } else {
-        q = id % Q;
-        mtile = id / Q;
-    }
-    if (mtile >= a.n_mtiles) return;
-    const int ntile = q / a.ksplit, kc = q % a.ksplit;
     const int64_t m0 = (int64_t)mtile * G::BM, n0 = (int64_t)ntile * G::BN;
     const Contraction& c = a.c;
-    const int nkt = c.nkt0 + c.nkt1;
-    const int kt_begin = (int)((int64_t)kc * nkt / a.ksplit);
-    const int kt_end = (int)((int64_t)(kc + 1) * nkt / a.ksplit);
     const int n = kt_end - kt_begin;
     float* base_dst = ntile == 0 ? a.part_base + (int64_t)kc * a.d_out : nullptr;
     const int rot = n > 0 ? (int)(((unsigned)id * 7u + ((unsigned)id >> 3) * 3u) % (unsigned)n) : 0;
@@ -1466,6 +1470,51 @@ __device__ __forceinline__ void w0_pass_big_body(const W0PassArgs& a, const int 
                 a.part_cross[((int64_t)ntile * a.ksplit + kc) * a.d_out + mrow] = v;
             }
         }
+    }
+}
+
+__device__ __forceinline__ void w0_pass_big_body(const W0PassArgs& a, const int id, char* smem) {
+    const int nkt = a.c.nkt0 + a.c.nkt1;
+    int nseg = 0, seg_mt[2] = {0, 0}, seg_nt[2] = {0, 0}, seg_slot[2] = {0, 0}, seg_k0[2] = {0, 0},
+        seg_k1[2] = {0, 0};
+    if (a.bal.nwg > 0) {
+        const Balance& b = a.bal;
+        const int64_t u0 = (int64_t)id * b.units / b.nwg, u1 = (int64_t)(id + 1) * b.units / b.nwg;
+        for (int64_t u = u0; u < u1 && nseg < 2; ++nseg) {
+            const int mt = (int)(u / nkt);
+            const int64_t t0 = (int64_t)mt * nkt;
+            const int64_t end = u1 < t0 + nkt ? u1 : t0 + nkt;
+            seg_mt[nseg] = mt;
+            seg_slot[nseg] = id - b.wg_of(t0);
+            seg_k0[nseg] = (int)(u - t0);
+            seg_k1[nseg] = (int)(end - t0);
+            u = end;
+        }
+    } else {
+        // workgroup -> (m-tile, n-tile, k-chunk), K-chunks mapped to XCDs
+        const int Q = a.n_ntiles * a.ksplit;
+        int q, mtile;
+        if (a.xcd_map) {
+            const int xcd = id % kNumXCD, slot = id / kNumXCD;
+            q = xcd % Q;
+            mtile = slot * (kNumXCD / Q) + xcd / Q;
+        } else {
+            q = id % Q;
+            mtile = id / Q;
+        }
+        if (mtile < a.n_mtiles) {
+            const int kc = q % a.ksplit;
+            nseg = 1;
+            seg_mt[0] = mtile;
+            seg_nt[0] = q / a.ksplit;
+            seg_slot[0] = kc;
+            seg_k0[0] = (int)((int64_t)kc * nkt / a.ksplit);
+            seg_k1[0] = (int)((int64_t)(kc + 1) * nkt / a.ksplit);
+        }
+    }
+    for (int s = 0; s < nseg; ++s) {
+        if (s > 0) __syncthreads();   // the previous segment's epilogue is done with LDS
+        w0_pass_big_seg(a, id, seg_mt[s], seg_nt[s], seg_slot[s], seg_k0[s], seg_k1[s], smem);
     }
 }
 
@@ -1753,8 +1802,10 @@ __global__ __launch_bounds__(256) void row_sumsq(const E* __restrict__ W0, int64
 __device__ __forceinline__ void norm_finalize_body(const float* __restrict__ pbase, int nbase,
                                                   const float* __restrict__ pcross, int ncross, int64_t d_out,
                                                   float two_s, const float* __restrict__ m, float eps,
-                                                  float* __restrict__ wnorm, float* __restrict__ g, const int64_t i) {
+                                                  float* __restrict__ wnorm, float* __restrict__ g, const int64_t i,
+                                                  const Balance bal = Balance{1, 0, 1}) {
     if (i >= d_out) return;
+    if (bal.nwg > 0) nbase = ncross = bal.slots((int)(i / Big::BM));   // this row's m-tile's slots
     // m is loaded ahead of the partials, so both come back in one memory
     // round trip; partials are loaded in batches of 16 (both kinds together)
     // before they are summed, each kind in partial order
@@ -1809,9 +1860,10 @@ __global__ __launch_bounds__(256) void gram_finalize(const float* __restrict__ p
 __global__ __launch_bounds__(256) void norm_finalize(const float* __restrict__ pbase, int nbase,
                                                      const float* __restrict__ pcross, int ncross, int64_t d_out,
                                                      float two_s, const float* __restrict__ m, float eps,
-                                                     float* __restrict__ wnorm, float* __restrict__ g) {
+                                                     float* __restrict__ wnorm, float* __restrict__ g,
+                                                     Balance bal) {
     norm_finalize_body(pbase, nbase, pcross, ncross, d_out, two_s, m, eps, wnorm, g,
-                       (int64_t)blockIdx.x * 256 + threadIdx.x);
+                       (int64_t)blockIdx.x * 256 + threadIdx.x, bal);
 }
 
 struct GramFinArgs {
@@ -1831,6 +1883,7 @@ struct NormFinArgs {
     const float* m;
     float* wnorm;
     float* g;
+    Balance bal;
 };
 
 template <typename A>
@@ -1872,7 +1925,7 @@ __global__ __launch_bounds__(256) void norm_finalize_group(Group<NormFinArgs> g)
     const int j = group_member(g, blockIdx.x);
     const NormFinArgs& a = g.a[j];
     norm_finalize_body(a.pbase, a.nbase, a.pcross, a.ncross, a.d_out, a.two_s, a.m, a.eps, a.wnorm, a.g,
-                       (int64_t)(blockIdx.x - g.start[j]) * 256 + threadIdx.x);
+                       (int64_t)(blockIdx.x - g.start[j]) * 256 + threadIdx.x, a.bal);
 }
 
 // ------------------------------------------------------------- configs
@@ -1985,6 +2038,7 @@ NormLaunch make_norm_launch(const NormPlan& p, bool aligned, const void* W0, con
     L.gfgrid = (unsigned)(p.gram_tiles * p.gram_tiles * kGfPerTile);
 
     W0PassArgs& wa = L.wa;
+    wa.bal = p.bal_nwg > 0 ? Balance{p.bal_units, p.bal_nwg, p.bal_nkt} : Balance{1, 0, 1};
     wa.c.left0 = Operand{W0, d_in, d_out, d_in};
     wa.c.right0 = Operand{A, d_in, r, d_in};
     wa.c.left1 = Operand{B, r, d_out, r};
@@ -2003,13 +2057,15 @@ NormLaunch make_norm_launch(const NormPlan& p, bool aligned, const void* W0, con
     wa.part_cross = reinterpret_cast<float*>(w + p.off_pcross);
     wa.half_s = 0.5f * s;
     if (gram_in_pass<E>(p, aligned)) wa.c.nkt1 = 0;   // no Gs k-tiles: the pass forms the Gram term
-    if (wa.xcd_map) {
+    if (p.bal_nwg > 0) {
+        L.wgrid = p.bal_nwg;
+    } else if (wa.xcd_map) {
         const int per = kNumXCD / Q;   // m-tiles per XCD slot
         L.wgrid = kNumXCD * ((p.n_mtiles + per - 1) / per);
     } else {
         L.wgrid = Q * p.n_mtiles;
     }
-    L.nf = NormFinArgs{wa.part_base, wa.part_cross, p.ksplit, Q, d_out, 2.0f * s, eps, m, wnorm, g};
+    L.nf = NormFinArgs{wa.part_base, wa.part_cross, p.ksplit, Q, d_out, 2.0f * s, eps, m, wnorm, g, wa.bal};
     L.nfgrid = (unsigned)((d_out + 255) / 256);
     return L;
 }
@@ -2031,7 +2087,7 @@ hipError_t norm_typed(const NormPlan& p, const void* W0, const void* A, const vo
             row_sumsq<E, false><<<grid, 256, 0, st>>>(static_cast<const E*>(W0), d_out, d_in, pbase);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         norm_finalize<<<(unsigned)((d_out + 255) / 256), 256, 0, st>>>(pbase, 1, nullptr, 0, d_out, 0.0f, m, eps,
-                                                                        wnorm, g);
+                                                                        wnorm, g, Balance{1, 0, 1});
         return hipGetLastError();
     }
     const bool al = operands_aligned<E>(p, W0, A, B);
@@ -2094,13 +2150,23 @@ hipError_t norm_typed(const NormPlan& p, const void* W0, const void* A, const vo
 
     // 3. assemble
     norm_finalize<<<L.nfgrid, 256, 0, st>>>(L.nf.pbase, L.nf.nbase, L.nf.pcross, L.nf.ncross, L.nf.d_out,
-                                            L.nf.two_s, L.nf.m, L.nf.eps, L.nf.wnorm, L.nf.g);
+                                            L.nf.two_s, L.nf.m, L.nf.eps, L.nf.wnorm, L.nf.g, L.nf.bal);
     return hipGetLastError();
 }
 
 }  // namespace
 
 namespace {
+
+// The balanced split is taken when the uniform one fills less than
+// kBalanceMaxFill percent of a round and its workgroups walk at least
+// kBalanceMinKtiles k-tiles.  Measured on MI355X at r = 384: 28672 x 8192
+// (112 m-tiles, 134 k-tiles per workgroup) 241.8 -> 230.9 us; with 60-90
+// k-tiles per workgroup the second epilogue costs more than the idle CUs
+// (27648 x 5120 a tie, 14336 x 8192 132.1 -> 136.1 us, 28672 x 4096 135.3 ->
+// 139.5 us, 20000 x 8200 188.0 -> 190.8 us).
+constexpr int64_t kBalanceMaxFill = 95;
+constexpr int kBalanceMinKtiles = 120;
 
 NormPlan plan_norm_impl(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool base_only, bool allow_big) {
     NormPlan p{};
@@ -2137,6 +2203,20 @@ NormPlan plan_norm_impl(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool 
         ks = tiles >= round ? 1 : (int)(round / tiles);
         if (ks > 64) ks = 64;
         while (ks > 1 && nkt / ks < 8) --ks;
+        // A uniform split that leaves CUs idle (112 m-tiles in two K-chunks
+        // use 224 of 256) is traded for equal ranges over all CUs when the
+        // workgroups are long: some then run two segments, i.e. two
+        // epilogues.
+        if (p.n_ntiles == 1 && tiles < round && tiles * ks * 100 < round * kBalanceMaxFill &&
+            nkt / ks >= kBalanceMinKtiles) {
+            const Balance b{tiles * nkt, (int)round, nkt};
+            p.bal_nwg = b.nwg;
+            p.bal_nkt = nkt;
+            p.bal_units = b.units;
+            int most = 1;
+            for (int mt = 0; mt < p.n_mtiles; ++mt) most = b.slots(mt) > most ? b.slots(mt) : most;
+            ks = most;   // partial slots per row
+        }
     } else {
         // widest configuration this dtype instantiates (fp32 fragments double
         // the register footprint, so fp32 stops at BN = 192)
@@ -2289,6 +2369,7 @@ hipError_t launch_norm_group(int n, const NormMember* mem, int64_t r, int dtype,
     longest_first([&](int j) { return (L[j].ga.c.nkt0 + L[j].ga.nsplit - 1) / L[j].ga.nsplit; }, og);
     longest_first(
         [&](int j) {
+            if (plans[j].bal_nwg > 0) return (int)((plans[j].bal_units + plans[j].bal_nwg - 1) / plans[j].bal_nwg);
             const int nkt = plans[j].nkt_w0 + plans[j].nkt_g;
             return (nkt + plans[j].ksplit - 1) / plans[j].ksplit;
         },

@@ -609,3 +609,25 @@ def test_graph_capture_replays_match_eager(d_out, d_in, r):
             assert torch.equal(got, ref), f"replay {rep}: {name}"
         D.factored_norm(other.W0, other.A, other.B, 1.0, other.m)   # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("d_out,d_in", [(28000, 8200), (24000, 12288)])
+def test_norm_balanced_k_split(d_out, d_in):
+    # r = 384 with 110 or 94 m-tiles of 256 rows (the last one ragged) and
+    # 134 or 198 k-tiles per workgroup under a uniform two-way K split, which
+    # would leave CUs idle: 256 workgroups take equal ranges of the (m-tile,
+    # k-tile) pairs instead, some running two segments (the tail of one
+    # m-tile and the head of the next) and each m-tile summing its partial
+    # slots.  Sampled rows plus every row at m-tile boundaries and the end.
+    say(f"[parity] balanced K split {d_out}x{d_in} r=384")
+    spec = DI.custom_spec(d_out, d_in, 384, 1, dtype="bf16", s=1.0, b_std=0.02)
+    L = DI.make_layer(spec, 77 + d_in, device=DEV, activations=False, gen_device="cuda")
+    wn, g = gpu_norm(L)
+    edges = [b + o for b in range(0, d_out, 256 * 7) for o in (-1, 0, 255) if 0 <= b + o < d_out]
+    rows = np.unique(np.concatenate([sample_rows(d_out, 160, seed=d_in), np.array(edges), np.arange(d_out - 40, d_out)]))
+    ref_wn, ref_g = oracle_norm(L, rows)
+    assert np.all(np.isfinite(host64(wn))) and np.all(host64(wn) > 0)
+    check_rel(host64(wn)[rows], ref_wn, NORM_RTOL[L.W0.dtype], "wnorm")
+    check_rel(host64(g)[rows], ref_g, NORM_RTOL[L.W0.dtype], "g")
+    wn2, _ = gpu_norm(L)
+    assert torch.equal(wn, wn2)
