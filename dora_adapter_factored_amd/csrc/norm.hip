@@ -705,7 +705,6 @@ struct Balance {
 };
 
 struct W0PassArgs {
-    Balance bal;          // large-tile pass only
     Contraction c;
     const void* B;          // [d_out, r], for the row-dot epilogue
     int64_t d_out, r;
@@ -714,6 +713,7 @@ struct W0PassArgs {
     float* part_base;       // [ksplit][d_out]
     float* part_cross;      // [n_ntiles * ksplit][d_out]
     float half_s;           // s / 2, for the Gram term formed inside the pass
+    Balance bal;            // large-tile pass only
 };
 
 template <int WM, int WN, int MT, int NT, bool ALIGNED>
@@ -1473,48 +1473,40 @@ __device__ __forceinline__ void w0_pass_big_seg(const W0PassArgs& a, const int i
     }
 }
 
+// Uniform K split: one segment per workgroup, K-chunks mapped to XCDs.  This
+// form keeps the segment body outside any loop: wrapped in the balanced
+// form's segment loop, the body's register allocation spills (256 VGPRs and
+// 60 bytes of scratch per lane, and 9% more time at 8192^2), so that loop
+// lives in its own kernel.
 __device__ __forceinline__ void w0_pass_big_body(const W0PassArgs& a, const int id, char* smem) {
     const int nkt = a.c.nkt0 + a.c.nkt1;
-    int nseg = 0, seg_mt[2] = {0, 0}, seg_nt[2] = {0, 0}, seg_slot[2] = {0, 0}, seg_k0[2] = {0, 0},
-        seg_k1[2] = {0, 0};
-    if (a.bal.nwg > 0) {
-        const Balance& b = a.bal;
-        const int64_t u0 = (int64_t)id * b.units / b.nwg, u1 = (int64_t)(id + 1) * b.units / b.nwg;
-        for (int64_t u = u0; u < u1 && nseg < 2; ++nseg) {
-            const int mt = (int)(u / nkt);
-            const int64_t t0 = (int64_t)mt * nkt;
-            const int64_t end = u1 < t0 + nkt ? u1 : t0 + nkt;
-            seg_mt[nseg] = mt;
-            seg_slot[nseg] = id - b.wg_of(t0);
-            seg_k0[nseg] = (int)(u - t0);
-            seg_k1[nseg] = (int)(end - t0);
-            u = end;
-        }
+    const int Q = a.n_ntiles * a.ksplit;
+    int q, mtile;
+    if (a.xcd_map) {
+        const int xcd = id % kNumXCD, slot = id / kNumXCD;
+        q = xcd % Q;
+        mtile = slot * (kNumXCD / Q) + xcd / Q;
     } else {
-        // workgroup -> (m-tile, n-tile, k-chunk), K-chunks mapped to XCDs
-        const int Q = a.n_ntiles * a.ksplit;
-        int q, mtile;
-        if (a.xcd_map) {
-            const int xcd = id % kNumXCD, slot = id / kNumXCD;
-            q = xcd % Q;
-            mtile = slot * (kNumXCD / Q) + xcd / Q;
-        } else {
-            q = id % Q;
-            mtile = id / Q;
-        }
-        if (mtile < a.n_mtiles) {
-            const int kc = q % a.ksplit;
-            nseg = 1;
-            seg_mt[0] = mtile;
-            seg_nt[0] = q / a.ksplit;
-            seg_slot[0] = kc;
-            seg_k0[0] = (int)((int64_t)kc * nkt / a.ksplit);
-            seg_k1[0] = (int)((int64_t)(kc + 1) * nkt / a.ksplit);
-        }
+        q = id % Q;
+        mtile = id / Q;
     }
-    for (int s = 0; s < nseg; ++s) {
-        if (s > 0) __syncthreads();   // the previous segment's epilogue is done with LDS
-        w0_pass_big_seg(a, id, seg_mt[s], seg_nt[s], seg_slot[s], seg_k0[s], seg_k1[s], smem);
+    if (mtile >= a.n_mtiles) return;
+    const int kc = q % a.ksplit;
+    w0_pass_big_seg(a, id, mtile, q / a.ksplit, kc, (int)((int64_t)kc * nkt / a.ksplit),
+                    (int)((int64_t)(kc + 1) * nkt / a.ksplit), smem);
+}
+
+// Balanced K split (Balance): one or two segments per workgroup.
+__device__ __forceinline__ void w0_pass_big_body_balanced(const W0PassArgs& a, const int id, char* smem) {
+    const int nkt = a.c.nkt0 + a.c.nkt1;
+    const Balance& b = a.bal;
+    const int64_t u0 = (int64_t)id * b.units / b.nwg, u1 = (int64_t)(id + 1) * b.units / b.nwg;
+    for (int64_t u = u0; u < u1;) {   // at most twice: a range is shorter than one m-tile's K
+        const int mt = (int)(u / nkt);
+        const int64_t t0 = (int64_t)mt * nkt, e = u1 < t0 + nkt ? u1 : t0 + nkt;
+        if (u > u0) __syncthreads();   // the previous segment's epilogue is done with LDS
+        w0_pass_big_seg(a, id, mt, 0, id - b.wg_of(t0), (int)(u - t0), (int)(e - t0), smem);
+        u = e;
     }
 }
 
@@ -1840,9 +1832,13 @@ __device__ __forceinline__ void norm_finalize_body(const float* __restrict__ pba
 // group runs each stage of every member in a single grid: member j owns
 // workgroups [start[j], start[j+1]), and its starts are multiples of the XCD
 // count, so member-local workgroup ids keep their XCD.
+template <bool BAL>
 __global__ __launch_bounds__(Big::NTH, Big::WG_PER_CU * Big::NW / 4) void w0_pass_big(W0PassArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[Big::LDS_BYTES];
-    w0_pass_big_body(a, blockIdx.x, smem);
+    if constexpr (BAL)
+        w0_pass_big_body_balanced(a, blockIdx.x, smem);
+    else
+        w0_pass_big_body(a, blockIdx.x, smem);
 }
 
 __global__ __launch_bounds__(256) void gram_split_bf16(GramArgs a) {
@@ -1901,10 +1897,14 @@ __device__ __forceinline__ int group_member(const Group<A>& g, int id) {
     return j;
 }
 
+template <bool BAL>
 __global__ __launch_bounds__(Big::NTH, Big::WG_PER_CU * Big::NW / 4) void w0_pass_big_group(Group<W0PassArgs> g) {
     __shared__ __attribute__((aligned(1024))) char smem[Big::LDS_BYTES];
     const int j = group_member(g, blockIdx.x);
-    w0_pass_big_body(g.a[j], blockIdx.x - g.start[j], smem);
+    if (BAL && g.a[j].bal.nwg > 0)
+        w0_pass_big_body_balanced(g.a[j], blockIdx.x - g.start[j], smem);
+    else
+        w0_pass_big_body(g.a[j], blockIdx.x - g.start[j], smem);
 }
 
 __global__ __launch_bounds__(256) void gram_split_bf16_group(Group<GramArgs> g) {
@@ -2138,7 +2138,10 @@ hipError_t norm_typed(const NormPlan& p, const void* W0, const void* A, const vo
     // 2. streaming pass over [W0 | B] x [A | Gs]^T with the row-dot epilogue
     if constexpr (sizeof(E) == 2) {
         if (p.big) {
-            w0_pass_big<<<L.wgrid, Big::NTH, 0, st>>>(L.wa);
+            if (p.bal_nwg > 0)
+                w0_pass_big<true><<<L.wgrid, Big::NTH, 0, st>>>(L.wa);
+            else
+                w0_pass_big<false><<<L.wgrid, Big::NTH, 0, st>>>(L.wa);
             e = hipGetLastError();
         } else {
             e = al ? launch_w0<E, true>(p.cfg, L.wa, L.wgrid, st) : launch_w0<E, false>(p.cfg, L.wa, L.wgrid, st);
@@ -2385,7 +2388,12 @@ hipError_t launch_norm_group(int n, const NormMember* mem, int64_t r, int dtype,
     if ((e = hipGetLastError()) != hipSuccess) return e;
     gram_finalize_group<<<gf.start[n], 256, 0, st>>>(gf);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    w0_pass_big_group<<<gw.start[n], Big::NTH, 0, st>>>(gw);
+    bool any_bal = false;
+    for (int j = 0; j < n; ++j) any_bal = any_bal || plans[j].bal_nwg > 0;
+    if (any_bal)
+        w0_pass_big_group<true><<<gw.start[n], Big::NTH, 0, st>>>(gw);
+    else
+        w0_pass_big_group<false><<<gw.start[n], Big::NTH, 0, st>>>(gw);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     norm_finalize_group<<<gn.start[n], 256, 0, st>>>(gn);
     return hipGetLastError();
