@@ -258,6 +258,10 @@ def main():
                     help="time the fused compose forward/backward against the eager op sequence (torch ops on "
                          "the GPU, the pages' comparator) over the workloads' activation shapes and a small-shape "
                          "grid, and print them as one JSON line")
+    ap.add_argument("--library", action="store_true",
+                    help="time the vendor library (hipBLASLt through torch) on the norm's dominant contraction "
+                         "W0 A^T, on the Gram A A^T and on the eager merge, beside this library's norm and merge "
+                         "at the r = 384 workloads, and print them as one JSON line")
     ap.add_argument("--ceilings", action="store_true",
                     help="measure the ceilings only (MFMA-only loops, streams, one CU's reads, the W0 pass's "
                          "access pattern) and print them as one JSON line")
@@ -275,6 +279,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.crossover:
         return crossover_main(args, D, dev)
+    if args.library:
+        return library_main(args, D, dev)
     if args.ceilings:
         from dora_adapter_factored_amd import ceilings as CL
         print(json.dumps({"metric": "measured ceilings (MI355X)", "ceilings": CL.measure(dev, full=True)}), flush=True)
@@ -615,6 +621,75 @@ def crossover_main(args, D, dev):
         torch.cuda.empty_cache()
     print(json.dumps({"metric": "fused compose vs eager op sequence, us per call (bf16, one MI355X)",
                       "rows": rows}), flush=True)
+
+
+def library_main(args, D, dev):
+    """Context, not a target: the vendor GEMM library (hipBLASLt, reached
+    through torch.mm / torch.addmm) on pieces of the same work, beside this
+    library's whole calls.  The norm's dominant contraction W0 A^T alone
+    (no base term, no Gram term, no row dots), the Gram A A^T alone, and the
+    merge as the two-op eager sequence g * addmm(W0, B, A, alpha = s).
+    Rotating input copies keep every timed loop past twice the MALL; the
+    calls alternate between the two sides in four batches and the best
+    batch's mean is reported."""
+    stream = torch.cuda.current_stream(dev)
+    rows = []
+    for cfg in (3, 4):
+        spec = DI.CONFIGS[cfg]
+        d_out, d_in, r, s = spec.d_out, spec.d_in, spec.r, spec.s
+        layer = DI.make_layer(spec, DI.config_seed(cfg), device=dev, activations=False)
+        dt = layer.W0.dtype
+        eps = D.default_eps(dt)
+        nb = (d_out * d_in + r * (d_in + d_out)) * layer.W0.element_size()
+        nsets = max(2, int(np.ceil(2 * MALL_BYTES / nb)) + 1)
+        sets = [dict(W0=layer.W0, A=layer.A, B=layer.B, m=layer.m)]
+        sets += [dict(W0=layer.W0.clone(), A=layer.A.clone(), B=layer.B.clone(), m=layer.m.clone())
+                 for _ in range(nsets - 1)]
+        for st in sets:
+            st["wn"], st["g"] = torch.empty(d_out, device=dev), torch.empty(d_out, device=dev)
+        ws_norm = torch.empty(D.norm_workspace_size(d_out, d_in, r, dt), dtype=torch.uint8, device=dev)
+        ws_merge = torch.empty(D.merge_workspace_size(d_in, r, dt), dtype=torch.uint8, device=dev)
+        w_out = torch.empty_like(layer.W0)
+        fns = {
+            "norm": lambda st: D.factored_norm(st["W0"], st["A"], st["B"], s, st["m"], eps, wnorm=st["wn"],
+                                               g=st["g"], ws=ws_norm),
+            "lib_mm_W0_At": lambda st: torch.mm(st["W0"], st["A"].t()),
+            "lib_mm_A_At": lambda st: torch.mm(st["A"], st["A"].t()),
+            "merge": lambda st: D.merge(st["W0"], st["A"], st["B"], st["g"], s, out=w_out, ws=ws_merge),
+            "lib_eager_merge": lambda st: torch.addmm(st["W0"], st["B"], st["A"], alpha=s).mul_(
+                st["g"].to(dt).unsqueeze(1)),
+        }
+        fns["norm"](sets[0])   # g for the merges
+        for st in sets[1:]:
+            st["g"].copy_(sets[0]["g"])
+        reps = 40
+        best = {k: float("inf") for k in fns}
+        for trial in range(4):
+            for name, fn in fns.items():
+                for i in range(3):
+                    fn(sets[i % nsets])
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(int(2e7))
+                e0.record(stream)
+                for i in range(reps):
+                    fn(sets[i % nsets])
+                e1.record(stream)
+                torch.cuda.synchronize()
+                best[name] = min(best[name], e0.elapsed_time(e1) * 1e3 / reps)
+        mm = 2.0 * d_out * d_in * r
+        row = {"workload": spec.name, **{k + "_us": round(v, 1) for k, v in best.items()},
+               "norm_TFLOPs": round(norm_flops(d_out, d_in, r) / best["norm"] / 1e6, 1),
+               "lib_mm_W0_At_TFLOPs": round(mm / best["lib_mm_W0_At"] / 1e6, 1),
+               "lib_mm_A_At_TFLOPs": round(2.0 * r * r * d_in / best["lib_mm_A_At"] / 1e6, 1),
+               "merge_TFLOPs": round(mm / best["merge"] / 1e6, 1),
+               "lib_eager_merge_TFLOPs": round(mm / best["lib_eager_merge"] / 1e6, 1)}
+        rows.append(row)
+        print(f"[library] {row}", file=sys.stderr, flush=True)
+        del sets, ws_norm, ws_merge, w_out, layer
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "this library's norm and merge beside the vendor GEMM library on pieces of the "
+                                "same work, us per call (bf16, one MI355X)", "rows": rows}), flush=True)
 
 
 SWEEP_METRIC = "many-module sweep: norm + compose fwd/bwd ms per step (64 layers x 7 projections, r=384 bf16)"

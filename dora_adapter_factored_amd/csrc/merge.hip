@@ -126,6 +126,52 @@ __global__ __launch_bounds__(256) void transpose_a_bf16(const bf16_t* __restrict
     }
 }
 
+// A^T as the tile kernel's LDS stages hold it: block (nt, kt) is rows
+// nt*128 .. nt*128 + 127 of A^T (columns of A) by K values kt*32 .. kt*32 + 31,
+// 64 bytes per row, with the row's 16-byte chunk c at slot c ^ swz64(row).
+// Blocks are 8 KB and contiguous, so every DMA instruction of a stage copies
+// 1 KiB of consecutive bytes (eight whole 128-byte lines) instead of sixteen
+// 64-byte row pieces.  Rows past d_in and K past r are zeros.  The transpose
+// goes through LDS as in transpose_a_bf16.
+constexpr int kTileRows = 128, kTileK = 32;
+
+__global__ __launch_bounds__(256) void transpose_a_tiles_bf16(const bf16_t* __restrict__ A, int64_t r,
+                                                              int64_t d_in, char* __restrict__ At, int64_t r_pad,
+                                                              int64_t n_pad) {
+    __shared__ uint32_t tile[kTrTile][kTrPitchW];   // [n][k / 2]
+    const int tid = threadIdx.x;
+    const int64_t n0 = (int64_t)blockIdx.x * kTrTile, k0 = (int64_t)blockIdx.y * kTrTile;
+    {
+        const int cc = tid & 7, kp = tid >> 3;
+        const int64_t n = n0 + (int64_t)cc * 8, k = k0 + 2 * kp;
+        Pack<bf16_t> lo, hi;
+        lo.u = (k < r && n < d_in) ? *reinterpret_cast<const u32x4_t*>(A + k * d_in + n) : u32x4_t{0u, 0u, 0u, 0u};
+        hi.u = (k + 1 < r && n < d_in) ? *reinterpret_cast<const u32x4_t*>(A + (k + 1) * d_in + n)
+                                       : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t w = (uint32_t)__builtin_bit_cast(uint16_t, lo.e[e]) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, hi.e[e]) << 16);
+            tile[cc * 8 + e][kp] = w;
+        }
+    }
+    __syncthreads();
+    const int64_t nk = r_pad / kTileK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = tid + 256 * i, nr = c >> 3, kc = c & 7;
+        const int64_t n = n0 + nr, k = k0 + (int64_t)kc * 8;
+        if (n < n_pad && k < r_pad) {
+            u32x4_t v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = tile[nr][kc * 4 + j];
+            const int rr = (int)(n % kTileRows), ch = (int)((k % kTileK) / 8);
+            const int64_t blk = (n / kTileRows) * nk + k / kTileK;
+            *reinterpret_cast<u32x4_t*>(At + (blk * kTileRows + rr) * 64 + ((ch ^ swz64(rr)) << 4)) = v;
+        }
+    }
+}
+
 // ------------------------------------------------------------- MFMA traits
 // A k-tile holds 64 bytes of K per row.  In each of its two MFMA k-steps a
 // lane supplies the 16-byte chunk 2*step + lane/32 of its row, for both
@@ -413,7 +459,19 @@ __device__ __forceinline__ void wait_stage(int after, bool w0) {
     }
 }
 
-template <typename E, bool DIRECT>
+// DMA of one 1 KiB run of a tiled operand block into LDS at dst.
+__device__ __forceinline__ void dma_run(const char* src, int lane, char* dst) {
+    const uint64_t addr = reinterpret_cast<uint64_t>(src);
+    i32x4_t rs;
+    rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+    rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32));
+    rs[2] = 1024;
+    rs[3] = kRsrcWord3;
+    raw_buffer_load_lds(rs, (lds_void_t*)dst, 16, lane * 16, 0, 0, 0);
+}
+
+// TILED: a.At holds A^T in the stage layout of transpose_a_tiles_bf16.
+template <typename E, bool DIRECT, bool TILED = false>
 __global__ __launch_bounds__(kNTh, sizeof(E) == 2 ? 3 : 2) void merge_tile_dma(MergeArgs a) {
     int mt, nt;
     if (!merge_tile_of(a, mt, nt)) return;
@@ -464,11 +522,15 @@ __global__ __launch_bounds__(kNTh, sizeof(E) == 2 ? 3 : 2) void merge_tile_dma(M
             }
             return;
         }
+        const char* rblk = static_cast<const char*>(a.At) + ((int64_t)nt * nk + kt) * (kBN * kRowB);
 #pragma unroll
         for (int q = 0; q < kDmaPerWave / 2; ++q) {
             const int grp = wave + q * (kNTh / 64);
             dma_group(lop, grp, kt, loff, chunk_b, st);
-            dma_group(rop, grp, kt, roff, chunk_b, st + kBM * kRowB);
+            if constexpr (TILED)
+                dma_run(rblk + grp * 1024, lane, st + kBM * kRowB + grp * 1024);
+            else
+                dma_group(rop, grp, kt, roff, chunk_b, st + kBM * kRowB);
         }
     };
     const E* W0 = static_cast<const E*>(a.W0);
@@ -769,7 +831,18 @@ hipError_t merge_typed(const void* W0, const void* A, const void* B, const float
     const bool aligned = d_in % VEC == 0 && r % VEC == 0 && al16(W0) && al16(B) && al16(W);
     // bf16 with one k-tile of r: the tile kernel stages A^T from A itself
     const bool a_direct = sizeof(E) == 2 && aligned && al16(A) && r_pad == KT;
+    // 256 x 256 tiles where they make one round of workgroups
+    const int64_t big_tiles = ((d_out + BigMerge::BM - 1) / BigMerge::BM) * ((d_in + BigMerge::BN - 1) / BigMerge::BN);
+    const bool big = sizeof(E) == 2 && aligned && !a_direct && big_tiles >= kMergeBigMinTiles &&
+                     big_tiles <= kMergeBigMaxTiles;
+    // the 128 x 128 bf16 kernel reads A^T as contiguous stage blocks
+    const bool tiled = sizeof(E) == 2 && aligned && !a_direct && !big && d_in % VEC == 0 && al16(A);
+    const int64_t n_pad = (d_in + kTileRows - 1) / kTileRows * kTileRows;
     if (a_direct) {
+    } else if (tiled) {
+        if constexpr (sizeof(E) == 2)
+            transpose_a_tiles_bf16<<<dim3((unsigned)(n_pad / kTrTile), tgrid.y), 256, 0, st>>>(
+                A_bf16(A), r, d_in, reinterpret_cast<char*>(At), r_pad, n_pad);
     } else if (d_in % VEC == 0 && al16(A)) {
         if constexpr (sizeof(E) == 2)
             transpose_a_bf16<<<tgrid, 256, 0, st>>>(A_bf16(A), r, d_in, reinterpret_cast<bf16_t*>(At), r_pad);
@@ -779,10 +852,6 @@ hipError_t merge_typed(const void* W0, const void* A, const void* B, const float
     else
         transpose_a<E><<<tgrid, 256, 0, st>>>(static_cast<const E*>(A), r, d_in, At, r_pad);
 
-    // 256 x 256 tiles where they make one round of workgroups
-    const int64_t big_tiles = ((d_out + BigMerge::BM - 1) / BigMerge::BM) * ((d_in + BigMerge::BN - 1) / BigMerge::BN);
-    const bool big = sizeof(E) == 2 && aligned && !a_direct && big_tiles >= kMergeBigMinTiles &&
-                     big_tiles <= kMergeBigMaxTiles;
     const int64_t bm = big ? BigMerge::BM : kBM, bn = big ? BigMerge::BN : kBN;
     MergeArgs a;
     a.W0 = W0;
@@ -804,6 +873,8 @@ hipError_t merge_typed(const void* W0, const void* A, const void* B, const float
         merge_tile_big<<<grid, BigMerge::NTH, 0, st>>>(a);
     } else if (a_direct) {
         if constexpr (sizeof(E) == 2) merge_tile_dma<E, true><<<grid, kNTh, 0, st>>>(a);
+    } else if (tiled) {
+        if constexpr (sizeof(E) == 2) merge_tile_dma<E, false, true><<<grid, kNTh, 0, st>>>(a);
     } else if (aligned) {
         merge_tile_dma<E, false><<<grid, kNTh, 0, st>>>(a);
     }
@@ -818,7 +889,8 @@ hipError_t merge_typed(const void* W0, const void* A, const void* B, const float
 size_t merge_workspace_bytes(int64_t d_in, int64_t r, int dtype) {
     const int64_t kt = dtype == kF32 ? MergeMma<float>::KT : MergeMma<bf16_t>::KT;
     const int64_t r_pad = (r + kt - 1) / kt * kt;
-    return align_up((size_t)d_in * (size_t)r_pad * dtype_size(dtype), 256);
+    const int64_t n_pad = (d_in + kTileRows - 1) / kTileRows * kTileRows;   // tiled A^T covers whole tiles
+    return align_up((size_t)n_pad * (size_t)r_pad * dtype_size(dtype), 256);
 }
 
 hipError_t launch_merge(const void* W0, const void* A, const void* B, const float* g, float s, int64_t d_out,

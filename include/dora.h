@@ -282,7 +282,9 @@ int dora_compose_backward_inner(const void* dy, const void* inner, const float* 
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Workspace bytes needed by dora_merge (host call, launches nothing).
+ * Workspace bytes needed by dora_merge (host call, launches nothing): A
+ * transposed, with d_in rounded up to whole 128-row tiles and r to whole
+ * 64-byte k-tiles.
  */
 int dora_merge_workspace_size(int64_t d_in, int64_t r, int dtype, size_t* bytes);
 
@@ -305,8 +307,9 @@ int dora_merge_workspace_size(int64_t d_in, int64_t r, int dtype, size_t* bytes)
  *   W         device [d_out, d_in], dtype, output; may alias W0 exactly (an
  *             in-place merge), must not overlap A, B, g or the workspace.
  *   workspace device scratch of at least dora_merge_workspace_size() bytes,
- *             256-byte aligned; it receives A transposed, no initialisation
- *             needed.
+ *             256-byte aligned; it receives A transposed (bf16: as 8 KB
+ *             blocks of 128 rows by one k-tile, the layout the tile kernel's
+ *             LDS stages take), no initialisation needed.
  */
 int dora_merge(const void* W0, const void* A, const void* B, const float* g, float s, int64_t d_out,
                int64_t d_in, int64_t r, int dtype, void* W, void* workspace, size_t workspace_bytes,
