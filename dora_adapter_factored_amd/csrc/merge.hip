@@ -134,6 +134,7 @@ __global__ __launch_bounds__(256) void transpose_a_bf16(const bf16_t* __restrict
 // 64-byte row pieces.  Rows past d_in and K past r are zeros.  The transpose
 // goes through LDS as in transpose_a_bf16.
 constexpr int kTileRows = 128, kTileK = 32;
+constexpr int kTilePad = 256;   // rows of A^T written: whole tiles of either tile kernel
 
 __global__ __launch_bounds__(256) void transpose_a_tiles_bf16(const bf16_t* __restrict__ A, int64_t r,
                                                               int64_t d_in, char* __restrict__ At, int64_t r_pad,
@@ -678,6 +679,9 @@ __device__ __forceinline__ void wait_stage_big(int after, bool w0) {
     }
 }
 
+// TILED: a.At holds A^T in the stage layout of transpose_a_tiles_bf16 (a
+// 256-row stage is two consecutive 128-row blocks).
+template <bool TILED>
 __global__ __launch_bounds__(BigMerge::NTH, 1) void merge_tile_big(MergeArgs a) {
     typedef bf16_t E;
     typedef BigMerge G;
@@ -705,7 +709,16 @@ __global__ __launch_bounds__(BigMerge::NTH, 1) void merge_tile_big(MergeArgs a) 
 #pragma unroll
         for (int q = 0; q < G::LDMA; ++q) dma_group(lop, wave + q * G::NW, kt, loff, chunk_b, st);
 #pragma unroll
-        for (int q = 0; q < G::RDMA; ++q) dma_group(rop, wave + q * G::NW, kt, roff, chunk_b, st + G::BM * kRowB);
+        for (int q = 0; q < G::RDMA; ++q) {
+            const int grp = wave + q * G::NW;
+            if constexpr (TILED) {
+                const int64_t blk = ((int64_t)nt * (G::BN / kTileRows) + grp / 8) * nk + kt;
+                dma_run(static_cast<const char*>(a.At) + blk * (kTileRows * kRowB) + (grp % 8) * 1024, lane,
+                        st + G::BM * kRowB + grp * 1024);
+            } else {
+                dma_group(rop, grp, kt, roff, chunk_b, st + G::BM * kRowB);
+            }
+        }
     };
     const E* W0 = static_cast<const E*>(a.W0);
     // W0 chunks and the g of one tile row per thread, loaded unconditionally
@@ -835,9 +848,9 @@ hipError_t merge_typed(const void* W0, const void* A, const void* B, const float
     const int64_t big_tiles = ((d_out + BigMerge::BM - 1) / BigMerge::BM) * ((d_in + BigMerge::BN - 1) / BigMerge::BN);
     const bool big = sizeof(E) == 2 && aligned && !a_direct && big_tiles >= kMergeBigMinTiles &&
                      big_tiles <= kMergeBigMaxTiles;
-    // the 128 x 128 bf16 kernel reads A^T as contiguous stage blocks
-    const bool tiled = sizeof(E) == 2 && aligned && !a_direct && !big && d_in % VEC == 0 && al16(A);
-    const int64_t n_pad = (d_in + kTileRows - 1) / kTileRows * kTileRows;
+    // the bf16 tile kernels read A^T as contiguous stage blocks
+    const bool tiled = sizeof(E) == 2 && aligned && !a_direct && al16(A);
+    const int64_t n_pad = (d_in + kTilePad - 1) / kTilePad * kTilePad;
     if (a_direct) {
     } else if (tiled) {
         if constexpr (sizeof(E) == 2)
@@ -870,7 +883,10 @@ hipError_t merge_typed(const void* W0, const void* A, const void* B, const float
     a.per_xcd = (int)((tiles + kNumXCD - 1) / kNumXCD);
     const unsigned grid = (unsigned)(a.per_xcd * kNumXCD);
     if (big) {
-        merge_tile_big<<<grid, BigMerge::NTH, 0, st>>>(a);
+        if (tiled)
+            merge_tile_big<true><<<grid, BigMerge::NTH, 0, st>>>(a);
+        else
+            merge_tile_big<false><<<grid, BigMerge::NTH, 0, st>>>(a);
     } else if (a_direct) {
         if constexpr (sizeof(E) == 2) merge_tile_dma<E, true><<<grid, kNTh, 0, st>>>(a);
     } else if (tiled) {
@@ -889,7 +905,7 @@ hipError_t merge_typed(const void* W0, const void* A, const void* B, const float
 size_t merge_workspace_bytes(int64_t d_in, int64_t r, int dtype) {
     const int64_t kt = dtype == kF32 ? MergeMma<float>::KT : MergeMma<bf16_t>::KT;
     const int64_t r_pad = (r + kt - 1) / kt * kt;
-    const int64_t n_pad = (d_in + kTileRows - 1) / kTileRows * kTileRows;   // tiled A^T covers whole tiles
+    const int64_t n_pad = (d_in + kTilePad - 1) / kTilePad * kTilePad;   // tiled A^T covers whole tiles
     return align_up((size_t)n_pad * (size_t)r_pad * dtype_size(dtype), 256);
 }
 

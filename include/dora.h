@@ -283,7 +283,7 @@ int dora_compose_backward_inner(const void* dy, const void* inner, const float* 
 
 /*
  * Workspace bytes needed by dora_merge (host call, launches nothing): A
- * transposed, with d_in rounded up to whole 128-row tiles and r to whole
+ * transposed, with d_in rounded up to whole 256-row tiles and r to whole
  * 64-byte k-tiles.
  */
 int dora_merge_workspace_size(int64_t d_in, int64_t r, int dtype, size_t* bytes);

@@ -272,11 +272,11 @@ def test_compose_backward_inner_validation(lib):
 
 def test_merge_workspace_size(lib):
     n = ctypes.c_size_t()
-    # A transposed: d_in padded to whole 128-row tiles, r to whole 64-byte k-tiles
+    # A transposed: d_in padded to whole 256-row tiles, r to whole 64-byte k-tiles
     assert lib.dora_merge_workspace_size(8192, 384, 1, ctypes.byref(n)) == 0 and n.value == 8192 * 384 * 2
     assert lib.dora_merge_workspace_size(1000, 40, 1, ctypes.byref(n)) == 0 and n.value == 1024 * 64 * 2
-    assert lib.dora_merge_workspace_size(3, 5, 1, ctypes.byref(n)) == 0 and n.value == 128 * 32 * 2
-    assert lib.dora_merge_workspace_size(100, 40, 0, ctypes.byref(n)) == 0 and n.value == 128 * 48 * 4
+    assert lib.dora_merge_workspace_size(3, 5, 1, ctypes.byref(n)) == 0 and n.value == 256 * 32 * 2
+    assert lib.dora_merge_workspace_size(100, 40, 0, ctypes.byref(n)) == 0 and n.value == 256 * 48 * 4
     assert lib.dora_merge_workspace_size(100, 40, 2, ctypes.byref(n)) == Bn.DORA_ERR_UNSUPPORTED
     assert lib.dora_merge_workspace_size(0, 40, 1, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
     assert lib.dora_merge_workspace_size(10, 1 << 23, 1, ctypes.byref(n)) == Bn.DORA_ERR_INVALID_ARG
