@@ -1122,14 +1122,15 @@ struct Big {
     static constexpr int WM = WG_PER_CU == 2 ? 1 : 2, WN = 4, NW = WM * WN, NTH = NW * 64;
     static constexpr int MT = 4, NT = 3;   // 32 x 32 blocks per wave
     static constexpr int WROWS = MT * 32;  // rows of one wave row
-    static constexpr int BM = WM * WROWS, BN = WN * NT * 32, BK = 32;
-    static constexpr int LS = 4, RS = WG_PER_CU == 2 ? 2 : 3;   // ring stages (left W0 | B, right A | Gs)
+    static constexpr int BM = WM * WROWS, BN = WN * NT * 32, BK = 64;
+    static constexpr int KS = BK / 16;     // 32 x 32 x 16 MFMA steps per k-tile
+    static constexpr int STAGES = 2;       // ring stages, each a k-tile of both operands
     static constexpr int ER = WM * 32;     // epilogue rows per round
-    static_assert(LS > RS && RS >= 2, "left tiles are issued before right tiles of the same step");
-    static constexpr int ROWB = BK * 2;    // bytes of K per tile row
+    static constexpr int ROWB = BK * 2;    // bytes of K per tile row: one whole 128-byte line
     static constexpr int LBYTES = BM * ROWB, RBYTES = BN * ROWB;
-    static constexpr int RING = LS * LBYTES + RS * RBYTES;
-    static constexpr int LPW = BM / 16 / NW, RPW = BN / 16 / NW;   // DMA instructions per wave per tile
+    static constexpr int STAGE = LBYTES + RBYTES;
+    static constexpr int RING = STAGES * STAGE;
+    static constexpr int LPW = BM / 8 / NW, RPW = BN / 8 / NW;   // DMA instructions (8 rows each) per wave per tile
     // epilogue: two staging buffers of 64 B rows (rows padded by 16 bytes)
     // and the per-row partials of all four rounds
     static constexpr int EB_SLOTS = BN * 2 / 16 + 1;
@@ -1138,18 +1139,20 @@ struct Big {
     static constexpr int EB_BYTES = (ER * EB_PITCH + 1023) / 1024 * 1024;
     static constexpr int EPI_BYTES = 2 * EB_BYTES + MT * WN * ER * 4;
     static constexpr int LDS_BYTES = RING > EPI_BYTES ? RING : EPI_BYTES;
-    static_assert(BM / 16 % NW == 0 && BN / 16 % NW == 0, "DMA groups split evenly across waves");
+    static_assert(BM / 8 % NW == 0 && BN / 8 % NW == 0, "DMA groups split evenly across waves");
+    static_assert(NW % 2 == 0, "a wave's DMA groups all have the parity of the wave");
     static_assert(LBYTES % 1024 == 0 && RBYTES % 1024 == 0, "ring stages hold whole 1 KiB DMA instructions");
     static_assert(MT == WN, "each wave sums the base term of one 32-row block");
+    static_assert(LPW + RPW < 64, "vmcnt range");
 };
 
 
-// One operand as the 64-byte-row DMA sees it; lane l moves slot l % 4 of row
-// l / 4 of a 16-row group (1 KiB per instruction).  The row and K offsets of
-// an instruction are wave-uniform, so they move the buffer's base address
-// (scalar registers) while the per-lane part stays one fixed VGPR; the
-// buffer is shrunk by the same amount, so rows past the operand still read
-// zeros.
+// One operand as the 128-byte-row DMA sees it; lane l moves slot l % 8 of row
+// l / 8 of an 8-row group (1 KiB per instruction, eight whole lines).  The
+// row and K offsets of an instruction are wave-uniform, so they move the
+// buffer's base address (scalar registers) while the per-lane part stays one
+// fixed VGPR; the buffer is shrunk by the same amount, so rows past the
+// operand still read zeros.
 struct Dma64 {
     uint32_t base_lo, base_hi;     // address of the workgroup's first row
     int bytes;                     // bytes from there to the operand's end (clamped to 31 bits)
@@ -1171,18 +1174,19 @@ __device__ __forceinline__ Dma64 make_dma64(const Operand& o, int64_t row0) {
     return d;
 }
 
-// Enqueue rows [0, ROWS) of a 64-byte K slab into LDS at dst.  `d` is the
+// Enqueue rows [0, ROWS) of a 128-byte K slab into LDS at dst.  `d` is the
 // phase's operand (scalar fields), k0b the slab's byte offset along K.  Lane
-// l moves slot l % 4 of row l / 4 of each 16-row group: lane_off =
-// (l / 4) * ld_bytes + chunk_b, where chunk_b is the byte offset of the
-// logical chunk that slot holds; a lane_off of kOutOfRange turns the whole
-// load into zeros.  Chunks past the operand's K extent read zeros.  Row and
-// K offsets fit 31 bits: a workgroup's rows of any operand span less than
-// 2^30 bytes.
+// l moves slot l % 8 of row l / 8 of each 8-row group: lane_off =
+// (l / 8) * ld_bytes + chunk_b, where chunk_b is the byte offset of the
+// logical chunk that slot holds (slot ^ swz(row); the groups a wave issues
+// all have the wave's parity, so one chunk serves them all); a lane_off of
+// kOutOfRange turns the whole load into zeros.  Chunks past the operand's K
+// extent read zeros.  Row and K offsets fit 31 bits: a workgroup's rows of
+// any operand span less than 2^30 bytes.
 template <int ROWS>
-__device__ __forceinline__ void dma64_tile(const Dma64& d, int lane_off, int chunk_b, int k0b, char* dst,
-                                           int wave) {
-    constexpr int PER = ROWS / 16 / Big::NW;
+__device__ __forceinline__ void dma128_tile(const Dma64& d, int lane_off, int chunk_b, int k0b, char* dst,
+                                            int wave) {
+    constexpr int PER = ROWS / 8 / Big::NW;
     const int ldb = d.ld_bytes, bytes = d.bytes, kmax = d.kmax_bytes;
     const uint64_t base = ((uint64_t)d.base_hi << 32) | d.base_lo;
     const bool full = k0b + Big::ROWB <= kmax;
@@ -1190,7 +1194,7 @@ __device__ __forceinline__ void dma64_tile(const Dma64& d, int lane_off, int chu
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
         const int grp = wave + q * Big::NW;
-        const int off = grp * 16 * ldb + k0b;
+        const int off = grp * 8 * ldb + k0b;
         const int left = bytes > off ? bytes - off : 0;
         const uint64_t addr = base + (uint32_t)off;
         i32x4_t rs;
@@ -1225,8 +1229,6 @@ __device__ __forceinline__ void w0_pass_big_seg(const W0PassArgs& a, const int i
             for (int e = 0; e < 16; ++e) acc[mt][nt][e] = 0.0f;
     float bs = 0.0f;
 
-    char* lring = smem;
-    char* rring = smem + G::LS * G::LBYTES;
     if (n > 0) {
         const Dma64 L0 = make_dma64(c.left0, m0);
         const Dma64 L1 = make_dma64(c.left1, m0);
@@ -1234,15 +1236,12 @@ __device__ __forceinline__ void w0_pass_big_seg(const W0PassArgs& a, const int i
         const Dma64 R1 = make_dma64(c.right1, n0);
         // per-lane DMA offsets; the two operands of a phase share a row pitch
         // (W0 and A: d_in; B and Gs: r, a multiple of 8 on this path)
-        const int dchunk = ((lane & 3) ^ swz64(lane >> 2)) * 16;
-        const int doff0 = (lane >> 2) * L0.ld_bytes + dchunk;
-        const int doff1 = (lane >> 2) * L1.ld_bytes + dchunk;
+        const int dchunk = ((lane & 7) ^ (lane >> 3) ^ (wave & 1)) * 16;
+        const int doff0 = (lane >> 3) * L0.ld_bytes + dchunk;
+        const int doff1 = (lane >> 3) * L1.ld_bytes + dchunk;
         // fragment byte offsets inside a tile: row (l % 32) of a 32-row block,
-        // logical chunk 2 ks + l / 32 for k16-step ks
-        const int sw = swz64(lane & 31);
-        const int h = (lane >> 5) ^ sw;
-        const int fo0 = (lane & 31) * G::ROWB + (h << 4);
-        const int fo1 = (lane & 31) * G::ROWB + ((h ^ 2) << 4);
+        // logical chunk 2 ks + l / 32 for MFMA step ks, i.e. fo0 ^ (ks << 5)
+        const int fo0 = (lane & 31) * G::ROWB + (((lane >> 5) ^ swz(lane & 31)) << 4);
         const int lrow0 = wm * G::WROWS * G::ROWB, rrow0 = wn * 96 * G::ROWB;
         const float base_on = base_dst != nullptr ? 1.0f : 0.0f;
 
@@ -1252,11 +1251,11 @@ __device__ __forceinline__ void w0_pass_big_seg(const W0PassArgs& a, const int i
             if (t >= n) t -= n;
             return kt_begin + t;
         };
-        // Loads of step i; steps past the last tile still issue (reading
-        // zeros into a stage no one reads), so the number of loads in flight
-        // is the same at every step and the loop carries no branches.
-        auto issue = [&](int i, auto rows, char* ring, int stage_bytes, int stages, const Dma64& P0,
-                         const Dma64& P1) __attribute__((always_inline)) {
+        // Loads of step i into stage i % 2; steps past the last tile still
+        // issue (reading zeros into a stage no one reads), so the loop carries
+        // no branches.
+        auto issue_op = [&](int i, auto rows, int soff, const Dma64& P0, const Dma64& P1)
+            __attribute__((always_inline)) {
             const bool valid = i < n;
             const int kt = tile(valid ? i : 0);
             const bool ph0 = kt < c.nkt0;
@@ -1268,17 +1267,16 @@ __device__ __forceinline__ void w0_pass_big_seg(const W0PassArgs& a, const int i
             d.kmax_bytes = ph0 ? P0.kmax_bytes : P1.kmax_bytes;
             const int lo = valid ? (ph0 ? doff0 : doff1) : kOutOfRange;
             const int k0b = (ph0 ? kt : kt - c.nkt0) * G::ROWB;
-            dma64_tile<decltype(rows)::value>(d, lo, dchunk, k0b, ring + (i % stages) * stage_bytes, wave);
+            dma128_tile<decltype(rows)::value>(d, lo, dchunk, k0b, smem + (i % G::STAGES) * G::STAGE + soff, wave);
         };
-        auto issue_left = [&](int i) __attribute__((always_inline)) {
-            issue(i, IntC<G::BM>{}, lring, G::LBYTES, G::LS, L0, L1);
+        auto issue = [&](int i) __attribute__((always_inline)) {
+            issue_op(i, IntC<G::BM>{}, 0, L0, L1);
+            issue_op(i, IntC<G::BN>{}, G::LBYTES, R0, R1);
         };
-        auto issue_right = [&](int i) __attribute__((always_inline)) {
-            issue(i, IntC<G::BN>{}, rring, G::RBYTES, G::RS, R0, R1);
-        };
-        auto read = [&](int i, int fo, bf16x8_t (&av)[G::MT], bf16x8_t (&bv)[G::NT]) __attribute__((always_inline)) {
-            const char* Lt = lring + (i % G::LS) * G::LBYTES + lrow0 + fo;
-            const char* Rt = rring + (i % G::RS) * G::RBYTES + rrow0 + fo;
+        auto read = [&](int i, int ks, bf16x8_t (&av)[G::MT], bf16x8_t (&bv)[G::NT]) __attribute__((always_inline)) {
+            const int fo = fo0 ^ (ks << 5);
+            const char* Lt = smem + (i % G::STAGES) * G::STAGE + lrow0 + fo;
+            const char* Rt = smem + (i % G::STAGES) * G::STAGE + G::LBYTES + rrow0 + fo;
 #pragma unroll
             for (int mt = 0; mt < G::MT; ++mt) av[mt] = *reinterpret_cast<const bf16x8_t*>(Lt + mt * 32 * G::ROWB);
 #pragma unroll
@@ -1312,50 +1310,49 @@ __device__ __forceinline__ void w0_pass_big_seg(const W0PassArgs& a, const int i
             return tile(i) < c.nkt0 ? base_on : 0.0f;
         };
 
-        // Software pipeline over k-tiles.  Tile j: MFMAs of k16-step 0 and
-        // its base term; fragments of step 1; MFMAs of step 1 except the last
-        // HOLD, and its base term.  Then wait for tile j + 1 (this wave's
-        // loads; this wave's fragment reads of tile j are complete), barrier
-        // (every wave's loads of tile j + 1 landed, every wave is done with
-        // tile j's stages), enqueue right(j + RS) and left(j + LS) into those
-        // stages, read tile j + 1's step-0 fragments, and only then issue the
+        // Software pipeline over k-tiles, two stages: tile j + 1 loads while
+        // tile j is computed.  Tile j: its four MFMA steps, the fragments of
+        // each next step read while the previous step's MFMAs run (two
+        // register sets), all but the last HOLD MFMAs of step 3.  Then wait
+        // for tile j + 1 (this wave's loads; its fragment reads of tile j are
+        // complete), barrier (every wave's loads of tile j + 1 landed, every
+        // wave is done with tile j's stage), enqueue tile j + 2 into that
+        // stage, read tile j + 1's step-0 fragments, and only then issue the
         // held-back MFMAs, which keep the matrix pipe busy across the barrier
-        // and the LDS latency.  Loads complete in issue order and every left
-        // tile is issued one step or more before the right tile of the same
-        // index, so waiting for right(j + 1) covers left(j + 1); what may stay
-        // in flight is the left tile issued with right(j + 1) and everything
-        // issued at the RS - 2 later steps.
+        // and the LDS latency.  (Enqueueing tile j + 2 earlier, behind a
+        // second barrier once step 3's fragments are read, measured 2-4%
+        // slower.)
         constexpr int HOLD = 2;
         constexpr int ALL = G::MT * G::NT;
-        constexpr int INFLIGHT = G::LPW + (G::RS - 2) * (G::RPW + G::LPW);
         auto main_loop = [&](auto wnc) __attribute__((always_inline)) {
             bf16x8_t a0[G::MT], b0[G::NT], a1[G::MT], b1[G::NT];
-            // the steps before tile 0, in the steady-state issue order
-#pragma unroll
-            for (int t = 0; t < G::LS - 1; ++t) {
-                if (t >= G::LS - G::RS) issue_right(t - (G::LS - G::RS));
-                issue_left(t);
-            }
-            wait_vmcnt<INFLIGHT>();
+            issue(0);
+            issue(1);
+            wait_vmcnt<G::LPW + G::RPW>();   // tile 0 landed; tile 1 may be in flight
             __builtin_amdgcn_s_barrier();
-            issue_right(G::RS - 1);
-            issue_left(G::LS - 1);
-            read(0, fo0, a0, b0);
+            read(0, 0, a0, b0);
             for (int j = 0; j < n - 1; ++j) {
                 const float on = base_on_at(j);
                 mma(a0, b0, 0, ALL);
                 base_sum(wnc, a0, on);
-                __builtin_amdgcn_sched_barrier(0);   // step-1 fragments reuse step 0's registers
-                read(j, fo1, a1, b1);
+                __builtin_amdgcn_sched_barrier(0);
+                read(j, 1, a1, b1);
+                mma(a1, b1, 0, ALL);
+                base_sum(wnc, a1, on);
+                __builtin_amdgcn_sched_barrier(0);
+                read(j, 2, a0, b0);
+                mma(a0, b0, 0, ALL);
+                base_sum(wnc, a0, on);
+                __builtin_amdgcn_sched_barrier(0);
+                read(j, 3, a1, b1);
                 mma(a1, b1, 0, ALL - HOLD);
                 base_sum(wnc, a1, on);
                 __builtin_amdgcn_sched_barrier(0);
-                wait_vmcnt<INFLIGHT>();
+                wait_vmcnt<0>();
                 __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
                 __builtin_amdgcn_s_barrier();
-                issue_right(j + G::RS);
-                issue_left(j + G::LS);
-                read(j + 1, fo0, a0, b0);
+                issue(j + 2);
+                read(j + 1, 0, a0, b0);
                 __builtin_amdgcn_sched_barrier(0);
                 mma(a1, b1, ALL - HOLD, ALL);
             }
@@ -1364,7 +1361,15 @@ __device__ __forceinline__ void w0_pass_big_seg(const W0PassArgs& a, const int i
                 mma(a0, b0, 0, ALL);
                 base_sum(wnc, a0, on);
                 __builtin_amdgcn_sched_barrier(0);
-                read(n - 1, fo1, a1, b1);
+                read(n - 1, 1, a1, b1);
+                mma(a1, b1, 0, ALL);
+                base_sum(wnc, a1, on);
+                __builtin_amdgcn_sched_barrier(0);
+                read(n - 1, 2, a0, b0);
+                mma(a0, b0, 0, ALL);
+                base_sum(wnc, a0, on);
+                __builtin_amdgcn_sched_barrier(0);
+                read(n - 1, 3, a1, b1);
                 mma(a1, b1, 0, ALL);
                 base_sum(wnc, a1, on);
             }
@@ -2163,13 +2168,14 @@ namespace {
 
 // The balanced split is taken when the uniform one fills less than
 // kBalanceMaxFill percent of a round and its workgroups walk at least
-// kBalanceMinKtiles k-tiles.  Measured on MI355X at r = 384: 28672 x 8192
-// (112 m-tiles, 134 k-tiles per workgroup) 241.8 -> 230.9 us; with 60-90
-// k-tiles per workgroup the second epilogue costs more than the idle CUs
-// (27648 x 5120 a tie, 14336 x 8192 132.1 -> 136.1 us, 28672 x 4096 135.3 ->
-// 139.5 us, 20000 x 8200 188.0 -> 190.8 us).
+// kBalanceMinKtiles 64-wide k-tiles (3840 of K).  Measured on MI355X at
+// r = 384, with 32-wide k-tiles: 28672 x 8192 (112 m-tiles, 8576 of K per
+// workgroup) 240.4 -> 233.2 us; with 1920-2880 of K per workgroup the second
+// epilogue costs more than the idle CUs (27648 x 5120 a tie, 14336 x 8192
+// 132.1 -> 136.1 us, 28672 x 4096 135.3 -> 139.5 us, 20000 x 8200 188.0 ->
+// 190.8 us).
 constexpr int64_t kBalanceMaxFill = 95;
-constexpr int kBalanceMinKtiles = 120;
+constexpr int kBalanceMinKtiles = 60;
 
 NormPlan plan_norm_impl(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool base_only, bool allow_big) {
     NormPlan p{};
@@ -2200,12 +2206,12 @@ NormPlan plan_norm_impl(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool 
         const int nkt = p.nkt_w0 + p.nkt_g;
         // Measured: a single round of workgroups beats several, whose every
         // round pays the cold start and the epilogue again; so split K as far
-        // as one round allows, keeping >= 8 k-tiles per workgroup.
+        // as one round allows, keeping >= 4 k-tiles (256 of K) per workgroup.
         const int64_t tiles = (int64_t)p.n_mtiles * p.n_ntiles;
         const int64_t round = (int64_t)kNumCU * Big::WG_PER_CU;
         ks = tiles >= round ? 1 : (int)(round / tiles);
         if (ks > 64) ks = 64;
-        while (ks > 1 && nkt / ks < 8) --ks;
+        while (ks > 1 && nkt / ks < 4) --ks;
         // A uniform split that leaves CUs idle (112 m-tiles in two K-chunks
         // use 224 of 256) is traded for equal ranges over all CUs when the
         // workgroups are long: some then run two segments, i.e. two
