@@ -951,16 +951,44 @@ __global__ __launch_bounds__(WM * WN * 64, (ALIGNED && WN == 1 && NT == 1) ? 3 :
     }
 }
 
+// One operand as the 128-byte-row DMA sees it; lane l moves slot l % 8 of row
+// l / 8 of an 8-row group (1 KiB per instruction, eight whole lines).  The
+// row and K offsets of an instruction are wave-uniform, so they move the
+// buffer's base address (scalar registers) while the per-lane part stays one
+// fixed VGPR; the buffer is shrunk by the same amount, so rows past the
+// operand still read zeros.
+struct Dma64 {
+    uint32_t base_lo, base_hi;     // address of the workgroup's first row
+    int bytes;                     // bytes from there to the operand's end (clamped to 31 bits)
+    int ld_bytes, kmax_bytes;
+};
+
+__device__ __forceinline__ Dma64 make_dma64(const Operand& o, int64_t row0) {
+    Dma64 d;
+    const int64_t ldb = o.ld * 2;
+    const uint64_t base = reinterpret_cast<uint64_t>(static_cast<const char*>(o.p) + row0 * ldb);
+    int64_t bytes = (o.rows - row0) * ldb;
+    if (bytes < 0) bytes = 0;
+    if (bytes > 0x7ffffff0) bytes = 0x7ffffff0;
+    d.base_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    d.base_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
+    d.bytes = __builtin_amdgcn_readfirstlane((int)bytes);
+    d.ld_bytes = __builtin_amdgcn_readfirstlane((int)ldb);
+    d.kmax_bytes = __builtin_amdgcn_readfirstlane((int)(o.kmax * 2));
+    return d;
+}
+
 // ------------------------------------------------------------- W0 pass, whole rows (low rank)
 // bf16, 16-byte aligned operands, r <= 32.  A workgroup owns 16 whole rows
 // of W0 and its eight waves split K eight ways (measured: 5-9% faster than
-// four waves, by the loads it keeps in flight per CU): each runs the narrow
-// register-fed loop over its K range (U, base and Gram blocks of that range,
-// whose Gram term is a sum over K ranges like any other K split), adds
-// (s/2) B G_w to its U accumulators and takes the row dots with B.  The
-// workgroup then adds the waves' base and cross partials in wave order in
-// LDS and writes wnorm and g itself: no partials leave the workgroup and no
-// assembly kernel runs.
+// four waves, by the loads it keeps in flight per CU): each walks its K range
+// (U, base and Gram blocks of that range, whose Gram term is a sum over K
+// ranges like any other K split), through its own LDS-DMA ring when the rows
+// fit one round of workgroups, else with register-fed fragment loads; then it
+// adds (s/2) B G_w to its U accumulators and takes the row dots with B.  The
+// workgroup adds the waves' base and cross partials in wave order in LDS and
+// writes wnorm and g itself: no partials leave the workgroup and no assembly
+// kernel runs.
 struct W0RowsArgs {
     Contraction c;        // left0 = W0, right0 = A; no second phase
     const void* B;        // [d_out, r]
@@ -973,9 +1001,108 @@ struct W0RowsArgs {
 
 constexpr int kRowsWaves = 8;
 constexpr int kRowsPerWg = 16;
-constexpr int kRowsDepth = kNarrowDepth;
 
+// The whole-row kernel's K walk.  Each wave moves its own 64-element k-tiles
+// of W0 (the workgroup's 16 rows) and of A (NT * 16 rows, zeros past r) by
+// LDS DMA into a private ring of D stages: whole 128-byte rows, so every
+// request to L2 is one full line (register-fed fragment loads can only ask
+// for 64 bytes of a row at a time, and a CU keeps only so many requests in
+// flight).  The fragments are read from the ring with the 128-byte-row
+// swizzle; per k-tile the MFMAs, base term and Gram blocks are those of the
+// register-fed loop.  A wave waits only for its own loads, so the walk has no
+// barriers.
 template <int NT>
+struct RowsRing {
+    static constexpr int AROWS = NT * 16;
+    static constexpr int D = NT == 1 ? 4 : 3;                       // stages per wave
+    static constexpr int STAGE = (kRowsPerWg + AROWS) * 128;        // bytes per stage
+    static constexpr int PER = (kRowsPerWg + AROWS) / 8;            // DMA instructions per stage
+    static constexpr int BYTES = kRowsWaves * D * STAGE;
+    static_assert((D - 2) * PER < 64, "vmcnt range");
+};
+
+template <int NT, int NG>
+__device__ __forceinline__ void mainloop_rows_dma(const Contraction& c, int64_t m0, int kt_begin, int kt_end,
+                                                  char* ring, f32x4_t (&acc)[1][NT], f32x4_t (&gacc)[NG],
+                                                  float& bsum) {
+    typedef Mma<bf16_t> M;
+    typedef RowsRing<NT> RR;
+    constexpr int D = RR::D;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = kt_end - kt_begin;
+    bsum = 0.0f;
+    if (n <= 0) return;
+    const Dma64 W = make_dma64(c.left0, m0);
+    const Dma64 A = make_dma64(c.right0, 0);
+    // lane l moves slot l % 8 of row l / 8 of an 8-row group, carrying
+    // logical chunk slot ^ swz(row) = (l % 8) ^ (l / 8) ^ (group parity)
+    const int ce = ((lane & 7) ^ (lane >> 3)) * 16, co = ce ^ 16;
+    const int we = (lane >> 3) * W.ld_bytes + ce, wo = (lane >> 3) * W.ld_bytes + co;
+    const int ae = (lane >> 3) * A.ld_bytes + ce, ao = (lane >> 3) * A.ld_bytes + co;
+    char* mine = ring + wave * D * RR::STAGE;
+    auto group = [&](const Dma64& d, int g, int lane_off, int chunk_b, int k0b, char* dst) __attribute__((always_inline)) {
+        const int kleft = d.kmax_bytes - k0b;
+        const int voff = chunk_b < kleft ? lane_off : kOutOfRange;
+        const int off = g * 8 * d.ld_bytes + k0b;
+        const int left = d.bytes > off ? d.bytes - off : 0;
+        const uint64_t addr = (((uint64_t)d.base_hi << 32) | d.base_lo) + (uint32_t)off;
+        i32x4_t rs;
+        rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+        rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32));
+        rs[2] = __builtin_amdgcn_readfirstlane(left);
+        rs[3] = 0x00020000;
+        raw_buffer_load_lds(rs, (lds_void_t*)dst, 16, voff, 0, 0, 0);
+    };
+    // step i's loads into stage i % D; steps past the walk load zeros
+    auto issue = [&](int i) __attribute__((always_inline)) {
+        const bool valid = i < n;
+        const int k0b = (kt_begin + (valid ? i : 0)) * 128;
+        char* st = mine + (i % D) * RR::STAGE;
+#pragma unroll
+        for (int g = 0; g < kRowsPerWg / 8; ++g)
+            group(W, g, valid ? ((g & 1) ? wo : we) : kOutOfRange, (g & 1) ? co : ce, k0b, st + g * 1024);
+#pragma unroll
+        for (int g = 0; g < RR::AROWS / 8; ++g)
+            group(A, g, valid ? ((g & 1) ? ao : ae) : kOutOfRange, (g & 1) ? co : ce, k0b,
+                  st + kRowsPerWg * 128 + g * 1024);
+    };
+    const int fr = lane & 15, q = lane >> 4, sw = swz(fr);
+    float bs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) issue(i);
+    for (int t = 0; t < n; ++t) {
+        wait_vmcnt<(D - 2) * RR::PER>();        // step t landed
+        __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): this wave's reads of step t - 1 are done
+        issue(t + D - 1);                      // into step t - 1's stage
+        const char* st = mine + (t % D) * RR::STAGE;
+#pragma unroll
+        for (int ks = 0; ks < M::BK / 32; ++ks) {
+            const M::frag_t af = M::load_frag_swz(st + fr * 128, ks, q, sw);
+            bs += M::frag_sumsq(af);
+            M::frag_t b[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                b[nt] = M::load_frag_swz(st + (kRowsPerWg + nt * 16 + fr) * 128, ks, q, sw);
+                M::mma(acc[0][nt], af, b[nt]);
+            }
+            int g = 0;
+#pragma unroll
+            for (int b1 = 0; b1 < NT; ++b1)
+#pragma unroll
+                for (int b2 = b1; b2 < NT; ++b2) M::mma(gacc[g++], b[b1], b[b2]);
+        }
+    }
+    wait_vmcnt<0>();   // the empty loads issued past the walk
+    bs += __shfl_xor(bs, 16);
+    bs += __shfl_xor(bs, 32);
+    bsum = bs;
+}
+
+// RING: the K walk of mainloop_rows_dma (one round of workgroups: its ring
+// holds the CU's LDS), else the register-fed walk, whose small footprint lets
+// several workgroups share a CU when the rows run to more than one round.
+template <int NT, bool RING>
 __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) {
     typedef bf16_t E;
     typedef Mma<E> M;
@@ -987,7 +1114,12 @@ __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) 
     constexpr int B_NINS = (kRowsPerWg * B_SLOTS + 63) / 64;      // DMA instructions staging B
     constexpr int GS_OFF = B_NINS * 1024;                         // the DMA fills whole 1 KiB blocks
     constexpr int RED_OFF = GS_OFF + kRowsWaves * GIP::BYTES;
-    constexpr int LDS = RED_OFF + 2 * kRowsWaves * kRowsPerWg * 4;
+    constexpr int EPI = RED_OFF + 2 * kRowsWaves * kRowsPerWg * 4;
+    // the K walk's ring follows the staged B and is reused by the Gs tiles
+    // and the reduction once the walk is done
+    constexpr int RING_OFF = GS_OFF;
+    constexpr int RING_END = RING ? RING_OFF + RowsRing<NT>::BYTES : 0;
+    constexpr int LDS = RING_END > EPI ? RING_END : EPI;
     __shared__ __attribute__((aligned(1024))) char smem[LDS];
 
     const int lane = threadIdx.x & 63;
@@ -1003,7 +1135,7 @@ __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) 
     f32x4_t gacc[GIP::NG];
 #pragma unroll
     for (int q = 0; q < GIP::NG; ++q) gacc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float bsum[1];
+    float bsum = 0.0f;
     // m of this workgroup's rows, requested before the K walk so that its
     // latency hides under it (loads retire in issue order, so the walk's
     // first wait covers it)
@@ -1031,7 +1163,15 @@ __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) 
             raw_buffer_load_lds(rs, (lds_void_t*)(smem + ins * 1024), 16, voff, 0, 0, 0);
         }
     }
-    mainloop_w0_narrow<E, 1, NT, true, GIP::NG, kRowsDepth>(a.c, m0, 0, kt_begin, kt_end, 0, true, acc, gacc, bsum);
+    if constexpr (RING) {
+        mainloop_rows_dma<NT, GIP::NG>(a.c, m0, kt_begin, kt_end, smem + RING_OFF, acc, gacc, bsum);
+        __syncthreads();   // every wave is done with the ring
+    } else {
+        float bs[1];
+        mainloop_w0_narrow<E, 1, NT, true, GIP::NG, kNarrowDepth>(a.c, m0, 0, kt_begin, kt_end, 0, true, acc, gacc,
+                                                                 bs);
+        bsum = bs[0];
+    }
 
     // this wave's Gs_w = (s/2) G_w as bf16 [RP][RP], zero past BN
     {
@@ -1080,7 +1220,7 @@ __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) 
         v += __shfl_xor(v, 8);
         if ((lane & 15) == 0) red[(kRowsWaves + wave) * kRowsPerWg + row] = v;
     }
-    if (lane < kRowsPerWg) red[wave * kRowsPerWg + lane] = bsum[0];
+    if (lane < kRowsPerWg) red[wave * kRowsPerWg + lane] = bsum;
     __syncthreads();
     if (threadIdx.x < kRowsPerWg) {
         const int row = threadIdx.x;
@@ -1108,9 +1248,9 @@ __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) 
 // Eight waves in a 2 x 4 grid each accumulate a 128 x 96 block with 32x32x16
 // MFMAs (4 x 3 blocks of 32 x 32, 192 accumulators per lane); one 16-deep
 // step of K needs only 7 operand registers per lane, so two waves fit on
-// every SIMD and cover each other's LDS and memory waits.  Tiles are 32
-// elements of K (64-byte rows): W0 (then B) runs in an LDS ring of LS = 4
-// stages, A (then Gs) in RS = 3 stages, all moved by LDS DMA.
+// every SIMD and cover each other's LDS and memory waits.  Tiles are 64
+// elements of K (whole 128-byte rows, so every DMA request is a full line):
+// W0 | B and A | Gs share a two-stage ring that fills the CU's 160 KB of LDS.
 
 template <int V>
 struct IntC {
@@ -1147,32 +1287,6 @@ struct Big {
 };
 
 
-// One operand as the 128-byte-row DMA sees it; lane l moves slot l % 8 of row
-// l / 8 of an 8-row group (1 KiB per instruction, eight whole lines).  The
-// row and K offsets of an instruction are wave-uniform, so they move the
-// buffer's base address (scalar registers) while the per-lane part stays one
-// fixed VGPR; the buffer is shrunk by the same amount, so rows past the
-// operand still read zeros.
-struct Dma64 {
-    uint32_t base_lo, base_hi;     // address of the workgroup's first row
-    int bytes;                     // bytes from there to the operand's end (clamped to 31 bits)
-    int ld_bytes, kmax_bytes;
-};
-
-__device__ __forceinline__ Dma64 make_dma64(const Operand& o, int64_t row0) {
-    Dma64 d;
-    const int64_t ldb = o.ld * 2;
-    const uint64_t base = reinterpret_cast<uint64_t>(static_cast<const char*>(o.p) + row0 * ldb);
-    int64_t bytes = (o.rows - row0) * ldb;
-    if (bytes < 0) bytes = 0;
-    if (bytes > 0x7ffffff0) bytes = 0x7ffffff0;
-    d.base_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
-    d.base_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
-    d.bytes = __builtin_amdgcn_readfirstlane((int)bytes);
-    d.ld_bytes = __builtin_amdgcn_readfirstlane((int)ldb);
-    d.kmax_bytes = __builtin_amdgcn_readfirstlane((int)(o.kmax * 2));
-    return d;
-}
 
 // Enqueue rows [0, ROWS) of a 128-byte K slab into LDS at dst.  `d` is the
 // phase's operand (scalar fields), k0b the slab's byte offset along K.  Lane
@@ -2115,10 +2229,18 @@ hipError_t norm_typed(const NormPlan& p, const void* W0, const void* A, const vo
             ra.wnorm = wnorm;
             ra.g = g;
             const unsigned grid = (unsigned)((d_out + kRowsPerWg - 1) / kRowsPerWg);
-            if (kCfgs[p.cfg].nt == 1)
-                w0_rows_narrow<1><<<grid, kRowsWaves * 64, 0, st>>>(ra);
-            else
-                w0_rows_narrow<2><<<grid, kRowsWaves * 64, 0, st>>>(ra);
+            const bool ring = grid <= (unsigned)kNumCU;
+            if (kCfgs[p.cfg].nt == 1) {
+                if (ring)
+                    w0_rows_narrow<1, true><<<grid, kRowsWaves * 64, 0, st>>>(ra);
+                else
+                    w0_rows_narrow<1, false><<<grid, kRowsWaves * 64, 0, st>>>(ra);
+            } else {
+                if (ring)
+                    w0_rows_narrow<2, true><<<grid, kRowsWaves * 64, 0, st>>>(ra);
+                else
+                    w0_rows_narrow<2, false><<<grid, kRowsWaves * 64, 0, st>>>(ra);
+            }
             return hipGetLastError();
         }
     }
