@@ -747,6 +747,148 @@ struct GramInPass {
     static constexpr int BYTES = value ? RP * PITCH : 0;
 };
 
+// One operand as the 128-byte-row DMA sees it; lane l moves slot l % 8 of row
+// l / 8 of an 8-row group (1 KiB per instruction, eight whole lines).  The
+// row and K offsets of an instruction are wave-uniform, so they move the
+// buffer's base address (scalar registers) while the per-lane part stays one
+// fixed VGPR; the buffer is shrunk by the same amount, so rows past the
+// operand still read zeros.
+struct Dma64 {
+    uint32_t base_lo, base_hi;     // address of the workgroup's first row
+    int bytes;                     // bytes from there to the operand's end (clamped to 31 bits)
+    int ld_bytes, kmax_bytes;
+};
+
+__device__ __forceinline__ Dma64 make_dma64(const Operand& o, int64_t row0) {
+    Dma64 d;
+    const int64_t ldb = o.ld * 2;
+    const uint64_t base = reinterpret_cast<uint64_t>(static_cast<const char*>(o.p) + row0 * ldb);
+    int64_t bytes = (o.rows - row0) * ldb;
+    if (bytes < 0) bytes = 0;
+    if (bytes > 0x7ffffff0) bytes = 0x7ffffff0;
+    d.base_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    d.base_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
+    d.bytes = __builtin_amdgcn_readfirstlane((int)bytes);
+    d.ld_bytes = __builtin_amdgcn_readfirstlane((int)ldb);
+    d.kmax_bytes = __builtin_amdgcn_readfirstlane((int)(o.kmax * 2));
+    return d;
+}
+
+// The register-free K walk of the narrow forms (bf16, aligned, the Gram
+// term formed in the pass).  Each wave moves its own 64-element k-tiles of
+// W0 (its MT * 16 rows from mrow0) and of A (NT * 16 rows from n0, zeros past
+// r) by LDS DMA into a private ring of D stages: whole 128-byte rows, so
+// every request to L2 is one full line (register-fed fragment loads can only
+// ask for 64 bytes of a row at a time, and a CU keeps only so many requests
+// in flight).  The fragments are read from the ring with the 128-byte-row
+// swizzle; per k-tile the MFMAs, base term and Gram blocks are those of the
+// register-fed loop, and so is the rotated walk.  A wave waits only for its
+// own loads, so the walk has no barriers.
+template <int MT, int NT, int NWAVES, int D>
+struct NarrowRing {
+    static constexpr int ROWS = (MT + NT) * 16;
+    static constexpr int STAGE = ROWS * 128;             // bytes per stage
+    static constexpr int PER = ROWS / 8;                 // DMA instructions per stage
+    static constexpr int BYTES = NWAVES * D * STAGE;
+    static_assert(D >= 2 && (D - 2) * PER < 64, "vmcnt range");
+};
+
+template <int MT, int NT, int NG, int D>
+__device__ __forceinline__ void mainloop_narrow_dma(const Contraction& c, int64_t mrow0, int64_t n0, int kt_begin,
+                                                    int kt_end, int rot, bool want_base, char* ring,
+                                                    f32x4_t (&acc)[MT][NT], f32x4_t (&gacc)[NG],
+                                                    float (&bsum)[MT]) {
+    typedef Mma<bf16_t> M;
+    typedef NarrowRing<MT, NT, 1, D> RR;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = kt_end - kt_begin;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) bsum[mt] = 0.0f;
+    if (n <= 0) return;
+    const Dma64 W = make_dma64(c.left0, mrow0);
+    const Dma64 A = make_dma64(c.right0, n0);
+    // lane l moves slot l % 8 of row l / 8 of an 8-row group, carrying
+    // logical chunk slot ^ swz(row) = (l % 8) ^ (l / 8) ^ (group parity)
+    const int ce = ((lane & 7) ^ (lane >> 3)) * 16, co = ce ^ 16;
+    const int we = (lane >> 3) * W.ld_bytes + ce, wo = (lane >> 3) * W.ld_bytes + co;
+    const int ae = (lane >> 3) * A.ld_bytes + ce, ao = (lane >> 3) * A.ld_bytes + co;
+    char* mine = ring + wave * D * RR::STAGE;
+    auto group = [&](const Dma64& d, int g, int lane_off, int chunk_b, int k0b, char* dst) __attribute__((always_inline)) {
+        const int kleft = d.kmax_bytes - k0b;
+        const int voff = chunk_b < kleft ? lane_off : kOutOfRange;
+        const int off = g * 8 * d.ld_bytes + k0b;
+        const int left = d.bytes > off ? d.bytes - off : 0;
+        const uint64_t addr = (((uint64_t)d.base_hi << 32) | d.base_lo) + (uint32_t)off;
+        i32x4_t rs;
+        rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+        rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32));
+        rs[2] = __builtin_amdgcn_readfirstlane(left);
+        rs[3] = 0x00020000;
+        raw_buffer_load_lds(rs, (lds_void_t*)dst, 16, voff, 0, 0, 0);
+    };
+    // k-tile of walk step i (the walk starts at a rotated tile)
+    auto tile = [&](int i) __attribute__((always_inline)) {
+        int t = i + rot;
+        if (t >= n) t -= n;
+        return kt_begin + t;
+    };
+    // step i's loads into stage i % D; steps past the walk load zeros
+    auto issue = [&](int i) __attribute__((always_inline)) {
+        const bool valid = i < n;
+        const int k0b = tile(valid ? i : 0) * 128;
+        char* st = mine + (i % D) * RR::STAGE;
+#pragma unroll
+        for (int g = 0; g < MT * 2; ++g)
+            group(W, g, valid ? ((g & 1) ? wo : we) : kOutOfRange, (g & 1) ? co : ce, k0b, st + g * 1024);
+#pragma unroll
+        for (int g = 0; g < NT * 2; ++g)
+            group(A, g, valid ? ((g & 1) ? ao : ae) : kOutOfRange, (g & 1) ? co : ce, k0b,
+                  st + MT * 16 * 128 + g * 1024);
+    };
+    const int fr = lane & 15, q = lane >> 4, sw = swz(fr);
+    const float on = want_base ? 1.0f : 0.0f;
+    float bs[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) bs[mt] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) issue(i);
+    for (int t = 0; t < n; ++t) {
+        wait_vmcnt<(D - 2) * RR::PER>();        // step t landed
+        __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): this wave's reads of step t - 1 are done
+        issue(t + D - 1);                      // into step t - 1's stage
+        const char* st = mine + (t % D) * RR::STAGE;
+#pragma unroll
+        for (int ks = 0; ks < M::BK / 32; ++ks) {
+            M::frag_t af[MT], b[NT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                af[mt] = M::load_frag_swz(st + (mt * 16 + fr) * 128, ks, q, sw);
+                bs[mt] = fmaf(on, M::frag_sumsq(af[mt]), bs[mt]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                b[nt] = M::load_frag_swz(st + (MT * 16 + nt * 16 + fr) * 128, ks, q, sw);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) M::mma(acc[mt][nt], af[mt], b[nt]);
+            }
+            int g = 0;
+#pragma unroll
+            for (int b1 = 0; b1 < NT; ++b1)
+#pragma unroll
+                for (int b2 = b1; b2 < NT; ++b2) M::mma(gacc[g++], b[b1], b[b2]);
+        }
+    }
+    wait_vmcnt<0>();   // the empty loads issued past the walk
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        float v = bs[mt];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        bsum[mt] = v;
+    }
+}
+
 // The narrowest register-fed form (r <= 16) is held to three workgroups per
 // CU (168 VGPRs, no spills): tall projections run several rounds of its
 // workgroups, and with the Gram blocks it would otherwise drop to two.
@@ -765,7 +907,12 @@ __global__ __launch_bounds__(WM * WN * 64, (ALIGNED && WN == 1 && NT == 1) ? 3 :
     typedef GramInPass<E, WN, NT, ALIGNED> GIP;
     constexpr int EPI_ALL = EPI + GIP::BYTES;
     constexpr int WIDE_BYTES = TL::DMA_BYTES;
-    constexpr int MAIN = F::WIDE ? WIDE_BYTES : (F::NARROW ? 0 : TL::STAGED_BYTES);
+    // the narrow form with the Gram term in the pass walks K through per-wave
+    // LDS-DMA rings (mainloop_narrow_dma), sized for two workgroups per CU
+    constexpr bool RING = F::NARROW && GIP::value;
+    constexpr int RING_D = NT == 1 ? 3 : 2;
+    constexpr int RING_BYTES = RING ? NarrowRing<MT, NT, WM, RING_D>::BYTES : 0;
+    constexpr int MAIN = F::WIDE ? WIDE_BYTES : (F::NARROW ? RING_BYTES : TL::STAGED_BYTES);
     __shared__ __attribute__((aligned(1024))) char smem[MAIN > EPI_ALL ? MAIN : EPI_ALL];
 
     // Workgroup -> (m-tile, n-tile, k-chunk).  Workgroups are handed to the 8
@@ -809,8 +956,14 @@ __global__ __launch_bounds__(WM * WN * 64, (ALIGNED && WN == 1 && NT == 1) ? 3 :
     else if constexpr (F::NARROW) {
         const int64_t mrow0 = m0 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * MT * 16;
         float bsum[MT];
-        mainloop_w0_narrow<E, MT, NT, GIP::value, GIP::NG, kNarrowDepth>(a.c, mrow0, n0, kt_begin, kt_end, rot,
-                                                           base_dst != nullptr, acc, gacc, bsum);
+        if constexpr (RING) {
+            mainloop_narrow_dma<MT, NT, GIP::NG, RING_D>(a.c, mrow0, n0, kt_begin, kt_end, rot, base_dst != nullptr,
+                                                         smem, acc, gacc, bsum);
+            __syncthreads();   // every wave is done with the ring before the epilogue reuses it
+        } else {
+            mainloop_w0_narrow<E, MT, NT, GIP::value, GIP::NG, kNarrowDepth>(a.c, mrow0, n0, kt_begin, kt_end, rot,
+                                                                             base_dst != nullptr, acc, gacc, bsum);
+        }
         if (base_dst) {
             const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -951,32 +1104,6 @@ __global__ __launch_bounds__(WM * WN * 64, (ALIGNED && WN == 1 && NT == 1) ? 3 :
     }
 }
 
-// One operand as the 128-byte-row DMA sees it; lane l moves slot l % 8 of row
-// l / 8 of an 8-row group (1 KiB per instruction, eight whole lines).  The
-// row and K offsets of an instruction are wave-uniform, so they move the
-// buffer's base address (scalar registers) while the per-lane part stays one
-// fixed VGPR; the buffer is shrunk by the same amount, so rows past the
-// operand still read zeros.
-struct Dma64 {
-    uint32_t base_lo, base_hi;     // address of the workgroup's first row
-    int bytes;                     // bytes from there to the operand's end (clamped to 31 bits)
-    int ld_bytes, kmax_bytes;
-};
-
-__device__ __forceinline__ Dma64 make_dma64(const Operand& o, int64_t row0) {
-    Dma64 d;
-    const int64_t ldb = o.ld * 2;
-    const uint64_t base = reinterpret_cast<uint64_t>(static_cast<const char*>(o.p) + row0 * ldb);
-    int64_t bytes = (o.rows - row0) * ldb;
-    if (bytes < 0) bytes = 0;
-    if (bytes > 0x7ffffff0) bytes = 0x7ffffff0;
-    d.base_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
-    d.base_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
-    d.bytes = __builtin_amdgcn_readfirstlane((int)bytes);
-    d.ld_bytes = __builtin_amdgcn_readfirstlane((int)ldb);
-    d.kmax_bytes = __builtin_amdgcn_readfirstlane((int)(o.kmax * 2));
-    return d;
-}
 
 // ------------------------------------------------------------- W0 pass, whole rows (low rank)
 // bf16, 16-byte aligned operands, r <= 32.  A workgroup owns 16 whole rows
@@ -1002,104 +1129,8 @@ struct W0RowsArgs {
 constexpr int kRowsWaves = 8;
 constexpr int kRowsPerWg = 16;
 
-// The whole-row kernel's K walk.  Each wave moves its own 64-element k-tiles
-// of W0 (the workgroup's 16 rows) and of A (NT * 16 rows, zeros past r) by
-// LDS DMA into a private ring of D stages: whole 128-byte rows, so every
-// request to L2 is one full line (register-fed fragment loads can only ask
-// for 64 bytes of a row at a time, and a CU keeps only so many requests in
-// flight).  The fragments are read from the ring with the 128-byte-row
-// swizzle; per k-tile the MFMAs, base term and Gram blocks are those of the
-// register-fed loop.  A wave waits only for its own loads, so the walk has no
-// barriers.
-template <int NT>
-struct RowsRing {
-    static constexpr int AROWS = NT * 16;
-    static constexpr int D = NT == 1 ? 4 : 3;                       // stages per wave
-    static constexpr int STAGE = (kRowsPerWg + AROWS) * 128;        // bytes per stage
-    static constexpr int PER = (kRowsPerWg + AROWS) / 8;            // DMA instructions per stage
-    static constexpr int BYTES = kRowsWaves * D * STAGE;
-    static_assert((D - 2) * PER < 64, "vmcnt range");
-};
 
-template <int NT, int NG>
-__device__ __forceinline__ void mainloop_rows_dma(const Contraction& c, int64_t m0, int kt_begin, int kt_end,
-                                                  char* ring, f32x4_t (&acc)[1][NT], f32x4_t (&gacc)[NG],
-                                                  float& bsum) {
-    typedef Mma<bf16_t> M;
-    typedef RowsRing<NT> RR;
-    constexpr int D = RR::D;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n = kt_end - kt_begin;
-    bsum = 0.0f;
-    if (n <= 0) return;
-    const Dma64 W = make_dma64(c.left0, m0);
-    const Dma64 A = make_dma64(c.right0, 0);
-    // lane l moves slot l % 8 of row l / 8 of an 8-row group, carrying
-    // logical chunk slot ^ swz(row) = (l % 8) ^ (l / 8) ^ (group parity)
-    const int ce = ((lane & 7) ^ (lane >> 3)) * 16, co = ce ^ 16;
-    const int we = (lane >> 3) * W.ld_bytes + ce, wo = (lane >> 3) * W.ld_bytes + co;
-    const int ae = (lane >> 3) * A.ld_bytes + ce, ao = (lane >> 3) * A.ld_bytes + co;
-    char* mine = ring + wave * D * RR::STAGE;
-    auto group = [&](const Dma64& d, int g, int lane_off, int chunk_b, int k0b, char* dst) __attribute__((always_inline)) {
-        const int kleft = d.kmax_bytes - k0b;
-        const int voff = chunk_b < kleft ? lane_off : kOutOfRange;
-        const int off = g * 8 * d.ld_bytes + k0b;
-        const int left = d.bytes > off ? d.bytes - off : 0;
-        const uint64_t addr = (((uint64_t)d.base_hi << 32) | d.base_lo) + (uint32_t)off;
-        i32x4_t rs;
-        rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
-        rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32));
-        rs[2] = __builtin_amdgcn_readfirstlane(left);
-        rs[3] = 0x00020000;
-        raw_buffer_load_lds(rs, (lds_void_t*)dst, 16, voff, 0, 0, 0);
-    };
-    // step i's loads into stage i % D; steps past the walk load zeros
-    auto issue = [&](int i) __attribute__((always_inline)) {
-        const bool valid = i < n;
-        const int k0b = (kt_begin + (valid ? i : 0)) * 128;
-        char* st = mine + (i % D) * RR::STAGE;
-#pragma unroll
-        for (int g = 0; g < kRowsPerWg / 8; ++g)
-            group(W, g, valid ? ((g & 1) ? wo : we) : kOutOfRange, (g & 1) ? co : ce, k0b, st + g * 1024);
-#pragma unroll
-        for (int g = 0; g < RR::AROWS / 8; ++g)
-            group(A, g, valid ? ((g & 1) ? ao : ae) : kOutOfRange, (g & 1) ? co : ce, k0b,
-                  st + kRowsPerWg * 128 + g * 1024);
-    };
-    const int fr = lane & 15, q = lane >> 4, sw = swz(fr);
-    float bs = 0.0f;
-#pragma unroll
-    for (int i = 0; i < D - 1; ++i) issue(i);
-    for (int t = 0; t < n; ++t) {
-        wait_vmcnt<(D - 2) * RR::PER>();        // step t landed
-        __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): this wave's reads of step t - 1 are done
-        issue(t + D - 1);                      // into step t - 1's stage
-        const char* st = mine + (t % D) * RR::STAGE;
-#pragma unroll
-        for (int ks = 0; ks < M::BK / 32; ++ks) {
-            const M::frag_t af = M::load_frag_swz(st + fr * 128, ks, q, sw);
-            bs += M::frag_sumsq(af);
-            M::frag_t b[NT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                b[nt] = M::load_frag_swz(st + (kRowsPerWg + nt * 16 + fr) * 128, ks, q, sw);
-                M::mma(acc[0][nt], af, b[nt]);
-            }
-            int g = 0;
-#pragma unroll
-            for (int b1 = 0; b1 < NT; ++b1)
-#pragma unroll
-                for (int b2 = b1; b2 < NT; ++b2) M::mma(gacc[g++], b[b1], b[b2]);
-        }
-    }
-    wait_vmcnt<0>();   // the empty loads issued past the walk
-    bs += __shfl_xor(bs, 16);
-    bs += __shfl_xor(bs, 32);
-    bsum = bs;
-}
-
-// RING: the K walk of mainloop_rows_dma (one round of workgroups: its ring
+// RING: the K walk of mainloop_narrow_dma (one round of workgroups: its ring
 // holds the CU's LDS), else the register-fed walk, whose small footprint lets
 // several workgroups share a CU when the rows run to more than one round.
 template <int NT, bool RING>
@@ -1118,7 +1149,8 @@ __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) 
     // the K walk's ring follows the staged B and is reused by the Gs tiles
     // and the reduction once the walk is done
     constexpr int RING_OFF = GS_OFF;
-    constexpr int RING_END = RING ? RING_OFF + RowsRing<NT>::BYTES : 0;
+    typedef NarrowRing<1, NT, kRowsWaves, NT == 1 ? 4 : 3> RR;
+    constexpr int RING_END = RING ? RING_OFF + RR::BYTES : 0;
     constexpr int LDS = RING_END > EPI ? RING_END : EPI;
     __shared__ __attribute__((aligned(1024))) char smem[LDS];
 
@@ -1164,7 +1196,10 @@ __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) 
         }
     }
     if constexpr (RING) {
-        mainloop_rows_dma<NT, GIP::NG>(a.c, m0, kt_begin, kt_end, smem + RING_OFF, acc, gacc, bsum);
+        float bs[1];
+        mainloop_narrow_dma<1, NT, GIP::NG, (NT == 1 ? 4 : 3)>(a.c, m0, 0, kt_begin, kt_end, 0, true,
+                                                                smem + RING_OFF, acc, gacc, bs);
+        bsum = bs[0];
         __syncthreads();   // every wave is done with the ring
     } else {
         float bs[1];
