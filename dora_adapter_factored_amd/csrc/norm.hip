@@ -1110,9 +1110,8 @@ __global__ __launch_bounds__(WM * WN * 64, (ALIGNED && WN == 1 && NT == 1) ? 3 :
 // of W0 and its eight waves split K eight ways (measured: 5-9% faster than
 // four waves, by the loads it keeps in flight per CU): each walks its K range
 // (U, base and Gram blocks of that range, whose Gram term is a sum over K
-// ranges like any other K split), through its own LDS-DMA ring when the rows
-// fit one round of workgroups, else with register-fed fragment loads; then it
-// adds (s/2) B G_w to its U accumulators and takes the row dots with B.  The
+// ranges like any other K split) through its own LDS-DMA ring; then it adds
+// (s/2) B G_w to its U accumulators and takes the row dots with B.  The
 // workgroup adds the waves' base and cross partials in wave order in LDS and
 // writes wnorm and g itself: no partials leave the workgroup and no assembly
 // kernel runs.
@@ -1130,10 +1129,8 @@ constexpr int kRowsWaves = 8;
 constexpr int kRowsPerWg = 16;
 
 
-// RING: the K walk of mainloop_narrow_dma (one round of workgroups: its ring
-// holds the CU's LDS), else the register-fed walk, whose small footprint lets
-// several workgroups share a CU when the rows run to more than one round.
-template <int NT, bool RING>
+// One round of workgroups (rows_form): each holds a CU's LDS for its rings.
+template <int NT>
 __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) {
     typedef bf16_t E;
     typedef Mma<E> M;
@@ -1150,7 +1147,7 @@ __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) 
     // and the reduction once the walk is done
     constexpr int RING_OFF = GS_OFF;
     typedef NarrowRing<1, NT, kRowsWaves, NT == 1 ? 4 : 3> RR;
-    constexpr int RING_END = RING ? RING_OFF + RR::BYTES : 0;
+    constexpr int RING_END = RING_OFF + RR::BYTES;
     constexpr int LDS = RING_END > EPI ? RING_END : EPI;
     __shared__ __attribute__((aligned(1024))) char smem[LDS];
 
@@ -1195,17 +1192,12 @@ __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) 
             raw_buffer_load_lds(rs, (lds_void_t*)(smem + ins * 1024), 16, voff, 0, 0, 0);
         }
     }
-    if constexpr (RING) {
+    {
         float bs[1];
         mainloop_narrow_dma<1, NT, GIP::NG, (NT == 1 ? 4 : 3)>(a.c, m0, 0, kt_begin, kt_end, 0, true,
                                                                 smem + RING_OFF, acc, gacc, bs);
         bsum = bs[0];
         __syncthreads();   // every wave is done with the ring
-    } else {
-        float bs[1];
-        mainloop_w0_narrow<E, 1, NT, true, GIP::NG, kNarrowDepth>(a.c, m0, 0, kt_begin, kt_end, 0, true, acc, gacc,
-                                                                 bs);
-        bsum = bs[0];
     }
 
     // this wave's Gs_w = (s/2) G_w as bf16 [RP][RP], zero past BN
@@ -2139,19 +2131,25 @@ bool gram_in_pass(const NormPlan& p, bool aligned) {
     return GramInPass<E, 1, 1, true>::value && aligned && t.wn == 1 && t.nt <= 2;
 }
 
-// Whether the norm runs as the single whole-row kernel (w0_rows_narrow).
-// Measured on MI355X at r <= 32: up to 2^25 W0 elements (4096 x 8192,
-// 16384 x 2048, ...) it beats the K-split pass plus assembly by 10-25%; at
-// 6144^2 they tie, and from 8192^2 up the K-split pass is faster (its
-// 128-row workgroups keep more bytes in flight than 16-row ones).  Below one
-// 16-row workgroup per CU the K-split pass wins as well: 2048 x 8192 r = 16
-// 17.5 against 19.0 us, 1024 x 16384 r = 16 20.6 against 33.3 us.
+// Whether the norm runs as the single whole-row kernel (w0_rows_narrow):
+// when its 16-row workgroups make exactly one round (4081 <= d_out <= 4096)
+// and W0 has at most 2^25 elements.  Measured on MI355X at r <= 32, both
+// forms walking K through LDS-DMA rings: 4096^2 r = 16 10.7 against 14.8 us
+// for the K-split pass plus assembly, r = 32 12.8 against 17.2 us, 4096 x
+// 8192 r = 16 16.2 against 22.5 us.  With more rows (several rounds, the
+// whole-row kernel then feeding registers directly) the K-split pass is as
+// fast or faster: 16384 x 2048 r = 16 20.5 against 21.1 us, 8192 x 4096
+// r = 24 21.6 against 26.4 us, 6144^2 r = 16 a tie; and so it is below one
+// workgroup per CU (2048 x 8192 r = 16 17.5 against 19.0 us with the
+// register-fed kernels).
 constexpr int64_t kRowsFormMaxElems = int64_t(1) << 25;
-constexpr int64_t kRowsFormMinRows = int64_t(kRowsPerWg) * kNumCU;
+constexpr int64_t kRowsFormMinRows = int64_t(kRowsPerWg) * (kNumCU - 1) + 1;
+constexpr int64_t kRowsFormMaxRows = int64_t(kRowsPerWg) * kNumCU;
 
 template <typename E>
 bool rows_form(const NormPlan& p, bool aligned) {
-    return gram_in_pass<E>(p, aligned) && p.d_out * p.d_in <= kRowsFormMaxElems && p.d_out >= kRowsFormMinRows;
+    return gram_in_pass<E>(p, aligned) && p.d_out * p.d_in <= kRowsFormMaxElems && p.d_out >= kRowsFormMinRows &&
+           p.d_out <= kRowsFormMaxRows;
 }
 
 // Arguments and grids of the three stages of one norm (not base-only).
@@ -2264,18 +2262,10 @@ hipError_t norm_typed(const NormPlan& p, const void* W0, const void* A, const vo
             ra.wnorm = wnorm;
             ra.g = g;
             const unsigned grid = (unsigned)((d_out + kRowsPerWg - 1) / kRowsPerWg);
-            const bool ring = grid <= (unsigned)kNumCU;
-            if (kCfgs[p.cfg].nt == 1) {
-                if (ring)
-                    w0_rows_narrow<1, true><<<grid, kRowsWaves * 64, 0, st>>>(ra);
-                else
-                    w0_rows_narrow<1, false><<<grid, kRowsWaves * 64, 0, st>>>(ra);
-            } else {
-                if (ring)
-                    w0_rows_narrow<2, true><<<grid, kRowsWaves * 64, 0, st>>>(ra);
-                else
-                    w0_rows_narrow<2, false><<<grid, kRowsWaves * 64, 0, st>>>(ra);
-            }
+            if (kCfgs[p.cfg].nt == 1)
+                w0_rows_narrow<1><<<grid, kRowsWaves * 64, 0, st>>>(ra);
+            else
+                w0_rows_narrow<2><<<grid, kRowsWaves * 64, 0, st>>>(ra);
             return hipGetLastError();
         }
     }

@@ -101,14 +101,15 @@ def test_norm_edge_shapes(d_out, d_in, r, dt):
     check_rel(host64(g), ref_g, NORM_RTOL[L.W0.dtype], "g")
 
 
-@pytest.mark.parametrize("d_out,d_in,r", [(4096, 8192, 16), (4111, 2056, 24), (4100, 8200, 16), (8192, 4104, 24),
-                                          (1024, 16384, 16)])
+@pytest.mark.parametrize("d_out,d_in,r", [(4096, 8192, 16), (4090, 2056, 24), (4111, 2056, 24), (4100, 8200, 16),
+                                          (8192, 4104, 24), (1024, 16384, 16)])
 def test_norm_low_rank_forms_at_scale(d_out, d_in, r):
-    # bf16 r <= 32: from 4096 rows up to 2^25 W0 elements (4096 x 8192; 4111 x
-    # 2056 with a ragged last workgroup and a K tail) one whole-row kernel
-    # assembles wnorm and g; above it, and below 4096 rows (1024 x 16384), the
-    # K-split W0 pass (each K-chunk's Gram term formed in the pass) and the
-    # assembly kernel run.  Sampled rows.
+    # bf16 r <= 32: when the 16-row workgroups make one round (4081 to 4096
+    # rows) and W0 has at most 2^25 elements (4096 x 8192; 4090 x 2056 with a
+    # ragged last workgroup and a K tail) one whole-row kernel assembles wnorm
+    # and g; otherwise (4111 rows, beyond 2^25, below 4081 rows) the K-split W0
+    # pass (each K-chunk's Gram term formed in the pass) and the assembly
+    # kernel run.  Sampled rows.
     say(f"[parity] low-rank norm {d_out}x{d_in} r={r}")
     spec = DI.custom_spec(d_out, d_in, r, 1, dtype="bf16", s=1.5, b_std=0.05)
     L = DI.make_layer(spec, 60 + r + d_out % 7, device=DEV, activations=False, gen_device="cuda")
