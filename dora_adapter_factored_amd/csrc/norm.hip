@@ -23,8 +23,9 @@
 //      takes the square root and divides m.
 // At low rank (bf16, r <= 32) the Gram term is a sum over K-chunks of
 // B_i A_c A_c^T B_i^T, so the W0 pass forms each chunk's term from the A
-// fragments it already holds and no Gram kernel runs; up to 2^25 W0 elements
-// a single kernel (w0_rows_narrow) owns whole rows and also does step 3.
+// fragments it already holds and no Gram kernel runs; where 16-row
+// workgroups make exactly one round (and W0 has at most 2^25 elements) a
+// single kernel (w0_rows_narrow) owns whole rows and also does step 3.
 // Every reduction has a fixed order, so results are bitwise reproducible.
 #include "dora_device.h"
 #include "dora_gfx950.h"
