@@ -1466,6 +1466,17 @@ __device__ __forceinline__ void w0_pass_big_seg(const W0PassArgs& a, const int i
         // slower.)
         constexpr int HOLD = 2;
         constexpr int ALL = G::MT * G::NT;
+        // Order of one step's MFMAs and the next step's fragment reads: one
+        // MFMA, then the MT + NT fragment reads, then the other MFMAs, so the
+        // reads' LDS latency runs under the matrix pipe instead of after it.
+        // Measured 3% faster at 28672 x 8192 and 27648 x 5120, r = 384, and
+        // no slower at 8192^2 and 4096^2.
+        auto interleave = []() __attribute__((always_inline)) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, G::MT + G::NT, 0);  // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, ALL - 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        };
         auto main_loop = [&](auto wnc) __attribute__((always_inline)) {
             bf16x8_t a0[G::MT], b0[G::NT], a1[G::MT], b1[G::NT];
             issue(0);
@@ -1476,17 +1487,17 @@ __device__ __forceinline__ void w0_pass_big_seg(const W0PassArgs& a, const int i
             for (int j = 0; j < n - 1; ++j) {
                 const float on = base_on_at(j);
                 mma(a0, b0, 0, ALL);
-                base_sum(wnc, a0, on);
-                __builtin_amdgcn_sched_barrier(0);
                 read(j, 1, a1, b1);
-                mma(a1, b1, 0, ALL);
-                base_sum(wnc, a1, on);
-                __builtin_amdgcn_sched_barrier(0);
-                read(j, 2, a0, b0);
-                mma(a0, b0, 0, ALL);
                 base_sum(wnc, a0, on);
-                __builtin_amdgcn_sched_barrier(0);
+                interleave();
+                mma(a1, b1, 0, ALL);
+                read(j, 2, a0, b0);
+                base_sum(wnc, a1, on);
+                interleave();
+                mma(a0, b0, 0, ALL);
                 read(j, 3, a1, b1);
+                base_sum(wnc, a0, on);
+                interleave();
                 mma(a1, b1, 0, ALL - HOLD);
                 base_sum(wnc, a1, on);
                 __builtin_amdgcn_sched_barrier(0);
