@@ -76,6 +76,7 @@ def merge_bytes(d_out, d_in, r, esz):
 COPY_CALIB_BYTES = 256 << 20
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 NORM_SOURCES = ("dora_adapter_factored_amd/csrc/norm.hip", "dora_adapter_factored_amd/csrc/dora_launch.h",
+                "dora_adapter_factored_amd/csrc/dora_balance.h",
                 "dora_adapter_factored_amd/csrc/dora_device.h", "dora_adapter_factored_amd/csrc/dora_gfx950.h")
 
 

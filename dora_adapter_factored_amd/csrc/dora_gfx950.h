@@ -21,6 +21,12 @@ __device__ void raw_buffer_load_lds(i32x4_t rsrc, lds_void_t* lds, int size, int
 // A per-lane buffer offset that is always out of range: the load reads zeros.
 constexpr int kOutOfRange = (int)0x80000000;
 
+// Cache-policy operand of a buffer load on gfx940-class chips: the NT
+// (non-temporal) bit, for data read exactly once.  Its lines are the first
+// the caches drop, so data that is re-read (the A tile every workgroup of an
+// XCD streams) keeps its place in L2.
+constexpr int kCachePolicyNT = 2;
+
 // Buffer resource word 3 used for raw byte-addressed buffers here.
 constexpr int kRsrcWord3 = 0x00020000;
 

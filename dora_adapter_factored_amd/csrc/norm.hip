@@ -27,6 +27,7 @@
 // workgroups make exactly one round (and W0 has at most 2^25 elements) a
 // single kernel (w0_rows_narrow) owns whole rows and also does step 3.
 // Every reduction has a fixed order, so results are bitwise reproducible.
+#include "dora_balance.h"
 #include "dora_device.h"
 #include "dora_gfx950.h"
 #include "dora_launch.h"
@@ -36,6 +37,12 @@ namespace {
 
 constexpr int kNumCU = 256;
 constexpr int kNumXCD = 8;
+
+// a compile-time int carried by value (selects template paths from lambdas)
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
 
 // ------------------------------------------------------------- MFMA traits
 // One "k-step" contracts 32 elements of K.  In a k-step each lane supplies 8
@@ -688,22 +695,9 @@ __device__ __forceinline__ void mainloop(const Contraction& c, int64_t m0, int64
 }
 
 // ------------------------------------------------------------- W0 pass
-// Balanced K split of the large-tile pass.  Workgroup w of nwg owns units
-// [w U / nwg, (w + 1) U / nwg) of the m-tile-major sequence of (m-tile,
-// k-tile) pairs, U = units = n_mtiles * nkt.  A range is shorter than one
-// m-tile's K, so it covers the tail of one m-tile and the head of the next
-// at most: two segments, each with its own epilogue, whose partials go to
-// slot (w - first workgroup of that m-tile).  nwg = 0: the uniform split.
-struct Balance {
-    int64_t units;
-    int nwg, nkt;
-    // the workgroup whose range holds unit u
-    __host__ __device__ int wg_of(int64_t u) const { return (int)(((u + 1) * nwg + units - 1) / units) - 1; }
-    // partial slots of m-tile mt (workgroups whose ranges meet it)
-    __host__ __device__ int slots(int mt) const {
-        return wg_of((int64_t)(mt + 1) * nkt - 1) - wg_of((int64_t)mt * nkt) + 1;
-    }
-};
+// Balanced K split of the large-tile pass (dora_balance.h): each workgroup
+// walks one or more segments (k-tile ranges of one m-tile), each with its
+// own epilogue and partial slot.  nwg = 0: the uniform split.
 
 struct W0PassArgs {
     Contraction c;
@@ -815,7 +809,9 @@ __device__ __forceinline__ void mainloop_narrow_dma(const Contraction& c, int64_
     const int we = (lane >> 3) * W.ld_bytes + ce, wo = (lane >> 3) * W.ld_bytes + co;
     const int ae = (lane >> 3) * A.ld_bytes + ce, ao = (lane >> 3) * A.ld_bytes + co;
     char* mine = ring + wave * D * RR::STAGE;
-    auto group = [&](const Dma64& d, int g, int lane_off, int chunk_b, int k0b, char* dst) __attribute__((always_inline)) {
+    // aux: the load's cache policy (W0 is read once: non-temporal)
+    auto group = [&](const Dma64& d, int g, int lane_off, int chunk_b, int k0b, char* dst, auto aux)
+        __attribute__((always_inline)) {
         const int kleft = d.kmax_bytes - k0b;
         const int voff = chunk_b < kleft ? lane_off : kOutOfRange;
         const int off = g * 8 * d.ld_bytes + k0b;
@@ -826,7 +822,7 @@ __device__ __forceinline__ void mainloop_narrow_dma(const Contraction& c, int64_
         rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32));
         rs[2] = __builtin_amdgcn_readfirstlane(left);
         rs[3] = 0x00020000;
-        raw_buffer_load_lds(rs, (lds_void_t*)dst, 16, voff, 0, 0, 0);
+        raw_buffer_load_lds(rs, (lds_void_t*)dst, 16, voff, 0, 0, decltype(aux)::value);
     };
     // k-tile of walk step i (the walk starts at a rotated tile)
     auto tile = [&](int i) __attribute__((always_inline)) {
@@ -841,11 +837,12 @@ __device__ __forceinline__ void mainloop_narrow_dma(const Contraction& c, int64_
         char* st = mine + (i % D) * RR::STAGE;
 #pragma unroll
         for (int g = 0; g < MT * 2; ++g)
-            group(W, g, valid ? ((g & 1) ? wo : we) : kOutOfRange, (g & 1) ? co : ce, k0b, st + g * 1024);
+            group(W, g, valid ? ((g & 1) ? wo : we) : kOutOfRange, (g & 1) ? co : ce, k0b, st + g * 1024,
+                  IntC<kCachePolicyNT>{});
 #pragma unroll
         for (int g = 0; g < NT * 2; ++g)
             group(A, g, valid ? ((g & 1) ? ao : ae) : kOutOfRange, (g & 1) ? co : ce, k0b,
-                  st + MT * 16 * 128 + g * 1024);
+                  st + MT * 16 * 128 + g * 1024, IntC<0>{});
     };
     const int fr = lane & 15, q = lane >> 4, sw = swz(fr);
     const float on = want_base ? 1.0f : 0.0f;
@@ -1280,11 +1277,6 @@ __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) 
 // elements of K (whole 128-byte rows, so every DMA request is a full line):
 // W0 | B and A | Gs share a two-stage ring that fills the CU's 160 KB of LDS.
 
-template <int V>
-struct IntC {
-    static constexpr int value = V;
-};
-
 struct Big {
     static constexpr int WG_PER_CU = 1;                 // workgroups resident on one CU
     static constexpr int WM = WG_PER_CU == 2 ? 1 : 2, WN = 4, NW = WM * WN, NTH = NW * 64;
@@ -1324,8 +1316,11 @@ struct Big {
 // all have the wave's parity, so one chunk serves them all); a lane_off of
 // kOutOfRange turns the whole load into zeros.  Chunks past the operand's K
 // extent read zeros.  Row and K offsets fit 31 bits: a workgroup's rows of
-// any operand span less than 2^30 bytes.
-template <int ROWS>
+// any operand span less than 2^30 bytes.  AUX is the loads' cache policy:
+// the left operand (W0, then B) is read once and goes non-temporal, which
+// measured 2-4% faster at 28672 x 8192, 36864 x 8192, 28672 x 16384 and
+// 27648 x 5120, r = 384, and no slower at 8192^2 and 4096^2.
+template <int ROWS, int AUX>
 __device__ __forceinline__ void dma128_tile(const Dma64& d, int lane_off, int chunk_b, int k0b, char* dst,
                                             int wave) {
     constexpr int PER = ROWS / 8 / Big::NW;
@@ -1344,7 +1339,7 @@ __device__ __forceinline__ void dma128_tile(const Dma64& d, int lane_off, int ch
         rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32));
         rs[2] = __builtin_amdgcn_readfirstlane(left);
         rs[3] = 0x00020000;
-        raw_buffer_load_lds(rs, (lds_void_t*)(dst + grp * 1024), 16, voff, 0, 0, 0);
+        raw_buffer_load_lds(rs, (lds_void_t*)(dst + grp * 1024), 16, voff, 0, 0, AUX);
     }
 }
 
@@ -1409,7 +1404,8 @@ __device__ __forceinline__ void w0_pass_big_seg(const W0PassArgs& a, const int i
             d.kmax_bytes = ph0 ? P0.kmax_bytes : P1.kmax_bytes;
             const int lo = valid ? (ph0 ? doff0 : doff1) : kOutOfRange;
             const int k0b = (ph0 ? kt : kt - c.nkt0) * G::ROWB;
-            dma128_tile<decltype(rows)::value>(d, lo, dchunk, k0b, smem + (i % G::STAGES) * G::STAGE + soff, wave);
+            dma128_tile<decltype(rows)::value, decltype(rows)::value == G::BM ? kCachePolicyNT : 0>(
+                d, lo, dchunk, k0b, smem + (i % G::STAGES) * G::STAGE + soff, wave);
         };
         auto issue = [&](int i) __attribute__((always_inline)) {
             issue_op(i, IntC<G::BM>{}, 0, L0, L1);
@@ -1654,18 +1650,14 @@ __device__ __forceinline__ void w0_pass_big_body(const W0PassArgs& a, const int 
                     (int)((int64_t)(kc + 1) * nkt / a.ksplit), smem);
 }
 
-// Balanced K split (Balance): one or two segments per workgroup.
+// Balanced K split (Balance): the workgroup's segments in walk order.
 __device__ __forceinline__ void w0_pass_big_body_balanced(const W0PassArgs& a, const int id, char* smem) {
-    const int nkt = a.c.nkt0 + a.c.nkt1;
-    const Balance& b = a.bal;
-    const int64_t u0 = (int64_t)id * b.units / b.nwg, u1 = (int64_t)(id + 1) * b.units / b.nwg;
-    for (int64_t u = u0; u < u1;) {   // at most twice: a range is shorter than one m-tile's K
-        const int mt = (int)(u / nkt);
-        const int64_t t0 = (int64_t)mt * nkt, e = u1 < t0 + nkt ? u1 : t0 + nkt;
-        if (u > u0) __syncthreads();   // the previous segment's epilogue is done with LDS
-        w0_pass_big_seg(a, id, mt, 0, id - b.wg_of(t0), (int)(u - t0), (int)(e - t0), smem);
-        u = e;
-    }
+    bool first = true;
+    balance_segments(a.bal, id, [&](const BalanceSeg& s) {
+        if (!first) __syncthreads();   // the previous segment's epilogue is done with LDS
+        first = false;
+        w0_pass_big_seg(a, id, s.mt, 0, s.slot, s.kt_begin, s.kt_end, smem);
+    });
 }
 
 // ------------------------------------------------------------- Gram
