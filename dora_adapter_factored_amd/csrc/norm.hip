@@ -349,8 +349,9 @@ __device__ __forceinline__ DmaSrc make_dma_src(const Operand& o, int64_t row0, i
 // dst.  One instruction moves a group of 8 rows (1 KiB): lane l fills slot
 // l % 8 of row l / 8 with the logical chunk the swizzle puts there.  The
 // groups are dealt to waves [W_FIRST, W_FIRST + W_COUNT); other waves issue
-// nothing.  Chunks past the K extent of the operand read zeros.
-template <int ROWS, int W_FIRST, int W_COUNT>
+// nothing.  Chunks past the K extent of the operand read zeros.  AUX is the
+// loads' cache policy (non-temporal for W0 and B, read once).
+template <int ROWS, int W_FIRST, int W_COUNT, int AUX = 0>
 __device__ __forceinline__ void dma_tile(const DmaSrc& d, int k0b, char* dst, int wave, int tile_kbytes) {
     constexpr int GROUPS = ROWS / 8;
     if (wave < W_FIRST || wave >= W_FIRST + W_COUNT) return;
@@ -364,7 +365,7 @@ __device__ __forceinline__ void dma_tile(const DmaSrc& d, int k0b, char* dst, in
             const bool odd = grp & 1;
             int voff = (odd ? d.off_odd : d.off_even) + grp * 8 * d.ld_bytes + k0b;
             if (!full) voff = (odd ? d.chunk_odd : d.chunk_even) < kleft ? voff : kOutOfRange;
-            raw_buffer_load_lds(d.rsrc, (lds_void_t*)(dst + grp * 1024), 16, voff, 0, 0, 0);
+            raw_buffer_load_lds(d.rsrc, (lds_void_t*)(dst + grp * 1024), 16, voff, 0, 0, AUX);
         }
     }
 }
@@ -436,9 +437,9 @@ __device__ __forceinline__ void mainloop_dma(const Contraction& c, int64_t m0, i
         const int kt = tile(i);
         char* dst = lring + stage * TL::LBYTES;
         if (kt < c.nkt0)
-            dma_tile<TL::BM, LW0, LWN>(L0, kt * TKB, dst, wave, TKB);
+            dma_tile<TL::BM, LW0, LWN, kCachePolicyNT>(L0, kt * TKB, dst, wave, TKB);
         else
-            dma_tile<TL::BM, LW0, LWN>(L1, (kt - c.nkt0) * TKB, dst, wave, TKB);
+            dma_tile<TL::BM, LW0, LWN, kCachePolicyNT>(L1, (kt - c.nkt0) * TKB, dst, wave, TKB);
     };
     auto issue_right = [&](int i, int stage) __attribute__((always_inline)) {
         const int kt = tile(i);
@@ -558,7 +559,8 @@ __device__ __forceinline__ FragSrc select_src(bool p, const FragSrc& f, const Fr
 // Load the fragments of NB consecutive 16-row blocks for every k-step of the
 // k-tile starting at element k0: regs[(ks * NB + b) * FL + h].  With live
 // false every offset is out of range: the loads read zeros and move no data.
-template <typename E, int NB>
+// AUX is the loads' cache policy.
+template <typename E, int NB, int AUX = 0>
 __device__ __forceinline__ void load_frags(const FragSrc& f, int64_t k0, u32x4_t* regs, bool live = true) {
     typedef Mma<E> M;
     constexpr int FR = M::BK / 32, FL = M::FL;
@@ -572,7 +574,7 @@ __device__ __forceinline__ void load_frags(const FragSrc& f, int64_t k0, u32x4_t
                 const bool ok = live && kb + f.kq_bytes + h * 16 < f.kmax_bytes;
                 const int voff = ok ? f.lane_off + b * 16 * f.ld_bytes + kb + h * 16 : kOutOfRange;
                 regs[(ks * NB + b) * FL + h] =
-                    __builtin_bit_cast(u32x4_t, raw_buffer_load_b128(f.rsrc, voff, 0, 0));
+                    __builtin_bit_cast(u32x4_t, raw_buffer_load_b128(f.rsrc, voff, 0, AUX));
             }
         }
     }
@@ -1266,7 +1268,7 @@ __global__ __launch_bounds__(kRowsWaves * 64) void w0_rows_narrow(W0RowsArgs a) 
 }
 
 // ------------------------------------------------------------- W0 pass, 256 x 384 tiles
-// Large-tile form of the W0 pass for bf16 operands, used when r > 192.  A
+// Large-tile form of the W0 pass for bf16 operands, used when r > 128.  A
 // workgroup owns 256 rows of W0 and 384 columns of r: every A tile that
 // crosses L2 feeds twice as many MFMAs as with 128-row tiles, which halves
 // the L2 -> CU traffic of A, the larger of the two streams per k-tile.
@@ -2087,11 +2089,19 @@ constexpr TileCfg kCfgs[] = {
     {4, 1, 2, 1},    // narrow, BM 128, BN 16
     {4, 1, 2, 2},    // narrow, BM 128, BN 32
     {4, 1, 2, 4},    // narrow, BM 128, BN 64
+    {1, 4, 8, 1},    // wide,   BM 128, BN 64
     {1, 4, 8, 2},    // wide,   BM 128, BN 128
     {1, 4, 8, 3},    // wide,   BM 128, BN 192
     {1, 4, 8, 6},    // wide,   BM 128, BN 384
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
+// bf16 at 32 < r <= 64 runs the wide tile of the same BN, whose four waves
+// share one A tile in LDS, in place of the narrow one, where each wave loads
+// its own copy.  Measured on MI355X (norm per call): 8192 x 8192 r = 40 60.4
+// -> 47.9 us, 8192 x 4096 r = 64 46.2 -> 34.4, 4096 x 8192 49.5 -> 37.9,
+// 6144 x 4096 45.5 -> 33.4, 16384 x 4096 r = 48 64.2 -> 54.1, 4096^2 r = 64
+// 31.6 -> 30.1, 2048 x 8192 35.3 -> 33.6; 4096^2 r = 48 29.4 against 30.0.
+constexpr int kNarrow64Cfg = 2;
 
 template <typename E, int CFG, bool AL>
 hipError_t launch_w0_cfg(const W0PassArgs& a, int grid, hipStream_t st) {
@@ -2108,8 +2118,9 @@ hipError_t launch_w0(int cfg, const W0PassArgs& a, int grid, hipStream_t st) {
         case 2: return launch_w0_cfg<E, 2, AL>(a, grid, st);
         case 3: return launch_w0_cfg<E, 3, AL>(a, grid, st);
         case 4: return launch_w0_cfg<E, 4, AL>(a, grid, st);
+        case 5: return launch_w0_cfg<E, 5, AL>(a, grid, st);
         default:
-            if constexpr (sizeof(E) == 2) return launch_w0_cfg<E, 5, AL>(a, grid, st);
+            if constexpr (sizeof(E) == 2) return launch_w0_cfg<E, 6, AL>(a, grid, st);
             return hipErrorInvalidValue;
     }
 }
@@ -2343,7 +2354,13 @@ NormPlan plan_norm_impl(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool 
         p.bytes = align_up((size_t)d_out * 4, 256);
         return p;
     }
-    p.big = allow_big && dtype == kBF16 && r > 192;
+    // 256 x 384 tiles from r = 129: above 128 they beat the 128 x 192 tiles
+    // even with a third or more of the tile's columns zero (measured on
+    // MI355X: 8192^2 r = 160 84.1 -> 69.3 us, r = 192 84.0 -> 70.9 us, 5120^2
+    // r = 192 63.3 -> 42.9 us, 4096^2 r = 192 37.4 -> 36.3 us); at r <= 128
+    // the zero columns' MFMAs cost more than the tiles save (8192^2 r = 128
+    // 55.3 against 66.1 us, 28672 x 8192 r = 128 160.1 against 188.9 us).
+    p.big = allow_big && dtype == kBF16 && r > 128;
     int ks = 1;
     if (p.big) {
         p.cfg = -1;
@@ -2380,9 +2397,10 @@ NormPlan plan_norm_impl(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool 
     } else {
         // widest configuration this dtype instantiates (fp32 fragments double
         // the register footprint, so fp32 stops at BN = 192)
-        const int max_cfg = dtype == kF32 ? 4 : kNumCfgs - 1;
+        const int max_cfg = dtype == kF32 ? 5 : kNumCfgs - 1;
         int cfg = 0;
         while (cfg < max_cfg && kCfgs[cfg].wn * kCfgs[cfg].nt * 16 < r) ++cfg;
+        if (cfg == kNarrow64Cfg && dtype == kBF16) cfg = kNarrow64Cfg + 1;
         p.cfg = cfg;
         p.bm = kCfgs[cfg].wm * kCfgs[cfg].mt * 16;
         p.bn = kCfgs[cfg].wn * kCfgs[cfg].nt * 16;

@@ -157,7 +157,7 @@ int dora_factored_norm_group_workspace_size(int n, const int64_t* d_out, const i
  * norms depend on its weights alone), in one call.  Each member computes
  * exactly what dora_factored_norm computes for it, with bitwise the same
  * result; when every member is bf16 with 16-byte aligned operands and
- * r > 192, each stage of the method ([ScalingDoRA] §2: Gram, the W0 pass with
+ * r > 128, each stage of the method ([ScalingDoRA] §2: Gram, the W0 pass with
  * its row epilogue, assembly) runs as one launch for the whole group, so
  * small projections (k/v rows) share the chip instead of paying launch and
  * tail costs one by one, and long ones fill each other's last round.

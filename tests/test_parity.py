@@ -84,6 +84,8 @@ EDGE_SHAPES = [
     (64, 48, 8, "f32"), (64, 48, 8, "bf16"),
     (300, 1000, 384, "bf16"),    # 256-row tiles: ragged rows, K tail inside a 32-wide tile
     (520, 8200, 200, "bf16"),    # 256-row tiles with r < 384 (ragged slice of r)
+    (1000, 4104, 136, "bf16"),   # 256-row tiles from r = 129 (most of the 384 columns zero)
+    (300, 2056, 128, "bf16"),    # the largest r of the 128-row tiles
     # r <= 32 bf16: the W0 pass forms each K-chunk's Gram term itself
     (520, 8200, 24, "bf16"),     # eight ragged K-chunks, r below the 32-wide tile
     (300, 4104, 8, "bf16"),      # rank 8 in a 16-wide tile, ragged rows

@@ -62,13 +62,15 @@ def test_group_of_one_layer_of_the_sweep():
 
 
 GROUP_CASES = [
-    # (members as (d_out, d_in), r, dtype): grouped kernels when bf16, aligned, r > 192
+    # (members as (d_out, d_in), r, dtype): grouped kernels when bf16, aligned, r > 128
     (((300, 4096), (1000, 4096), (520, 4096)), 256, "bf16"),
     (((64, 1024), (8, 1024), (1, 1024)), 384, "bf16"),
     (((257, 2048), (129, 2048)), 200, "bf16"),
     (((300, 1000), (520, 4096), (64, 2048), (96, 8200)), 256, "bf16"),   # different d_in
     (((64, 48), (40, 100)), 8, "f32"),             # member by member
-    (((500, 640), (33, 640)), 16, "bf16"),         # r <= 192: member by member
+    (((500, 640), (33, 640)), 16, "bf16"),         # r <= 128: member by member
+    (((300, 2056), (40, 2056)), 136, "bf16"),      # grouped from r = 129
+    (((200, 1024), (64, 1024)), 128, "bf16"),      # r = 128: member by member
 ]
 
 
