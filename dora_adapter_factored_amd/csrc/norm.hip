@@ -383,10 +383,17 @@ __device__ __forceinline__ void dma_tile(const DmaSrc& d, int k0b, char* dst, in
 // every row and pile onto a few memory channels; rotating the start spreads
 // them.  The base term is summed from the left fragments the MFMAs consume;
 // the WN waves sharing a row block split its 16-row blocks between them.
-template <typename E, int WM, int WN, int MT, int NT, bool ROLES>
+// With GRAM (bf16, one n-tile covering r), the right fragments also feed this
+// K range's Gram blocks G_c = A_c A_c^T: wave wn accumulates block (b1, b2)
+// of 16-row blocks of the tile's A rows, b1 its own blocks wn NT + j, b2 >=
+// b1 any block, in gacc[j * WN * NT + b2]; the waves together cover the
+// upper half once.
+template <typename E, int WM, int WN, int MT, int NT, bool ROLES, bool GRAM = false, int NG = 1>
 __device__ __forceinline__ void mainloop_dma(const Contraction& c, int64_t m0, int64_t n0, int kt_begin,
                                              int kt_end, int rot, float* base_dst, int64_t d_out,
-                                             f32x4_t (&acc)[MT][NT], char* smem) {
+                                             f32x4_t (&acc)[MT][NT], char* smem, f32x4_t (&gacc)[NG]) {
+    constexpr int NBLK = WN * NT;   // 16-row blocks of the right tile
+    static_assert(!GRAM || NG == NT * NBLK, "one Gram accumulator per (own block, any block)");
     typedef Tile<E, WM, WN, MT, NT> TL;
     typedef Mma<E> M;
     static_assert(TL::NW % 2 == 0, "DMA lane offsets assume an even wave count");
@@ -427,6 +434,7 @@ __device__ __forceinline__ void mainloop_dma(const Contraction& c, int64_t m0, i
     for (int mt = 0; mt < MT; ++mt) bs[mt] = 0.0f;
 
     const int n = kt_end - kt_begin;
+    bool base_tile = false;   // the tile being computed is a W0 | A one
     // k-tile visited at step i (the walk starts at a rotated tile)
     auto tile = [&](int i) __attribute__((always_inline)) {
         int t = i + rot;
@@ -466,6 +474,19 @@ __device__ __forceinline__ void mainloop_dma(const Contraction& c, int64_t m0, i
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) M::mma(acc[mt][nt], a[mt], b[nt]);
+            if constexpr (GRAM) {
+                // base is set on the W0 | A k-tiles only, the ones G_c sums over
+                if (base_tile) {
+#pragma unroll
+                    for (int b2 = 0; b2 < NBLK; ++b2) {
+                        const int row = b2 * 16 + (lane & 15);
+                        const typename M::frag_t f = M::load_frag_swz(Rt + row * 128, ks, q, swz(row));
+#pragma unroll
+                        for (int j = 0; j < NT; ++j)
+                            if (b2 >= wn * NT + j) M::mma(gacc[j * NBLK + b2], b[j], f);
+                    }
+                }
+            }
         }
     };
 
@@ -490,7 +511,8 @@ __device__ __forceinline__ void mainloop_dma(const Contraction& c, int64_t m0, i
             const int ls_next2 = ls == 0 ? 2 : ls - 1;   // (ls + 2) % 3
             if (j + 1 < n) issue_right(j + 1, rs_next);
             if (j + 2 < n) issue_left(j + 2, ls_next2);
-            compute(lring + ls * TL::LBYTES, rring + rs * TL::RBYTES, base_dst != nullptr && tile(j) < c.nkt0);
+            base_tile = tile(j) < c.nkt0;
+            compute(lring + ls * TL::LBYTES, rring + rs * TL::RBYTES, base_dst != nullptr && base_tile);
             ls = ls == 2 ? 0 : ls + 1;
             rs = rs_next;
         }
@@ -690,8 +712,10 @@ template <typename E, int WM, int WN, int MT, int NT, bool ALIGNED>
 __device__ __forceinline__ void mainloop(const Contraction& c, int64_t m0, int64_t n0, int kt_begin, int kt_end,
                                          int rot, float* base_dst, int64_t d_out, f32x4_t (&acc)[MT][NT],
                                          char* smem) {
-    if constexpr (ALIGNED)
-        mainloop_dma<E, WM, WN, MT, NT, false>(c, m0, n0, kt_begin, kt_end, rot, base_dst, d_out, acc, smem);
+    if constexpr (ALIGNED) {
+        f32x4_t none[1];
+        mainloop_dma<E, WM, WN, MT, NT, false>(c, m0, n0, kt_begin, kt_end, rot, base_dst, d_out, acc, smem, none);
+    }
     else
         mainloop_staged<E, WM, WN, MT, NT>(c, m0, n0, kt_begin, kt_end, base_dst, d_out, acc, smem);
 }
@@ -728,18 +752,30 @@ struct W0Form {
 // contention in the memory system.
 constexpr int kNarrowDepth = 2;
 
-// Narrow bf16 tiles with r <= 32 form the Gram term inside the W0 pass.  The
-// norm's Gram term is a sum over K of per-chunk terms,
+// bf16 tiles whose one n-tile covers r <= 32 (narrow) or r <= 64 (wide)
+// form the Gram term inside the W0 pass.  The norm's Gram term is a sum over
+// K of per-chunk terms,
 //   B_i G B_i^T = sum_c B_i (A_c A_c^T) B_i^T,
 // so each K-chunk workgroup builds G_c from the A fragments it already
 // holds and adds (s/2) B G_c to its U accumulators before the row dot with
 // B, exactly as the extended contraction adds B Gs with the whole Gram.  No
-// Gram kernels run and the contraction has no Gs k-tiles.
+// Gram kernels run and the contraction has no Gs k-tiles.  A narrow wave
+// holds all of the tile's A rows and builds every upper 16 x 16 block of
+// G_c; wide waves split the blocks (mainloop_dma).  Every m-tile's
+// workgroups build the same G_c, so the in-pass Gram grows with d_out while
+// the Gram kernels do not: measured on MI355X, the wide 128-column tile lost
+// with it (8192^2 r = 128 54.8 -> 61.7 us, 28672 x 8192 153.0 -> 194.8 us;
+// 4096^2 33.7 -> 32.6 us), the 64-column one won everywhere (4096^2 r = 64
+// 30.2 -> 25.3 us, r = 40 30.0 -> 25.0, 8192 x 4096 r = 64 34.5 -> 29.7,
+// 8192^2 48.2 -> 44.6, 1024 x 8192 32.6 -> 25.6).
 template <typename E, int WN, int NT, bool ALIGNED>
 struct GramInPass {
-    static constexpr bool value = ALIGNED && WN == 1 && NT <= 2 && sizeof(E) == 2;
-    static constexpr int NG = value ? NT * (NT + 1) / 2 : 1;   // upper 16 x 16 blocks of G_c
-    static constexpr int RP = 32;                               // K of the B Gs product, zero-padded
+    static constexpr bool NARROW = ALIGNED && WN == 1 && NT <= 2 && sizeof(E) == 2;
+    static constexpr bool WIDE = ALIGNED && WN == 4 && NT == 1 && sizeof(E) == 2;
+    static constexpr bool value = NARROW || WIDE;
+    static constexpr int NBLK = WN * NT;                        // 16-row blocks of A in the tile
+    static constexpr int NG = NARROW ? NT * (NT + 1) / 2 : (WIDE ? NT * NBLK : 1);
+    static constexpr int RP = WIDE ? NBLK * 16 : 32;            // K of the B Gs product (narrow: zero-padded)
     static constexpr int PITCH = RP * 2 + 16;                   // Gs tile row bytes in LDS
     static constexpr int BYTES = value ? RP * PITCH : 0;
 };
@@ -952,7 +988,8 @@ __global__ __launch_bounds__(WM * WN * 64, (ALIGNED && WN == 1 && NT == 1) ? 3 :
     const int nk = kt_end - kt_begin;
     const int rot = nk > 0 ? (int)(((unsigned)id * 7u + ((unsigned)id >> 3) * 3u) % (unsigned)nk) : 0;
     if constexpr (F::WIDE)
-        mainloop_dma<E, WM, WN, MT, NT, false>(a.c, m0, n0, kt_begin, kt_end, rot, base_dst, a.d_out, acc, smem);
+        mainloop_dma<E, WM, WN, MT, NT, false, GIP::WIDE, GIP::NG>(a.c, m0, n0, kt_begin, kt_end, rot, base_dst,
+                                                                   a.d_out, acc, smem, gacc);
     else if constexpr (F::NARROW) {
         const int64_t mrow0 = m0 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * MT * 16;
         float bsum[MT];
@@ -1010,7 +1047,26 @@ __global__ __launch_bounds__(WM * WN * 64, (ALIGNED && WN == 1 && NT == 1) ? 3 :
                 raw_buffer_load_lds(rs, (lds_void_t*)(smem + ins * 1024), 16, voff, 0, 0, 0);
             }
         }
-        if constexpr (GIP::value) {
+        if constexpr (GIP::WIDE) {
+            // each wave stores its blocks of Gs_c = (s/2) G_c as bf16 [RP][RP]
+            // and their mirrors; the blocks cover all of it (RP = BN)
+            char* gs = smem + B_BYTES + RED_BYTES;
+#pragma unroll
+            for (int jb = 0; jb < NT; ++jb) {
+                const int b1 = wn * NT + jb;
+#pragma unroll
+                for (int b2 = 0; b2 < GIP::NBLK; ++b2) {
+                    if (b2 < b1) continue;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int i = b1 * 16 + 4 * (lane >> 4) + j, k = b2 * 16 + (lane & 15);
+                        const E v = Cvt<E>::from_f(a.half_s * gacc[jb * GIP::NBLK + b2][j]);
+                        *reinterpret_cast<E*>(gs + i * GIP::PITCH + k * 2) = v;
+                        if (b1 != b2) *reinterpret_cast<E*>(gs + k * GIP::PITCH + i * 2) = v;
+                    }
+                }
+            }
+        } else if constexpr (GIP::value) {
             // wave 0 stores Gs_c = (s/2) G_c as bf16 [RP][RP] (zero past BN)
             // from its accumulators (every wave holds the same G_c)
             char* gs = smem + B_BYTES + RED_BYTES;
@@ -1035,21 +1091,26 @@ __global__ __launch_bounds__(WM * WN * 64, (ALIGNED && WN == 1 && NT == 1) ? 3 :
         __syncthreads();
         if constexpr (GIP::value) {
             // U += B Gs_c: left fragments are this wave's rows of the staged B
-            // (K = columns of r, zero at and past BN), right fragments rows of Gs_c
+            // (K = columns of r, zero at and past BN), right fragments the
+            // rows of Gs_c of this wave's columns
             const char* gs = smem + B_BYTES + RED_BYTES;
             typedef Mma<E> M;
-            const int kk = 8 * (lane >> 4);
-            typename M::frag_t gf[NT];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                gf[nt] = *reinterpret_cast<const typename M::frag_t*>(gs + (nt * 16 + (lane & 15)) * GIP::PITCH + kk * 2);
+            for (int ks = 0; ks < GIP::RP / 32; ++ks) {
+                const int kk = 32 * ks + 8 * (lane >> 4);
+                typename M::frag_t gf[NT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int row = wm * MT * 16 + mt * 16 + (lane & 15);
-                typename M::frag_t bf{};
-                if (kk < TL::BN) bf = *reinterpret_cast<const typename M::frag_t*>(smem + row * B_PITCH + kk * 2);
+                for (int nt = 0; nt < NT; ++nt)
+                    gf[nt] = *reinterpret_cast<const typename M::frag_t*>(
+                        gs + ((wn * NT + nt) * 16 + (lane & 15)) * GIP::PITCH + kk * 2);
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) M::mma(acc[mt][nt], bf, gf[nt]);
+                for (int mt = 0; mt < MT; ++mt) {
+                    const int row = wm * MT * 16 + mt * 16 + (lane & 15);
+                    typename M::frag_t bf{};
+                    if (kk < TL::BN) bf = *reinterpret_cast<const typename M::frag_t*>(smem + row * B_PITCH + kk * 2);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) M::mma(acc[mt][nt], bf, gf[nt]);
+                }
             }
         }
 #pragma unroll
@@ -2143,7 +2204,7 @@ template <typename E>
 bool gram_in_pass(const NormPlan& p, bool aligned) {
     if (p.big || p.cfg < 0) return false;
     const TileCfg t = kCfgs[p.cfg];
-    return GramInPass<E, 1, 1, true>::value && aligned && t.wn == 1 && t.nt <= 2;
+    return sizeof(E) == 2 && aligned && ((t.wn == 1 && t.nt <= 2) || (t.wn == 4 && t.nt == 1));
 }
 
 // Whether the norm runs as the single whole-row kernel (w0_rows_narrow):
@@ -2163,7 +2224,8 @@ constexpr int64_t kRowsFormMaxRows = int64_t(kRowsPerWg) * kNumCU;
 
 template <typename E>
 bool rows_form(const NormPlan& p, bool aligned) {
-    return gram_in_pass<E>(p, aligned) && p.d_out * p.d_in <= kRowsFormMaxElems && p.d_out >= kRowsFormMinRows &&
+    return gram_in_pass<E>(p, aligned) && kCfgs[p.cfg].wn == 1 && p.d_out * p.d_in <= kRowsFormMaxElems &&
+           p.d_out >= kRowsFormMinRows &&
            p.d_out <= kRowsFormMaxRows;
 }
 
