@@ -89,6 +89,11 @@ EDGE_SHAPES = [
     # r <= 32 bf16: the W0 pass forms each K-chunk's Gram term itself
     (520, 8200, 24, "bf16"),     # eight ragged K-chunks, r below the 32-wide tile
     (300, 4104, 8, "bf16"),      # rank 8 in a 16-wide tile, ragged rows
+    # 32 < r <= 64 bf16: the wide 64-column tile, Gram blocks split over its waves
+    (300, 4104, 48, "bf16"),     # ragged rows and K-chunks, three of four A blocks live
+    (1000, 8200, 64, "bf16"),    # every A block live, many K-chunks
+    (4096, 1000, 33, "bf16"),    # one live column in the last A block
+    (77, 64, 40, "bf16"),        # a single k-tile
 ]
 
 
