@@ -752,8 +752,8 @@ struct W0Form {
 // contention in the memory system.
 constexpr int kNarrowDepth = 2;
 
-// bf16 tiles whose one n-tile covers r <= 32 (narrow) or r <= 64 (wide)
-// form the Gram term inside the W0 pass.  The norm's Gram term is a sum over
+// bf16 tiles whose one n-tile covers r <= 64 (narrow, and the wide 64-column
+// tile) form the Gram term inside the W0 pass.  The norm's Gram term is a sum over
 // K of per-chunk terms,
 //   B_i G B_i^T = sum_c B_i (A_c A_c^T) B_i^T,
 // so each K-chunk workgroup builds G_c from the A fragments it already
@@ -770,12 +770,12 @@ constexpr int kNarrowDepth = 2;
 // 8192^2 48.2 -> 44.6, 1024 x 8192 32.6 -> 25.6).
 template <typename E, int WN, int NT, bool ALIGNED>
 struct GramInPass {
-    static constexpr bool NARROW = ALIGNED && WN == 1 && NT <= 2 && sizeof(E) == 2;
+    static constexpr bool NARROW = ALIGNED && WN == 1 && NT <= 4 && sizeof(E) == 2;
     static constexpr bool WIDE = ALIGNED && WN == 4 && NT == 1 && sizeof(E) == 2;
     static constexpr bool value = NARROW || WIDE;
     static constexpr int NBLK = WN * NT;                        // 16-row blocks of A in the tile
     static constexpr int NG = NARROW ? NT * (NT + 1) / 2 : (WIDE ? NT * NBLK : 1);
-    static constexpr int RP = WIDE ? NBLK * 16 : 32;            // K of the B Gs product (narrow: zero-padded)
+    static constexpr int RP = WIDE ? NBLK * 16 : (NT <= 2 ? 32 : 64);   // K of the B Gs product (narrow: zero-padded)
     static constexpr int PITCH = RP * 2 + 16;                   // Gs tile row bytes in LDS
     static constexpr int BYTES = value ? RP * PITCH : 0;
 };
@@ -944,7 +944,8 @@ __global__ __launch_bounds__(WM * WN * 64, (ALIGNED && WN == 1 && NT == 1) ? 3 :
     constexpr int EPI_ALL = EPI + GIP::BYTES;
     constexpr int WIDE_BYTES = TL::DMA_BYTES;
     // the narrow form with the Gram term in the pass walks K through per-wave
-    // LDS-DMA rings (mainloop_narrow_dma), sized for two workgroups per CU
+    // LDS-DMA rings (mainloop_narrow_dma): two workgroups per CU at r <= 32,
+    // one at r <= 64
     constexpr bool RING = F::NARROW && GIP::value;
     constexpr int RING_D = NT == 1 ? 3 : 2;
     constexpr int RING_BYTES = RING ? NarrowRing<MT, NT, WM, RING_D>::BYTES : 0;
@@ -2156,12 +2157,16 @@ constexpr TileCfg kCfgs[] = {
     {1, 4, 8, 6},    // wide,   BM 128, BN 384
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
-// bf16 at 32 < r <= 64 runs the wide tile of the same BN, whose four waves
-// share one A tile in LDS, in place of the narrow one, where each wave loads
-// its own copy.  Measured on MI355X (norm per call): 8192 x 8192 r = 40 60.4
-// -> 47.9 us, 8192 x 4096 r = 64 46.2 -> 34.4, 4096 x 8192 49.5 -> 37.9,
-// 6144 x 4096 45.5 -> 33.4, 16384 x 4096 r = 48 64.2 -> 54.1, 4096^2 r = 64
-// 31.6 -> 30.1, 2048 x 8192 35.3 -> 33.6; 4096^2 r = 48 29.4 against 30.0.
+// bf16 at 32 < r <= 64: the narrow tile walks K through per-wave LDS-DMA
+// rings (96 KB per workgroup, one per CU), each wave with its own copy of
+// the A tile; where its workgroups take more than one round, the wide tile
+// of the same BN, whose four waves share one A tile in LDS, runs instead.
+// Measured on MI355X (norm per call, both forming the Gram term in the
+// pass): one round, narrow against wide, 4096^2 r = 64 19.3 against 25.6 us,
+// r = 48 19.2 against 25.4, 1024 x 8192 r = 64 19.8 against 26.0; two or
+// more rounds, wide against narrow, 8192^2 r = 64 45.1 against 50.1, r = 40
+// 44.7 against 48.8, 8192 x 4096 30.1 against 32.8, 16384 x 4096 r = 48 52.6
+// against 58.9, 28672 x 8192 r = 64 143.1 against 156.8.
 constexpr int kNarrow64Cfg = 2;
 
 template <typename E, int CFG, bool AL>
@@ -2204,7 +2209,7 @@ template <typename E>
 bool gram_in_pass(const NormPlan& p, bool aligned) {
     if (p.big || p.cfg < 0) return false;
     const TileCfg t = kCfgs[p.cfg];
-    return sizeof(E) == 2 && aligned && ((t.wn == 1 && t.nt <= 2) || (t.wn == 4 && t.nt == 1));
+    return sizeof(E) == 2 && aligned && ((t.wn == 1 && t.nt <= 4) || (t.wn == 4 && t.nt == 1));
 }
 
 // Whether the norm runs as the single whole-row kernel (w0_rows_narrow):
@@ -2224,7 +2229,8 @@ constexpr int64_t kRowsFormMaxRows = int64_t(kRowsPerWg) * kNumCU;
 
 template <typename E>
 bool rows_form(const NormPlan& p, bool aligned) {
-    return gram_in_pass<E>(p, aligned) && kCfgs[p.cfg].wn == 1 && p.d_out * p.d_in <= kRowsFormMaxElems &&
+    return gram_in_pass<E>(p, aligned) && kCfgs[p.cfg].wn == 1 && kCfgs[p.cfg].nt <= 2 &&
+           p.d_out * p.d_in <= kRowsFormMaxElems &&
            p.d_out >= kRowsFormMinRows &&
            p.d_out <= kRowsFormMaxRows;
 }
@@ -2462,23 +2468,28 @@ NormPlan plan_norm_impl(int64_t d_out, int64_t d_in, int64_t r, int dtype, bool 
         const int max_cfg = dtype == kF32 ? 5 : kNumCfgs - 1;
         int cfg = 0;
         while (cfg < max_cfg && kCfgs[cfg].wn * kCfgs[cfg].nt * 16 < r) ++cfg;
-        if (cfg == kNarrow64Cfg && dtype == kBF16) cfg = kNarrow64Cfg + 1;
-        p.cfg = cfg;
-        p.bm = kCfgs[cfg].wm * kCfgs[cfg].mt * 16;
-        p.bn = kCfgs[cfg].wn * kCfgs[cfg].nt * 16;
-        p.bk = gram_bk;
-        p.n_mtiles = (int)((d_out + p.bm - 1) / p.bm);
-        p.n_ntiles = (int)((r + p.bn - 1) / p.bn);
-        p.nkt_w0 = (int)((d_in + p.bk - 1) / p.bk);
-        p.nkt_g = (int)((r + p.bk - 1) / p.bk);
-        const int nkt = p.nkt_w0 + p.nkt_g;
-        // k-split: W0 is cut into ks K-stripes per m-tile.  Workgroup ids
-        // place stripe c on XCD c % 8, and streaming W0 measures near the HBM
-        // roofline when every XCD owns its own stripe (ks a multiple of 8) but
-        // ~40% lower with 4 stripes; beyond that, split further only to give
-        // >= 2 workgroups per CU.  Every stripe keeps >= 8 k-tiles.
-        while (ks < kNumXCD && nkt / (2 * ks) >= 8) ks *= 2;
-        while (ks < 64 && (int64_t)p.n_mtiles * p.n_ntiles * ks < 2 * kNumCU && nkt / (2 * ks) >= 8) ks *= 2;
+        auto tiles_for = [&](int c) {
+            p.cfg = c;
+            p.bm = kCfgs[c].wm * kCfgs[c].mt * 16;
+            p.bn = kCfgs[c].wn * kCfgs[c].nt * 16;
+            p.bk = gram_bk;
+            p.n_mtiles = (int)((d_out + p.bm - 1) / p.bm);
+            p.n_ntiles = (int)((r + p.bn - 1) / p.bn);
+            p.nkt_w0 = (int)((d_in + p.bk - 1) / p.bk);
+            p.nkt_g = (int)((r + p.bk - 1) / p.bk);
+            const int nkt = p.nkt_w0 + p.nkt_g;
+            // k-split: W0 is cut into ks K-stripes per m-tile.  Workgroup ids
+            // place stripe c on XCD c % 8, and streaming W0 measures near the
+            // HBM roofline when every XCD owns its own stripe (ks a multiple
+            // of 8) but ~40% lower with 4 stripes; beyond that, split further
+            // only to give >= 2 workgroups per CU.  Every stripe keeps >= 8
+            // k-tiles.
+            ks = 1;
+            while (ks < kNumXCD && nkt / (2 * ks) >= 8) ks *= 2;
+            while (ks < 64 && (int64_t)p.n_mtiles * p.n_ntiles * ks < 2 * kNumCU && nkt / (2 * ks) >= 8) ks *= 2;
+        };
+        tiles_for(cfg);
+        if (cfg == kNarrow64Cfg && dtype == kBF16 && (int64_t)p.n_mtiles * ks > kNumCU) tiles_for(cfg + 1);
     }
     p.ksplit = ks;
     // Gram
