@@ -128,6 +128,30 @@ def test_norm_low_rank_forms_at_scale(d_out, d_in, r):
     check_rel(host64(g)[rows], ref_g, NORM_RTOL[L.W0.dtype], "g")
 
 
+@pytest.mark.parametrize("d_out,d_in,r", [(8000, 2056, 384), (7200, 4096, 136), (8192, 1792, 256),
+                                          (7169, 3000, 200)])
+def test_norm_eight_chunk_shapes(d_out, d_in, r):
+    # bf16 r > 128 with 29 to 32 m-tiles of 256 rows: the large-tile pass in
+    # eight K-chunks, chunk 7 ending in the B | Gs k-tiles.  Ragged last
+    # m-tiles (8000, 7200, 7169 rows), K tails (2056, 3000) and the fewest
+    # k-tiles per chunk (1792: 4 or 5 of 34); sampled rows against the
+    # oracle, repeated calls bitwise equal, and a group of one member
+    # bitwise equal too
+    say(f"[parity] eight-chunk norm {d_out}x{d_in} r={r}")
+    spec = DI.custom_spec(d_out, d_in, r, 1, dtype="bf16", s=1.5, b_std=0.05)
+    L = DI.make_layer(spec, 90 + r + d_out % 11, device=DEV, activations=False, gen_device="cuda")
+    wn, g = gpu_norm(L)
+    rows = sample_rows(d_out, 256, seed=r + 1)
+    ref_wn, ref_g = oracle_norm(L, rows)
+    check_rel(host64(wn)[rows], ref_wn, NORM_RTOL[L.W0.dtype], "wnorm")
+    check_rel(host64(g)[rows], ref_g, NORM_RTOL[L.W0.dtype], "g")
+    wn2, g2 = gpu_norm(L)
+    (wn3, g3), = D.factored_norm_group([(L.W0, L.A, L.B, L.spec.s, L.m)])
+    torch.cuda.synchronize()
+    assert torch.equal(wn, wn2) and torch.equal(g, g2)
+    assert torch.equal(wn, wn3) and torch.equal(g, g3)
+
+
 def test_norm_unaligned_operands_take_the_fallback_plan():
     # a W0 that is not 16-byte aligned cannot use the LDS-DMA tiles; the call
     # runs the register-staged plan inside the same workspace size
@@ -576,7 +600,7 @@ def test_sweep_shapes_compose(proj):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("d_out,d_in,r", [(1024, 2048, 384), (2048, 4096, 16)])
+@pytest.mark.parametrize("d_out,d_in,r", [(1024, 2048, 384), (2048, 4096, 16), (8000, 2048, 384)])
 def test_graph_capture_replays_match_eager(d_out, d_in, r):
     # norm, compose forward and backward captured in one HIP graph (the
     # library records no memsets): every replay, with eager work and a

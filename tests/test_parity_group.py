@@ -71,6 +71,8 @@ GROUP_CASES = [
     (((500, 640), (33, 640)), 16, "bf16"),         # r <= 128: member by member
     (((300, 2056), (40, 2056)), 136, "bf16"),      # grouped from r = 129
     (((200, 1024), (64, 1024)), 128, "bf16"),      # r = 128: member by member
+    # 32 and 29 m-tiles in eight K-chunks beside a short member
+    (((8000, 2048), (7200, 2048), (300, 2048)), 384, "bf16"),
 ]
 
 
