@@ -22,6 +22,9 @@ stream, several launches back to back after a warm-up:
                                            and with the 384-row A tile per k-tile
                                            (A row-major, or k-tile-major so that
                                            each tile is one contiguous run)
+  (w0_stream_with_a_7chunks)               the row-major pattern in seven K-chunks
+                                           on 224 workgroups: 8/7 the k-tiles per
+                                           CU, the same bytes per XCD
 """
 from __future__ import annotations
 
@@ -147,7 +150,10 @@ def w0_stream(dev, d_out: int = 8192, d_in: int = 8192, r: int = 384) -> dict:
             for _ in range(3)]
     out = torch.empty(256 * 512, dtype=torch.int32, device=dev)
     res = {}
-    for name, with_a in (("w0_stream", 0), ("w0_stream_with_a", 1), ("w0_stream_with_a_tiled", 2)):
+    modes = [("w0_stream", 0), ("w0_stream_with_a", 1), ("w0_stream_with_a_tiled", 2)]
+    if d_out == 32 * 256:
+        modes.append(("w0_stream_with_a_7chunks", 3))   # same bytes per XCD, 224 workgroups
+    for name, with_a in modes:
         i = [0]
 
         def run():

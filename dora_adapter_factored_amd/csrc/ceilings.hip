@@ -198,7 +198,11 @@ __global__ __launch_bounds__(512) void cu_read(const u32x4_t* buf, int64_t bytes
 // 16 bytes of the landed tile so the data is consumed.  AMODE 1 reads A
 // row-major ([r][d_in], each k-tile 384 pieces of 64 bytes a row apart), as
 // the W0 pass does; AMODE 2 reads the same bytes k-tile-major ([k-tile][r][32
-// elements], each k-tile's A tile one contiguous 24 KB run).
+// elements], each k-tile's A tile one contiguous 24 KB run).  AMODE 3 moves
+// what AMODE 1 moves with K cut into seven chunks over 224 workgroups: chunk
+// x < 7 on XCD x for m-tiles [0, 28), the last XCD taking m-tiles 28..31 of
+// every chunk; each CU then walks 8/7 as many k-tiles while each XCD moves
+// the same bytes as in the eight-chunk layout.
 constexpr int kRows = 256, kArows = 384, kStages = 4, kRowB = 64;
 constexpr int kStageBytes = (kRows + kArows) * kRowB;
 
@@ -207,14 +211,19 @@ __global__ __launch_bounds__(512) void w0_stream(const bf16_t* W0, const bf16_t*
                                                  int64_t r, uint32_t* out) {
     // DMA instructions per wave per tile: 16 (W0) and 24 (A) groups of 16 rows over 8 waves
     constexpr int PER = kRows / 16 / 8 + (AMODE ? kArows / 16 / 8 : 0);
+    constexpr int NCH = AMODE == 3 ? 7 : 8;   // K-chunks
     __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int id = blockIdx.x;
-    const int kc = id % 8, mtile = id / 8;
+    int kc = id % 8, mtile = id / 8;
+    if (AMODE == 3 && kc == 7) {   // the last XCD: 4 m-tiles of each chunk
+        kc = mtile / 4;
+        mtile = 28 + mtile % 4;
+    }
     const int64_t m0 = (int64_t)mtile * kRows;
     const int nkt = (int)((d_in * 2 + kRowB - 1) / kRowB);
-    const int kt0 = (int)((int64_t)kc * nkt / 8), kt1 = (int)((int64_t)(kc + 1) * nkt / 8);
+    const int kt0 = (int)((int64_t)kc * nkt / NCH), kt1 = (int)((int64_t)(kc + 1) * nkt / NCH);
     const int n = kt1 - kt0;
     // the walk starts at a rotated k-tile, as the W0 pass's does (workgroups
     // reading the same column offset of a power-of-two pitch at the same time
@@ -251,7 +260,7 @@ __global__ __launch_bounds__(512) void w0_stream(const bf16_t* W0, const bf16_t*
             raw_buffer_load_lds(rw, (lds_void_t*)(st + g * 1024), 16, in ? loff + kb + g * 16 * ldb : kOutOfRange, 0,
                                 0, 0);
         }
-        if (AMODE == 1) {
+        if (AMODE == 1 || AMODE == 3) {
 #pragma unroll
             for (int g0 = 0; g0 < kArows / 16; g0 += 8) {
                 const int g = g0 + wave;
@@ -359,7 +368,8 @@ int dora_ceiling_cu_read(const void* buf, int64_t bytes_per_wg, int64_t stride, 
 // W0 [d_out, d_in] and A [r, d_in] bf16, d_in a multiple of 8 and d_out up
 // to 32 row tiles of 256 (rows of A past r read zeros); out holds 256 x 512
 // words.  with_a: 0 W0 alone, 1 A row-major, 2 A k-tile-major (offsets past
-// A's r * d_in elements read zeros).
+// A's r * d_in elements read zeros), 3 as 1 in seven K-chunks on 224
+// workgroups (d_out exactly 32 row tiles).
 int dora_ceiling_w0_stream(const void* W0, const void* A, int64_t d_out, int64_t d_in, int64_t r, int with_a,
                            void* out, void* stream) {
     if (!W0 || !A || !out || d_out < 1 || d_out > 32 * 256 || d_in < 8 || d_in % 8 || r < 1 ||
@@ -375,6 +385,8 @@ int dora_ceiling_w0_stream(const void* W0, const void* A, int64_t d_out, int64_t
         dora::w0_stream<2><<<256, 512, 0, st>>>(w, a, d_out, d_in, r, o);
     else if (with_a == 0)
         dora::w0_stream<0><<<256, 512, 0, st>>>(w, a, d_out, d_in, r, o);
+    else if (with_a == 3 && d_out == 32 * 256)
+        dora::w0_stream<3><<<224, 512, 0, st>>>(w, a, d_out, d_in, r, o);
     else
         return 1;
     return hipGetLastError() == hipSuccess ? 0 : 4;

@@ -34,4 +34,5 @@ def test_argument_checks(lib):
     assert lib.dora_ceiling_cu_read(FAKE, 1024, 0, 1, 256, 9, FAKE, None) == 1          # more than 8 waves
     assert lib.dora_ceiling_w0_stream(FAKE, FAKE, 8193 * 32, 8192, 384, 1, FAKE, None) == 1   # beyond 32 row tiles
     assert lib.dora_ceiling_w0_stream(FAKE, FAKE, 8192, 8190, 384, 1, FAKE, None) == 1   # d_in not a multiple of 8
-    assert lib.dora_ceiling_w0_stream(FAKE, FAKE, 8192, 8192, 384, 3, FAKE, None) == 1   # unknown A layout
+    assert lib.dora_ceiling_w0_stream(FAKE, FAKE, 8192, 8192, 384, 4, FAKE, None) == 1   # unknown A layout
+    assert lib.dora_ceiling_w0_stream(FAKE, FAKE, 8000, 8192, 384, 3, FAKE, None) == 1   # seven chunks: 32 row tiles
